@@ -1,0 +1,8 @@
+"""MI355X-native backward pass of a GPT-2 linear layer.
+
+``linear_layer_backward_amd.mmb`` binds the HIP library (``libmmb.so``) that
+computes dinp += dout.W, dweight += dout^T.inp and dbias = column sums of
+dout; ``linear_layer_backward_amd.workloads`` generates seeded synthetic
+inputs.  Importing this package loads nothing: the binding loads the library
+when ``mmb`` is imported and raises if it is missing.
+"""

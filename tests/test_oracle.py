@@ -1,0 +1,328 @@
+"""Pins for the CPU oracle, independent of the oracle's own code.
+
+Method: llm.c page "dev/cuda/matmul_backward.cu" (CPU reference
+matmul_backward_cpu; the forward GEMM recalled in matmul_backward1's comments,
+out = inp . W^T).  The page prints no numeric results, so the oracle is
+pinned by:
+  * a hand-worked example (tests/golden/hand_example.txt);
+  * brute-force derivatives of the forward loss L = sum(dout * out), computed
+    with exact Python integers on tiny shapes (L is linear in every parameter,
+    so L(x + e_j) - L(x) is the gradient entry exactly);
+  * closed forms (dout = 1, weight = identity, one-hot input rows);
+  * invariants (linearity in dout, accumulation onto a prefill, dbias as the
+    dweight of an appended ones column, the LM-head row-sum-zero property);
+  * mutation tests: textual mistakes planted in a copy of the oracle's C
+    source must each fail at least one pin.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_layer_backward_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.txt")
+
+
+def read_golden(path=GOLDEN):
+    lines = [ln.split("#")[0].strip() for ln in open(path)]
+    lines = [ln for ln in lines if ln]
+    out, k = {}, 0
+    while k < len(lines):
+        name, r, c = lines[k].split()
+        r, c = int(r), int(c)
+        rows = [[float(v) for v in lines[k + 1 + j].split()] for j in range(r)]
+        out[name] = np.array(rows).reshape(r, c)
+        k += 1 + r
+    return out
+
+
+# ---------------------------------------------------------------------------
+# pins, written once so the mutation tests can run them against a mutant
+
+def pin_hand_example(o):
+    g = read_golden()
+    B, T, C, OC = (int(g[k][0, 0]) for k in ("B", "T", "C", "OC"))
+    gi, gw, gb = o.backward(g["dout"], g["inp"], g["weight"], g["dinp_prefill"],
+                            g["dweight_prefill"], True, B=B, T=T, C=C, OC=OC)
+    np.testing.assert_array_equal(gi, g["expect_dinp"])
+    np.testing.assert_array_equal(gw, g["expect_dweight"])
+    np.testing.assert_array_equal(gb, g["expect_dbias"].ravel())
+
+
+def _forward_loss(inp, weight, bias, dout):
+    """L = sum_{r,o} dout[r,o] * (sum_i inp[r,i] * weight[o,i] + bias[o]),
+    in Python ints (exact)."""
+    BT, C = len(inp), len(inp[0])
+    OC = len(weight)
+    L = 0
+    for r in range(BT):
+        for o in range(OC):
+            out = bias[o]
+            for i in range(C):
+                out += inp[r][i] * weight[o][i]
+            L += dout[r][o] * out
+    return L
+
+
+def brute_force_grads(inp, weight, dout):
+    """Gradients of the forward loss by unit perturbation, exact integers."""
+    BT, C, OC = inp.shape[0], inp.shape[1], weight.shape[0]
+    X = [[int(v) for v in row] for row in inp]
+    W = [[int(v) for v in row] for row in weight]
+    D = [[int(v) for v in row] for row in dout]
+    b = [0] * OC
+    L0 = _forward_loss(X, W, b, D)
+    gi = np.zeros((BT, C))
+    gw = np.zeros((OC, C))
+    gb = np.zeros(OC)
+    for r in range(BT):
+        for i in range(C):
+            X[r][i] += 1
+            gi[r, i] = _forward_loss(X, W, b, D) - L0
+            X[r][i] -= 1
+    for o in range(OC):
+        for i in range(C):
+            W[o][i] += 1
+            gw[o, i] = _forward_loss(X, W, b, D) - L0
+            W[o][i] -= 1
+        b[o] += 1
+        gb[o] = _forward_loss(X, W, b, D) - L0
+        b[o] -= 1
+    return gi, gw, gb
+
+
+BRUTE_SHAPES = [(1, 1, 1, 1), (1, 2, 3, 5), (2, 3, 5, 2), (1, 5, 2, 3), (2, 2, 4, 4)]
+
+
+def pin_brute_force(o, shapes=BRUTE_SHAPES):
+    for n, (B, T, C, OC) in enumerate(shapes):
+        case = wl.integer_case(B, T, C, OC, seed=n, lo=-3, hi=3)
+        gi_ref, gw_ref, gb_ref = brute_force_grads(case.inp, case.weight, case.dout)
+        gi, gw, gb = o.backward(case.dout, case.inp, case.weight, case.dinp0,
+                                case.dweight0, True, B=B, T=T, C=C, OC=OC)
+        np.testing.assert_array_equal(gi - case.dinp0, gi_ref)
+        np.testing.assert_array_equal(gw - case.dweight0, gw_ref)
+        np.testing.assert_array_equal(gb, gb_ref)
+
+
+def pin_dbias_overwrites(o):
+    dout = np.arange(12, dtype=np.float64).reshape(4, 3)
+    np.testing.assert_array_equal(o.dbias(dout, B=2, T=2, OC=3), [18.0, 22.0, 26.0])
+
+
+PINS = [pin_hand_example, pin_brute_force, pin_dbias_overwrites]
+
+
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def o():
+    oracle.build()
+    return oracle.Oracle(oracle.LIBRARY)
+
+
+def test_hand_example(o):
+    pin_hand_example(o)
+
+
+def test_brute_force_integer(o):
+    pin_brute_force(o)
+
+
+def test_brute_force_float():
+    """Random float inputs: forward-loss perturbation in fp64 (h = 1, exact
+    up to rounding because L is affine in each parameter)."""
+    B, T, C, OC = 1, 3, 4, 5
+    case = wl.random_case(B, T, C, OC, seed=3)
+    inp, w, d = (x.astype(np.float64) for x in (case.inp, case.weight, case.dout))
+
+    def loss(inp, w, b):
+        return float(np.sum(d * (inp @ w.T + b)))
+
+    b = np.zeros(OC)
+    L0 = loss(inp, w, b)
+    gi = np.zeros_like(inp)
+    for r in range(B * T):
+        for i in range(C):
+            x = inp.copy(); x[r, i] += 1.0
+            gi[r, i] = loss(x, w, b) - L0
+    gw = np.zeros_like(w)
+    for oc in range(OC):
+        for i in range(C):
+            ww = w.copy(); ww[oc, i] += 1.0
+            gw[oc, i] = loss(inp, ww, b) - L0
+    gb = np.array([loss(inp, w, b + np.eye(OC)[oc]) - L0 for oc in range(OC)])
+    ri, rw, rb = oracle.backward(d, inp, w, None, None, True, B=B, T=T, C=C, OC=OC)
+    np.testing.assert_allclose(ri, gi, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rw, gw, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rb, gb, rtol=0, atol=1e-12)
+
+
+def test_dbias_overwrites(o):
+    pin_dbias_overwrites(o)
+
+
+@pytest.mark.parametrize("shape", [(2, 16, 64, 192), (3, 7, 33, 65), (1, 1, 8, 1)])
+def test_numpy_special_case(shape):
+    """numpy float64 matmul and sum reproduce the three formulas."""
+    B, T, C, OC = shape
+    case = wl.random_case(B, T, C, OC, seed=7)
+    d, x, w = (a.astype(np.float64) for a in (case.dout, case.inp, case.weight))
+    gi, gw, gb = oracle.case_backward(case)
+    np.testing.assert_allclose(gi, case.dinp0 + d @ w, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(gw, case.dweight0 + d.T @ x, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(gb, d.sum(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def test_closed_form_dout_ones():
+    """dout = 1: dbias[o] = B*T exactly; dinp increment[r,i] = sum_o W[o,i];
+    dweight increment[o,i] = sum_r inp[r,i]."""
+    B, T, C, OC = 2, 5, 7, 9
+    case = wl.integer_case(B, T, C, OC, seed=11)
+    d = np.ones((B * T, OC))
+    gi, gw, gb = oracle.backward(d, case.inp, case.weight, None, None, True,
+                                 B=B, T=T, C=C, OC=OC)
+    np.testing.assert_array_equal(gb, np.full(OC, float(B * T)))
+    for r in range(B * T):
+        np.testing.assert_array_equal(gi[r], case.weight.sum(axis=0))
+    for oc in range(OC):
+        np.testing.assert_array_equal(gw[oc], case.inp.sum(axis=0))
+
+
+def test_closed_form_identity_weight():
+    """weight = I (C == OC): the dinp increment equals dout."""
+    B, T, C = 2, 3, 6
+    case = wl.random_case(B, T, C, C, seed=5)
+    gi = oracle.dinp(case.dout, np.eye(C), None, B=B, T=T, C=C, OC=C)
+    np.testing.assert_array_equal(gi, case.dout.astype(np.float64))
+
+
+def test_closed_form_one_hot_inp():
+    """inp rows one-hot at column j(r): dweight[:, j] = sum of the dout rows
+    whose one-hot sits at j, and other columns stay zero."""
+    B, T, C, OC = 1, 12, 5, 4
+    rng = np.random.default_rng(3)
+    hot = rng.integers(0, C - 1, size=B * T)   # column C-1 never hot
+    inp = np.zeros((B * T, C)); inp[np.arange(B * T), hot] = 1.0
+    dout = rng.standard_normal((B * T, OC))
+    gw = oracle.dweight(dout, inp, None, B=B, T=T, C=C, OC=OC)
+    for j in range(C):
+        expect = np.zeros(OC)
+        for r in range(B * T):
+            if hot[r] == j:
+                expect += dout[r]
+        np.testing.assert_allclose(gw[:, j], expect, rtol=0, atol=1e-15)
+    assert np.all(gw[:, C - 1] == 0.0)
+
+
+def test_linearity_in_dout():
+    B, T, C, OC = 2, 4, 6, 10
+    a = wl.integer_case(B, T, C, OC, seed=21)
+    b = wl.integer_case(B, T, C, OC, seed=22)
+    alpha = 3.0
+    d = alpha * a.dout + b.dout
+    r1 = oracle.backward(d, a.inp, a.weight, None, None, True, B=B, T=T, C=C, OC=OC)
+    ra = oracle.backward(a.dout, a.inp, a.weight, None, None, True, B=B, T=T, C=C, OC=OC)
+    rb = oracle.backward(b.dout, a.inp, a.weight, None, None, True, B=B, T=T, C=C, OC=OC)
+    for x, y, z in zip(r1, ra, rb):
+        np.testing.assert_array_equal(x, alpha * y + z)
+
+
+def test_accumulation_onto_prefill():
+    """out(prefill P) - P == out(0), exactly with integer inputs."""
+    B, T, C, OC = 3, 5, 8, 6
+    c = wl.integer_case(B, T, C, OC, seed=31)
+    gi, gw, gb = oracle.case_backward(c)
+    zi, zw, zb = oracle.backward(c.dout, c.inp, c.weight, None, None, True,
+                                 B=B, T=T, C=C, OC=OC)
+    np.testing.assert_array_equal(gi - c.dinp0, zi)
+    np.testing.assert_array_equal(gw - c.dweight0, zw)
+    np.testing.assert_array_equal(gb, zb)   # dbias ignores the buffer
+
+
+def test_dbias_is_dweight_of_ones_column():
+    B, T, C, OC = 2, 6, 5, 7
+    c = wl.random_case(B, T, C, OC, seed=41)
+    inp1 = np.concatenate([c.inp.astype(np.float64), np.ones((B * T, 1))], axis=1)
+    gw1 = oracle.dweight(c.dout, inp1, None, B=B, T=T, C=C + 1, OC=OC)
+    gb = oracle.dbias(c.dout, B=B, T=T, OC=OC)
+    np.testing.assert_array_equal(gw1[:, C], gb)
+
+
+def test_lm_head_properties():
+    """Softmax-minus-one-hot rows sum to zero, so the column sums of dweight
+    vanish up to rounding, and dweight rows of padded vocab entries are 0."""
+    BT, vocab, padded, C = 64, 300, 320, 16
+    dout = wl.lm_head_dout(1, 2, BT, vocab, padded, "f32")
+    inp = wl.normal(3, (BT, C), 1.0, "f32")
+    gw = oracle.dweight(dout, inp, None, B=1, T=BT, C=C, OC=padded)
+    assert np.all(gw[vocab:] == 0.0)
+    col = gw.sum(axis=0)
+    scale = np.abs(gw).sum(axis=0)
+    assert np.all(np.abs(col) <= 1e-6 * scale + 1e-12)
+
+
+def test_thread_count_invariance(tmp_path):
+    """Each output element is one sequential sum: 1 and 4 threads agree bitwise."""
+    c = wl.random_case(2, 9, 13, 11, seed=51)
+    code = (
+        "import numpy as np, oracle\n"
+        "from linear_layer_backward_amd import workloads as wl\n"
+        "c = wl.random_case(2, 9, 13, 11, seed=51)\n"
+        "gi, gw, gb = oracle.case_backward(c)\n"
+        f"np.save(r'{tmp_path}/' + __import__('os').environ['OMP_NUM_THREADS'] + '.npy',"
+        " np.concatenate([gi.ravel(), gw.ravel(), gb]))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for n in ("1", "4"):
+        env = dict(os.environ, OMP_NUM_THREADS=n, PYTHONPATH=root)
+        subprocess.run(["python", "-c", code], check=True, env=env, cwd=root)
+    a = np.load(tmp_path / "1.npy")
+    b = np.load(tmp_path / "4.npy")
+    assert a.tobytes() == b.tobytes()
+    assert c.BT == 18
+
+
+# ---------------------------------------------------------------------------
+# mutation tests: each planted mistake must be caught by some pin
+
+MUTATIONS = [
+    ("dinp drops the prefill",
+     "dinp[r * C + i] = dinp[r * C + i] + s;", "dinp[r * C + i] = s;"),
+    ("dinp sign flipped",
+     "s += dout[r * OC + o] * weight[o * C + i];", "s -= dout[r * OC + o] * weight[o * C + i];"),
+    ("dinp drops the last term",
+     "for (long o = 0; o < OC; o++)\n                s += dout",
+     "for (long o = 0; o < OC - 1; o++)\n                s += dout"),
+    ("dweight wrong input column",
+     "s += dout[r * OC + o] * inp[r * C + i];", "s += dout[r * OC + o] * inp[r * C + (C - 1 - i)];"),
+    ("dweight written transposed",
+     "dweight[o * C + i] = dweight[o * C + i] + s;", "dweight[i * OC + o] = dweight[i * OC + o] + s;"),
+    ("dweight drops the first row",
+     "for (long r = 0; r < BT; r++)\n                s += dout[r * OC + o] * inp",
+     "for (long r = 1; r < BT; r++)\n                s += dout[r * OC + o] * inp"),
+    ("dbias accumulates instead of assigning",
+     "dbias[o] = s;", "dbias[o] = dbias[o] + s;"),
+    ("dbias sums a row instead of a column",
+     "s += dout[r * OC + o];\n        dbias", "s += dout[(o % BT) * OC + (r % OC)];\n        dbias"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.compile_library(str(mutant_src), str(tmp_path / "libmutant.so"))
+    m = oracle.Oracle(lib)
+    failures = 0
+    for pin in PINS:
+        try:
+            pin(m)
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no pin caught the mutation: {name}"
