@@ -1,0 +1,216 @@
+"""Benchmark of the linear-layer backward pass (dinp + dweight + dbias) on one
+MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+
+A step is one whole backward pass over the workload (one mmb_backward call;
+two for the MLP pair).  Prints one JSON line: TFLOP/s over the timed steps
+(4*B*T*C*OC flops plus B*T*OC adds for the bias), the dominant kernel's
+MFMA roofline fraction from HIP events recorded around every launch on the
+stream it runs on, and the CPU oracle timed on a bounded sample of the same
+workload on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "matmul-backward TFLOP/s (dinp+dweight+dbias) at GPT-2 fc shape; % MFMA peak"
+# MI355X dense peaks (AMD published): bf16 MFMA 2.5 PFLOP/s (256 CUs x 2.4 GHz
+# x 4096 flop/clk/CU = 2516.6 TFLOP/s), fp32 MFMA 157.3 TFLOP/s
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+KERNEL_NAME = "mmb_tiles_kernel"
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_layer_backward_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_cfg{cfg}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^source_digest:\s*(\w+)", text, re.M)
+    b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not b or m.group(1) != source_digest():
+        return None
+    return float(b.group(1))
+
+
+def upload(case, dev):
+    import torch
+    from linear_layer_backward_amd import workloads as wl
+
+    def up(a):
+        raw = wl.storage(np.asarray(a, np.float32).ravel(), case.dtype)
+        if case.dtype == "bf16":
+            return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(raw.copy()).to(dev)
+
+    return dict(dinp=up(case.dinp0), dweight=up(case.dweight0),
+                dbias=up(case.dbias0) if case.with_bias else None,
+                dout=up(case.dout), inp=up(case.inp), weight=up(case.weight))
+
+
+def cpu_baseline(case, target_s: float = 12.0):
+    """The oracle (unchanged) on a bounded sample of the workload: the first
+    `rows` rows of dinp and the first `chans` rows of dweight (plus their
+    dbias entries), sized from a probe to about target_s seconds."""
+    import oracle
+    d64 = case.dout.astype(np.float64)
+    x64 = case.inp.astype(np.float64)
+    w64 = case.weight.astype(np.float64)
+
+    def run(rows, chans):
+        dr = np.ascontiguousarray(d64[:rows])
+        dc = np.ascontiguousarray(d64[:, :chans])
+        t0 = time.perf_counter()
+        oracle.dinp(dr, w64, None, B=1, T=rows, C=case.C, OC=case.OC)
+        oracle.dweight(dc, x64, None, B=case.B, T=case.T, C=case.C, OC=chans)
+        if case.with_bias:
+            oracle.dbias(dc, B=case.B, T=case.T, OC=chans)
+        dt = time.perf_counter() - t0
+        flops = 2 * rows * case.C * case.OC + 2 * chans * case.BT * case.C
+        if case.with_bias:
+            flops += chans * case.BT
+        return dt, flops
+
+    threads = oracle.threads()
+    r0, c0 = max(threads, 16), max(threads, 4)
+    t, _ = run(r0, c0)
+    scale = max(1.0, target_s / max(t, 1e-3))
+    rows = int(min(case.BT, r0 * scale))
+    chans = int(min(case.OC, c0 * scale))
+    dt, flops = run(rows, chans)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{case.name}: dinp rows 0..{rows - 1} of {case.BT}, dweight"
+                      f"{'+dbias' if case.with_bias else ''} channels 0..{chans - 1} of "
+                      f"{case.OC}; fp64 OpenMP, {dt:.1f} s for {flops:.3e} flops"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the "
+              "multi-GPU (data-parallel) sharding is a design note only.", file=sys.stderr)
+        return 2
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
+        return 0
+
+    from linear_layer_backward_amd import mmb
+    from linear_layer_backward_amd import workloads as wl
+
+    cases = wl.config_cases(args.config)
+    print(f"[bench] workload: {wl.CONFIG_NAMES[args.config]}", file=sys.stderr, flush=True)
+    bufs = [upload(c, dev) for c in cases]
+    stream = torch.cuda.current_stream(dev)
+    codes = [mmb.MMB_BF16 if c.dtype == "bf16" else mmb.MMB_FP32 for c in cases]
+
+    def step():
+        for c, b, code in zip(cases, bufs, codes):
+            mmb.mmb_backward_stream(b["dinp"], b["dweight"], b["dbias"], b["dout"], b["inp"],
+                                    b["weight"], c.B, c.T, c.C, c.OC, code, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = total_ms / K
+
+    flops = sum(c.flops() for c in cases)
+    dtype = cases[0].dtype
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    traffic = measured_traffic(args.config)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.CONFIG_NAMES[args.config],
+                   "calls": [{"B": c.B, "T": c.T, "C": c.C, "OC": c.OC, "bias": c.with_bias}
+                             for c in cases],
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "launch_ms": round(launch_ms, 5)},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cases[0])
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,115 @@
+/*
+ * mmb.h -- C ABI of libmmb.so, the backward pass of a GPT-2 linear layer
+ * (out = inp . W^T + bias) on AMD Instinct MI355X (gfx950).
+ *
+ * Operation (llm.c page "dev/cuda/matmul_backward.cu": CPU reference
+ * matmul_backward_cpu and the cuBLAS launcher matmul_backward1), with
+ * BT = B*T rows:
+ *
+ *   dinp[r,i]    += sum_{o<OC} dout[r,o] * weight[o,i]     r<BT, i<C
+ *   dweight[o,i] += sum_{r<BT} dout[r,o] * inp[r,i]        o<OC, i<C
+ *   dbias[o]      = sum_{r<BT} dout[r,o]                   o<OC, if dbias != NULL
+ *
+ * dinp and dweight accumulate onto what the buffers already hold (gradients
+ * of a parameter used several times add; the page's launcher runs both GEMMs
+ * with beta = 1).  dbias is assigned, as in every version on that page.
+ *
+ * Layout: every tensor is dense and row-major, as on the page:
+ *   inp [BT,C], dout [BT,OC], weight [OC,C], dinp [BT,C], dweight [OC,C],
+ *   dbias [OC].
+ *
+ * dtype (one for all six tensors):
+ *   MMB_FP32  IEEE fp32 storage, fp32 products and sums (no reduced-precision
+ *             substitute; the page's check turns TF32 off).
+ *   MMB_BF16  bfloat16 storage, exact products, fp32 accumulation over the
+ *             whole reduction; each output is rounded to bf16 once, to
+ *             nearest-even, from  float(old) + fp32 sum  (dinp, dweight) or
+ *             the fp32 sum (dbias).
+ *
+ * Pointers are device pointers (hipMalloc or torch CUDA memory) owned by the
+ * caller.  dout, inp, weight are read only; dinp and dweight are read and
+ * written; dbias is written only.  Output buffers may not overlap each other
+ * or any input (MMB_ERR_ALIAS).  Any alignment and any dims >= 1 are
+ * accepted; 16-byte aligned pointers with C and OC multiples of 8 (bf16) or
+ * 4 (fp32) take the MFMA path, anything else a slower generic path.
+ *
+ * The library owns only a per-(device, stream) workspace (split-K partial
+ * sums, tile counters and work lists), allocated on first use, grown on
+ * demand and freed by mmb_release().  Work is enqueued asynchronously; launch
+ * errors are returned, faults during execution surface at the caller's next
+ * synchronisation.  Results are deterministic: the same inputs give the same
+ * bits on every run (no floating-point atomics; split-K partials are summed
+ * in a fixed order).  Calls on different streams are independent; calls on
+ * one stream are ordered by it.
+ *
+ * All functions return MMB_OK (0) or a negative mmb_status; none of them
+ * exits or aborts.
+ */
+#ifndef MMB_H
+#define MMB_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MMB_FP32 = 0,
+    MMB_BF16 = 1
+} mmb_dtype;
+
+typedef enum {
+    MMB_OK = 0,
+    MMB_ERR_NULL = -1,      /* a required pointer is NULL (only dbias may be)  */
+    MMB_ERR_DIM = -2,       /* B, T, C or OC < 1                                */
+    MMB_ERR_DTYPE = -3,     /* dtype is not an mmb_dtype                       */
+    MMB_ERR_OVERFLOW = -4,  /* B*T >= 2^31                                      */
+    MMB_ERR_ALIAS = -5,     /* an output range overlaps another buffer's range */
+    MMB_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed      */
+    MMB_ERR_NOMEM = -7      /* the workspace could not be allocated            */
+} mmb_status;
+
+/* The backward pass on the calling thread's current device, enqueued on the
+ * NULL (default) stream.  Arguments as in the file comment. */
+int mmb_backward(void* dinp, void* dweight, void* dbias,
+                 const void* dout, const void* inp, const void* weight,
+                 int B, int T, int C, int OC, int dtype);
+
+/* As mmb_backward, enqueued on `stream` (a hipStream_t; NULL = default). */
+int mmb_backward_stream(void* dinp, void* dweight, void* dbias,
+                        const void* dout, const void* inp, const void* weight,
+                        int B, int T, int C, int OC, int dtype, void* stream);
+
+/* Host-only validation of an argument set, exactly the checks that
+ * mmb_backward performs before touching the GPU.  Makes no HIP call. */
+int mmb_check_args(const void* dinp, const void* dweight, const void* dbias,
+                   const void* dout, const void* inp, const void* weight,
+                   int B, int T, int C, int OC, int dtype);
+
+/* Static English text for a status code (never NULL). */
+const char* mmb_strerror(int status);
+
+/* Which kernel path a call with these arguments takes: 1 = MFMA tiles,
+ * 0 = generic path, or a negative mmb_status.  Host only, no HIP call. */
+int mmb_path(const void* dinp, const void* dweight, const void* dbias,
+             const void* dout, const void* inp, const void* weight,
+             int B, int T, int C, int OC, int dtype);
+
+/* Host-only view of the work plan the MFMA path would use on a device with
+ * `num_cus` compute units (8 XCDs when num_cus >= 128): writes the split
+ * counts {dweight, dinp} to splits[2] and, when `units` is not NULL, up to
+ * max_units launch-ordered work units as 4 ints each {kind (0 = dweight,
+ * 1 = dinp), tile_m, tile_n, split}.  Returns the number of units, or a
+ * negative mmb_status.  Honours the MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP
+ * environment overrides like mmb_backward.  Makes no HIP call. */
+int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
+                   int* splits, int* units, int max_units);
+
+/* Synchronise every device the library has used, then free its workspaces.
+ * The next call allocates again. */
+int mmb_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMB_H */

@@ -1,0 +1,48 @@
+"""Compile the HIP sources under csrc/ into libmmb.so (gfx950) in-tree.
+
+    python -m linear_layer_backward_amd.build [-v]
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+LIBRARY = os.path.join(PKG, "libmmb.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-Wall", "-Wno-unused-function",
+    # keep hipcc from forming packed fp32 instructions (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    tmp = LIBRARY + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *extra, *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 feature; that warning is noise
+    noise = "is not a recognized feature for this target"
+    out = "\n".join(ln for ln in r.stdout.splitlines() if noise not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

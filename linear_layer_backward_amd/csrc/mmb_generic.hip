@@ -1,0 +1,99 @@
+// mmb_generic.hip -- the generic path: one thread per output element, fp32
+// accumulation, any shape and any alignment.  It serves calls the MFMA tiles
+// cannot take (C or OC not a multiple of the 16-byte vector, unaligned
+// pointers).
+//
+// Operation: llm.c page "dev/cuda/matmul_backward.cu" -- the dinp and
+// dweight GEMMs of matmul_backward1 (beta = 1) and the one-thread-per-channel
+// bias kernel matmul_backward_bias_kernel_naive (assigning dbias).
+#include "mmb_internal.h"
+#include "mmb_numeric.h"
+
+namespace mmb {
+namespace {
+
+constexpr int kBlock = 256;
+
+// dinp[r,i] = old + sum_o dout[r,o] * weight[o,i]; block = one row r and 256
+// consecutive i, so weight reads coalesce and dout[r,o] is a broadcast.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void generic_dinp(T* __restrict__ dinp,
+                                                       const T* __restrict__ dout,
+                                                       const T* __restrict__ weight,
+                                                       int C, int OC) {
+    const long long r = blockIdx.y;
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    if (i >= C) return;
+    const T* d = dout + r * OC;
+    float acc = 0.f;
+    for (int o = 0; o < OC; ++o)
+        acc = fmaf(to_f32(d[o]), to_f32(weight[(long long)o * C + i]), acc);
+    T* out = dinp + r * C + i;
+    *out = from_f32<T>(to_f32(*out) + acc);
+}
+
+// dweight[o,i] = old + sum_r dout[r,o] * inp[r,i]; block = one channel o and
+// 256 consecutive i.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void generic_dweight(T* __restrict__ dweight,
+                                                          const T* __restrict__ dout,
+                                                          const T* __restrict__ inp,
+                                                          int BT, int C, int OC) {
+    const long long o = blockIdx.y;
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    if (i >= C) return;
+    float acc = 0.f;
+    for (long long r = 0; r < BT; ++r)
+        acc = fmaf(to_f32(dout[r * OC + o]), to_f32(inp[r * C + i]), acc);
+    T* out = dweight + o * C + i;
+    *out = from_f32<T>(to_f32(*out) + acc);
+}
+
+// dbias[o] = sum_r dout[r,o]: one thread per channel, reads coalesce along o.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void generic_dbias(T* __restrict__ dbias,
+                                                        const T* __restrict__ dout,
+                                                        int BT, int OC) {
+    const int o = blockIdx.x * kBlock + threadIdx.x;
+    if (o >= OC) return;
+    float acc = 0.f;
+    for (long long r = 0; r < BT; ++r) acc += to_f32(dout[r * OC + o]);
+    dbias[o] = from_f32<T>(acc);
+}
+
+template <typename T>
+hipError_t launch(void* dinp, void* dweight, void* dbias, const void* dout,
+                  const void* inp, const void* weight, int BT, int C, int OC,
+                  hipStream_t s) {
+    const dim3 block(kBlock);
+    const unsigned gx = (unsigned)((C + kBlock - 1) / kBlock);
+    // grid.y is limited to 65535 by the hardware dispatcher: chunk the rows
+    const int kRowsPerLaunch = 65535;
+    for (int r0 = 0; r0 < BT; r0 += kRowsPerLaunch) {
+        const int rows = BT - r0 < kRowsPerLaunch ? BT - r0 : kRowsPerLaunch;
+        hipLaunchKernelGGL(generic_dinp<T>, dim3(gx, rows), block, 0, s,
+                           (T*)dinp + (long long)r0 * C, (const T*)dout + (long long)r0 * OC,
+                           (const T*)weight, C, OC);
+    }
+    for (int o0 = 0; o0 < OC; o0 += kRowsPerLaunch) {
+        const int rows = OC - o0 < kRowsPerLaunch ? OC - o0 : kRowsPerLaunch;
+        hipLaunchKernelGGL(generic_dweight<T>, dim3(gx, rows), block, 0, s,
+                           (T*)dweight + (long long)o0 * C, (const T*)dout + o0,
+                           (const T*)inp, BT, C, OC);
+    }
+    if (dbias != nullptr)
+        hipLaunchKernelGGL(generic_dbias<T>, dim3((OC + kBlock - 1) / kBlock), block, 0, s,
+                           (T*)dbias, (const T*)dout, BT, OC);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
+                          const void* dout, const void* inp, const void* weight,
+                          int BT, int C, int OC, hipStream_t s) {
+    if (dtype == 0) return launch<float>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s);
+    return launch<bf16_t>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s);
+}
+
+}  // namespace mmb

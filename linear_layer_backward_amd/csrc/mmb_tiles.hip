@@ -1,0 +1,417 @@
+// mmb_tiles.hip -- the MFMA path: both GEMMs of the linear-layer backward
+// pass and the bias reduction in one launch of output-tile work units.
+//
+// Operation (llm.c page "dev/cuda/matmul_backward.cu", launcher
+// matmul_backward1 and bias kernels):
+//   dinp    [BT,C] += dout[BT,OC] . weight[OC,C]      (unit kind UNIT_DINP)
+//   dweight [OC,C] += dout^T[OC,BT] . inp[BT,C]       (unit kind UNIT_DWEIGHT)
+//   dbias   [OC]    = column sums of dout             (inside dweight units
+//                                                      of output column tile 0)
+//
+// gfx950 design:
+//  * One workgroup = 4 wave64s = one output tile (BM x BN), each wave a
+//    2 x 2 quarter of it built from 32x32 MFMA blocks (bf16: 32x32x16 with
+//    fp32 accumulators; fp32: 32x32x2 fp32, no reduced-precision products).
+//  * Operands are staged global -> registers -> LDS with a 2-stage ping-pong
+//    (the loads of stage k+1 are in flight while the MFMAs of stage k run;
+//    one barrier per stage).  LDS always holds K-contiguous rows of 128
+//    bytes, so every MFMA fragment is one ds_read_b128.  Operands stored
+//    K-strided in HBM (weight, inp, and dout for dweight) are transposed in
+//    registers, E x E elements per thread, on the way in.  The 16-byte chunk
+//    c of LDS row r lives at chunk c ^ (r & 7): conflict-free for the
+//    fragment reads (8 rows, same chunk) and the staging writes (1 row,
+//    8 chunks).
+//  * The MFMA "A" input is the N-side tile and "B" the M-side tile, so each
+//    lane's accumulator holds 4 consecutive output columns: 16-byte fp32 /
+//    8-byte bf16 epilogue accesses along the contiguous output dimension.
+//  * dweight's long reduction (K = B*T) is split over several units; each
+//    writes its fp32 partial tile to the workspace and takes a ticket; the
+//    last arriver adds the partials in split order (deterministic), adds the
+//    old output (beta = 1), rounds once, stores, and resets the ticket.
+//  * dbias: the dweight units of column tile 0 already stream the dout
+//    columns of their rows; each thread sums the dout values it stages, a
+//    3-step xor shuffle combines the 8 threads that share a column, and split
+//    partials go through the same last-arriver path.
+//  * Operands are read at 16-byte granularity; C and OC are multiples of the
+//    vector width on this path, so a vector is wholly inside or outside a
+//    ragged edge, which is zero-filled on load and masked on store.
+#include "mmb_internal.h"
+#include "mmb_numeric.h"
+
+namespace mmb {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;  // one LDS row: BK elements of one m or n
+
+template <typename T> struct Cfg;
+template <> struct Cfg<bf16_t> {
+    static constexpr int BM = 256, BN = 192, BK = 64;
+    static constexpr int E = 8;               // elements per 16-byte vector
+    static constexpr int WM = 128, WN = 96;   // wave tile
+};
+template <> struct Cfg<float> {
+    static constexpr int BM = 128, BN = 128, BK = 32;
+    static constexpr int E = 4;
+    static constexpr int WM = 64, WN = 64;
+};
+
+template <typename T>
+struct K {
+    static constexpr int BM = Cfg<T>::BM, BN = Cfg<T>::BN, BK = Cfg<T>::BK, E = Cfg<T>::E;
+    static constexpr int WM = Cfg<T>::WM, WN = Cfg<T>::WN;
+    static constexpr int MB = WM / 32, NB = WN / 32;        // 32x32 blocks per wave
+    static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int A_KC_PER = BM * 8 / kThreads;      // K-contiguous A: vectors/thread
+    static_assert(BK * (int)sizeof(T) == kRowBytes, "row = 8 vectors of 16 bytes");
+    static_assert(BM == 2 * WM && BN == 2 * WN, "2 x 2 waves");
+    static_assert(BM / E * 8 <= kThreads && BN / E * 8 <= kThreads, "one staging pass");
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+}
+
+// ---- E x E transpose of one staged block ---------------------------------
+// in[r] holds E consecutive columns of K-row r; out[x] gets E consecutive
+// K-rows of column x.
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8], bf16_t) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        const int d = x >> 1;
+        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            out[x][p] = __builtin_amdgcn_perm(in[2 * p + 1][d], in[2 * p][d], sel);
+    }
+}
+__device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4], float) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) out[x][p] = in[p][x];
+}
+
+// column sums of a staged block (dbias), fp32
+__device__ __forceinline__ void add_columns(const u32x4 (&in)[8], float (&s)[8], bf16_t) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            s[2 * d] += __uint_as_float(in[r][d] << 16);
+            s[2 * d + 1] += __uint_as_float(in[r][d] & 0xffff0000u);
+        }
+}
+__device__ __forceinline__ void add_columns(const u32x4 (&in)[4], float (&s)[4], float) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) s[x] += __uint_as_float(in[r][x]);
+}
+
+// ---- MFMA step over one LDS stage ----------------------------------------
+template <typename T>
+__device__ __forceinline__ void mma_stage(const char* sa, const char* sb, int wm0, int wn0,
+                                          int lane, f32x16 (&acc)[K<T>::MB][K<T>::NB]) {
+    using Kt = K<T>;
+    const int lr = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int chunk = 2 * s + half;
+        u32x4 fa[Kt::NB], fb[Kt::MB];
+#pragma unroll
+        for (int nb = 0; nb < Kt::NB; ++nb)
+            fa[nb] = *(const u32x4*)(sb + swz(wn0 + nb * 32 + lr, chunk));
+#pragma unroll
+        for (int mb = 0; mb < Kt::MB; ++mb)
+            fb[mb] = *(const u32x4*)(sa + swz(wm0 + mb * 32 + lr, chunk));
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int mb = 0; mb < Kt::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < Kt::NB; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fa[nb]), __builtin_bit_cast(bf16x8, fb[mb]),
+                        acc[mb][nb], 0, 0, 0);
+        } else {
+            // lane half h holds k = 8s + 4h + q in element q: MFMA q reduces
+            // over the pair {8s + q, 8s + 4 + q}; all four cover the 8 k.
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int mb = 0; mb < Kt::MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < Kt::NB; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            __uint_as_float(fa[nb][q]), __uint_as_float(fb[mb][q]),
+                            acc[mb][nb], 0, 0, 0);
+        }
+    }
+}
+
+// ---- epilogue helpers -----------------------------------------------------
+__device__ __forceinline__ void store4(float* d, f32x4 v, bool accumulate) {
+    f32x4 o = v;
+    if (accumulate) o += *(const f32x4*)d;
+    *(f32x4*)d = o;
+}
+__device__ __forceinline__ void store4(bf16_t* d, f32x4 v, bool accumulate) {
+    f32x4 o = v;
+    if (accumulate) {
+        const u32x2 old = *(const u32x2*)d;
+        o[0] += __uint_as_float(old[0] << 16);
+        o[1] += __uint_as_float(old[0] & 0xffff0000u);
+        o[2] += __uint_as_float(old[1] << 16);
+        o[3] += __uint_as_float(old[1] & 0xffff0000u);
+    }
+    u32x2 r;
+    r[0] = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+    r[1] = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+    *(u32x2*)d = r;
+}
+
+// ---- one work unit ---------------------------------------------------------
+// AK: the A operand (M side) is K-contiguous in memory (dinp: A = dout rows);
+// otherwise it is M-contiguous (dweight: A = dout^T).  B is always
+// N-contiguous (weight for dinp, inp for dweight).
+template <typename T, bool AK>
+__device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u,
+                                         char* smem, int* s_flag) {
+    using Kt = K<T>;
+    constexpr int BM = Kt::BM, BN = Kt::BN, BK = Kt::BK, E = Kt::E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tile_m = u.y, tile_n = u.z, split = u.w;
+    const int M = g.M, N = g.N, Kd = g.K;
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int kt0 = (int)((long long)split * g.kiters / g.splits);
+    const int kt1 = (int)((long long)(split + 1) * g.kiters / g.splits);
+
+    const T* A = (const T*)p.dout;                       // ld = OC either way
+    const T* Bop = (const T*)(AK ? p.weight : p.inp);    // ld = C
+    T* D = (T*)(AK ? p.dinp : p.dweight);                // ld = C
+    const long long lda = p.OC, ldb = p.C, ldd = p.C;
+    const bool do_bias = !AK && p.dbias != nullptr && tile_n == 0;
+
+    // staging thread roles
+    const int kg = tid & 7, xg = tid >> 3;       // E x E block: K-group, column group
+    const bool b_active = xg < BN / E;
+    const bool a_active = AK || xg < BM / E;
+
+    constexpr int APER = AK ? Kt::A_KC_PER : E;
+    u32x4 ra[APER], rb[E];
+    float bsum[E];
+#pragma unroll
+    for (int x = 0; x < E; ++x) bsum[x] = 0.f;
+
+    auto load = [&](int kt) {
+        const int k0 = kt * BK;
+        // B: rows k (K-strided), E columns starting at n0 + xg*E
+        {
+            const int n = n0 + xg * E;
+            const bool colok = b_active && n < N;
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const int k = k0 + kg * E + r;
+                rb[r] = (colok && k < Kd) ? *(const u32x4*)(Bop + (long long)k * ldb + n)
+                                          : u32x4{0, 0, 0, 0};
+            }
+        }
+        if constexpr (AK) {
+            // A: rows m, 16-byte vectors along K
+#pragma unroll
+            for (int j = 0; j < APER; ++j) {
+                const int m = m0 + (tid >> 3) + 32 * j;
+                const int k = k0 + (tid & 7) * E;
+                ra[j] = (m < M && k < Kd) ? *(const u32x4*)(A + (long long)m * lda + k)
+                                          : u32x4{0, 0, 0, 0};
+            }
+        } else {
+            const int m = m0 + xg * E;
+            const bool colok = a_active && m < M;
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const int k = k0 + kg * E + r;
+                ra[r] = (colok && k < Kd) ? *(const u32x4*)(A + (long long)k * lda + m)
+                                          : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    auto store = [&](int stage) {
+        char* sa = smem + stage * Kt::STAGE_BYTES;
+        char* sb = sa + BM * kRowBytes;
+        if (b_active) {
+            u32x4 t[E];
+            transpose_block(rb, t, T{});
+#pragma unroll
+            for (int x = 0; x < E; ++x) *(u32x4*)(sb + swz(xg * E + x, kg)) = t[x];
+        }
+        if constexpr (AK) {
+#pragma unroll
+            for (int j = 0; j < APER; ++j)
+                *(u32x4*)(sa + swz((tid >> 3) + 32 * j, tid & 7)) = ra[j];
+        } else {
+            if (a_active) {
+                if (do_bias) add_columns(ra, bsum, T{});
+                u32x4 t[E];
+                transpose_block(ra, t, T{});
+#pragma unroll
+                for (int x = 0; x < E; ++x) *(u32x4*)(sa + swz(xg * E + x, kg)) = t[x];
+            }
+        }
+    };
+
+    f32x16 acc[Kt::MB][Kt::NB];
+#pragma unroll
+    for (int i = 0; i < Kt::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < Kt::NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int wm0 = (wave & 1) * Kt::WM, wn0 = (wave >> 1) * Kt::WN;
+
+    load(kt0);
+    store(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        const bool more = kt + 1 < kt1;
+        if (more) load(kt + 1);
+        const char* sa = smem + cur * Kt::STAGE_BYTES;
+        mma_stage<T>(sa, sa + BM * kRowBytes, wm0, wn0, lane, acc);
+        if (more) store(cur ^ 1);
+        __syncthreads();
+    }
+
+    // dbias: combine the 8 K-groups of each column (lanes differing in bits 0..2)
+    if (do_bias) {
+#pragma unroll
+        for (int x = 0; x < E; ++x) {
+            float v = bsum[x];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            bsum[x] = v;
+        }
+    }
+
+    const int lr = lane & 31, half = lane >> 5;
+    if (g.splits > 1) {
+        // 1. publish this split's partial tile (fragment order, 16-byte stores)
+        const int tile = tile_m * g.tiles_n + tile_n;
+        float* wt = p.ws + g.ws_base + ((long long)tile * g.splits + split) * (BM * BN);
+#pragma unroll
+        for (int mb = 0; mb < Kt::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < Kt::NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                               acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+                    *(f32x4*)(wt + ((mb * Kt::NB + nb) * 4 + q) * (kThreads * 4) + tid * 4) = v;
+                }
+        if (do_bias && kg == 0 && a_active) {
+            float* wb = p.ws_bias + ((long long)tile_m * g.splits + split) * BM + xg * E;
+#pragma unroll
+            for (int x = 0; x < E; ++x) wb[x] = bsum[x];
+        }
+        // 2. take a ticket; the last of the tile's splits finishes it
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = atomicAdd(p.counters + g.tile_base + tile, 1);
+            *s_flag = (prev == g.splits - 1);
+        }
+        __syncthreads();
+        if (!*s_flag) return;
+        __threadfence();
+        // 3. sum the partials in split order
+        const float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
+#pragma unroll
+        for (int mb = 0; mb < Kt::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < Kt::NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int off = ((mb * Kt::NB + nb) * 4 + q) * (kThreads * 4) + tid * 4;
+                    f32x4 mine = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                                  acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+                    f32x4 s = split == 0 ? mine : *(const f32x4*)(w0 + off);
+                    for (int sp = 1; sp < g.splits; ++sp)
+                        s += sp == split ? mine : *(const f32x4*)(w0 + (long long)sp * (BM * BN) + off);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[mb][nb][4 * q + r] = s[r];
+                }
+        if (do_bias && kg == 0 && a_active) {
+            const float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + xg * E;
+#pragma unroll
+            for (int x = 0; x < E; ++x) {
+                float s = split == 0 ? bsum[x] : wb[x];
+                for (int sp = 1; sp < g.splits; ++sp)
+                    s += sp == split ? bsum[x] : wb[(long long)sp * BM + x];
+                bsum[x] = s;
+            }
+        }
+        if (tid == 0) p.counters[g.tile_base + tile] = 0;
+    }
+
+    // 4. output tile: D = old + acc (rounded once), dbias = sum
+#pragma unroll
+    for (int mb = 0; mb < Kt::MB; ++mb) {
+        const int m = m0 + wm0 + mb * 32 + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int nb = 0; nb < Kt::NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn0 + nb * 32 + 8 * q + 4 * half;
+                if (n >= N) continue;
+                f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                           acc[mb][nb][4 * q + 3]};
+                store4(D + (long long)m * ldd + n, v, true);
+            }
+    }
+    if (do_bias && kg == 0 && a_active) {
+        T* db = (T*)p.dbias;
+#pragma unroll
+        for (int x = 0; x < E; ++x) {
+            const int m = m0 + xg * E + x;
+            if (m < M) db[m] = from_f32<T>(bsum[x]);
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void mmb_tiles_kernel(TilesParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[K<T>::LDS_BYTES];
+    __shared__ int s_flag;
+    const int4 u = p.units[blockIdx.x];
+    if (u.x == UNIT_DINP)
+        run_unit<T, true>(p, p.g[UNIT_DINP], u, smem, &s_flag);
+    else
+        run_unit<T, false>(p, p.g[UNIT_DWEIGHT], u, smem, &s_flag);
+}
+
+}  // namespace
+
+TileShape tile_shape(int dtype) {
+    if (dtype == 1) return TileShape{K<bf16_t>::BM, K<bf16_t>::BN, K<bf16_t>::BK};
+    return TileShape{K<float>::BM, K<float>::BN, K<float>::BK};
+}
+
+hipError_t launch_tiles(int dtype, const TilesParams& p, hipStream_t s) {
+    if (dtype == 1) return launch_tiles_bf16(p, s);
+    if (p.n_units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mmb_tiles_kernel<float>, dim3(p.n_units), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace mmb

@@ -1,0 +1,156 @@
+"""Python binding of libmmb.so (C ABI in include/mmb.h).
+
+Argument marshalling only: every step of the backward pass runs in the HIP
+kernels of the library.  Importing this module loads ``libmmb.so`` from this
+package directory and raises ImportError if it has not been built
+(``python -m linear_layer_backward_amd.build``); there is no fallback.
+
+The functions named like the C entry points take raw device addresses
+(ints) or torch tensors (their ``data_ptr()`` is passed) and raise
+``MmbError`` on a non-zero status, except ``mmb_check_args`` and
+``mmb_path``, which return the status like their C counterparts.
+``backward`` is the tensor-level convenience: it infers B, T, C, OC and the
+dtype from the tensors and enqueues on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libmmb.so")
+
+MMB_FP32 = 0
+MMB_BF16 = 1
+
+STATUS = {
+    0: "MMB_OK", -1: "MMB_ERR_NULL", -2: "MMB_ERR_DIM", -3: "MMB_ERR_DTYPE",
+    -4: "MMB_ERR_OVERFLOW", -5: "MMB_ERR_ALIAS", -6: "MMB_ERR_HIP", -7: "MMB_ERR_NOMEM",
+}
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(f"{LIBRARY} is not built; run `python -m linear_layer_backward_amd.build`")
+
+_lib = ctypes.CDLL(LIBRARY)
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_ARGS = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i]
+_lib.mmb_backward.argtypes = _ARGS
+_lib.mmb_backward.restype = _i
+_lib.mmb_backward_stream.argtypes = _ARGS + [_vp]
+_lib.mmb_backward_stream.restype = _i
+_lib.mmb_check_args.argtypes = _ARGS
+_lib.mmb_check_args.restype = _i
+_lib.mmb_path.argtypes = _ARGS
+_lib.mmb_path.restype = _i
+_lib.mmb_strerror.argtypes = [_i]
+_lib.mmb_strerror.restype = ctypes.c_char_p
+_lib.mmb_plan_units.argtypes = [_i] * 7 + [ctypes.POINTER(_i), ctypes.POINTER(_i), _i]
+_lib.mmb_plan_units.restype = _i
+_lib.mmb_release.argtypes = []
+_lib.mmb_release.restype = _i
+
+
+class MmbError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {mmb_strerror(status)}")
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype):
+    return (_addr(dinp), _addr(dweight), _addr(dbias), _addr(dout), _addr(inp),
+            _addr(weight), int(B), int(T), int(C), int(OC), int(dtype))
+
+
+def mmb_strerror(status: int) -> str:
+    return _lib.mmb_strerror(int(status)).decode()
+
+
+def mmb_check_args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype) -> int:
+    return _lib.mmb_check_args(*_args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype))
+
+
+def mmb_path(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype) -> int:
+    return _lib.mmb_path(*_args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype))
+
+
+def mmb_backward(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype) -> None:
+    st = _lib.mmb_backward(*_args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype))
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_backward_stream(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype,
+                        stream) -> None:
+    s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
+    st = _lib.mmb_backward_stream(*_args(dinp, dweight, dbias, dout, inp, weight,
+                                         B, T, C, OC, dtype), s or None)
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_release() -> None:
+    st = _lib.mmb_release()
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_plan_units(B, T, C, OC, dtype, has_bias, num_cus):
+    """(splits {dweight, dinp}, list of (kind, tile_m, tile_n, split)) of the
+    plan for a device with num_cus compute units.  Host only."""
+    sp = (_i * 2)()
+    n = _lib.mmb_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, None, 0)
+    if n < 0:
+        raise MmbError(n)
+    buf = (_i * (4 * n))()
+    _lib.mmb_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, buf, n)
+    return (sp[0], sp[1]), [tuple(buf[4 * k:4 * k + 4]) for k in range(n)]
+
+
+def torch_dtype_code(dt) -> int:
+    import torch
+    if dt == torch.float32:
+        return MMB_FP32
+    if dt == torch.bfloat16:
+        return MMB_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def backward(dinp, dweight, dbias, dout, inp, weight, B=None, T=None, stream=None) -> None:
+    """dinp += dout.weight, dweight += dout^T.inp, dbias = sum of dout rows.
+
+    Tensors: contiguous, on one GPU, all float32 or all bfloat16.  dout is
+    [B, T, OC] (or [B*T, OC] with B and T given), inp/dinp hold B*T*C
+    elements, weight/dweight OC*C, dbias OC or None.  Enqueued on `stream`
+    (default: torch's current stream of dout's device)."""
+    import torch
+    ts = [dinp, dweight, dout, inp, weight] + ([dbias] if dbias is not None else [])
+    dt = dout.dtype
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.device != dout.device:
+            raise ValueError("tensors must be contiguous, on one GPU, and share one dtype")
+    OC = dout.shape[-1]
+    if B is None or T is None:
+        if dout.dim() != 3:
+            raise ValueError("give B and T for a 2-D dout")
+        B, T = dout.shape[0], dout.shape[1]
+    if dout.numel() != B * T * OC or weight.numel() % OC != 0:
+        raise ValueError("inconsistent shapes")
+    C = weight.numel() // OC
+    if inp.numel() != B * T * C or dinp.numel() != B * T * C or dweight.numel() != OC * C:
+        raise ValueError("inconsistent shapes")
+    if dbias is not None and dbias.numel() != OC:
+        raise ValueError("dbias must hold OC elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(dout.device)
+    with torch.cuda.device(dout.device):
+        mmb_backward_stream(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC,
+                            torch_dtype_code(dt), stream)

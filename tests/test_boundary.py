@@ -1,0 +1,158 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/mmb.h declares, validates arguments and plans work.
+Pointers here are fake addresses; nothing dereferences them."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmb.h")
+
+
+@pytest.fixture(scope="module")
+def mmb():
+    lib = os.path.join(ROOT, "linear_layer_backward_amd", "libmmb.so")
+    if not os.path.exists(lib):
+        from linear_layer_backward_amd import build
+        build.build()
+    from linear_layer_backward_amd import mmb as m
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mmb_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for f in ("mmb_backward", "mmb_backward_stream", "mmb_check_args", "mmb_strerror",
+              "mmb_release", "mmb_path", "mmb_plan_units"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(mmb):
+    out = subprocess.run(["nm", "-D", "--defined-only", mmb.LIBRARY], check=True,
+                         stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (mmb_\w+)$", out, flags=re.M))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    # exported C names only: nothing mangled from the mmb namespace leaks as T
+    for f in declared_functions():
+        assert hasattr(mmb._lib, f)
+
+
+# fake, 256-byte aligned, well separated device addresses
+BASE = 1 << 40
+GAP = 1 << 44
+
+
+def addrs(n=6):
+    return [BASE + k * GAP for k in range(n)]
+
+
+def args(dtype=1, B=16, T=1024, C=768, OC=3072, bias=True):
+    dinp, dweight, dbias, dout, inp, weight = addrs()
+    return [dinp, dweight, dbias if bias else None, dout, inp, weight, B, T, C, OC, dtype]
+
+
+def test_valid_arguments(mmb):
+    assert mmb.mmb_check_args(*args()) == 0
+    assert mmb.mmb_check_args(*args(bias=False)) == 0
+    assert mmb.mmb_check_args(*args(dtype=0, B=1, T=1, C=1, OC=1)) == 0
+
+
+@pytest.mark.parametrize("idx", [0, 1, 3, 4, 5])
+def test_null_pointers(mmb, idx):
+    a = args()
+    a[idx] = None
+    assert mmb.mmb_check_args(*a) == -1
+
+
+@pytest.mark.parametrize("idx", [6, 7, 8, 9])
+@pytest.mark.parametrize("val", [0, -1])
+def test_bad_dims(mmb, idx, val):
+    a = args()
+    a[idx] = val
+    assert mmb.mmb_check_args(*a) == -2
+
+
+@pytest.mark.parametrize("dt", [-1, 2, 7])
+def test_bad_dtype(mmb, dt):
+    assert mmb.mmb_check_args(*args(dtype=dt)) == -3
+
+
+def test_overflow(mmb):
+    assert mmb.mmb_check_args(*args(B=65536, T=32768, C=8, OC=8)) == -4
+    assert mmb.mmb_check_args(*args(B=65535, T=32768, C=8, OC=8)) == 0
+
+
+def test_alias(mmb):
+    a = args(dtype=0, B=2, T=4, C=8, OC=8)  # fp32: dinp holds 64 floats = 256 B
+    a[1] = a[0] + 255                         # dweight starts inside dinp
+    assert mmb.mmb_check_args(*a) == -5
+    a[1] = a[0] + 256                         # adjacent, not overlapping
+    assert mmb.mmb_check_args(*a) == 0
+    b = args(dtype=1)
+    b[2] = b[3] + 2                           # dbias inside dout
+    assert mmb.mmb_check_args(*b) == -5
+    c = args(dtype=1)
+    c[0] = c[4]                               # dinp == inp
+    assert mmb.mmb_check_args(*c) == -5
+    d = args(dtype=1)
+    d[4] = d[5]                               # inputs may share memory
+    assert mmb.mmb_check_args(*d) == 0
+
+
+def test_strerror(mmb):
+    for st in range(-7, 1):
+        assert mmb.mmb_strerror(st)
+    assert "unknown" in mmb.mmb_strerror(-99)
+
+
+def test_path_choice(mmb):
+    assert mmb.mmb_path(*args(dtype=1)) == 1
+    assert mmb.mmb_path(*args(dtype=1, C=764)) == 0          # C % 8 for bf16
+    assert mmb.mmb_path(*args(dtype=0, C=764)) == 1          # C % 4 is enough for fp32
+    assert mmb.mmb_path(*args(dtype=0, OC=3070)) == 0
+    a = args(dtype=1)
+    a[4] += 8                                                  # inp only 8-byte aligned
+    assert mmb.mmb_path(*a) == 0
+    b = args(dtype=1)
+    b[2] += 2                                                  # dbias alignment is free
+    assert mmb.mmb_path(*b) == 1
+    assert mmb.mmb_path(*args(dtype=5)) == -3
+
+
+@pytest.mark.parametrize("shape", [
+    (16, 1024, 768, 3072, 1, True), (8, 1024, 768, 50304, 1, False),
+    (8, 1024, 768, 2304, 0, True), (8, 1024, 3072, 768, 0, True), (2, 16, 64, 192, 0, True),
+    (3, 100, 200, 328, 0, True), (1, 1, 8, 8, 1, True)])
+@pytest.mark.parametrize("cus", [256, 32])
+def test_plan_covers_every_tile_and_split_once(mmb, shape, cus):
+    B, T, C, OC, dt, bias = shape
+    (sw, si), units = mmb.mmb_plan_units(B, T, C, OC, dt, bias, cus)
+    BM, BN, BK = (256, 192, 64) if dt == 1 else (128, 128, 32)
+    cd = lambda a, b: -(-a // b)
+    expect = set()
+    for s in range(sw):
+        for m in range(cd(OC, BM)):
+            for n in range(cd(C, BN)):
+                expect.add((0, m, n, s))
+    for s in range(si):
+        for m in range(cd(B * T, BM)):
+            for n in range(cd(C, BN)):
+                expect.add((1, m, n, s))
+    assert len(units) == len(expect)
+    assert set(units) == expect
+    assert 1 <= sw <= cd(B * T, BK) and 1 <= si <= cd(OC, BK)
+
+
+def test_plan_split_override(mmb, monkeypatch):
+    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", "3")
+    monkeypatch.setenv("MMB_SPLITS_DINP", "2")
+    (sw, si), units = mmb.mmb_plan_units(2, 150, 264, 400, 1, True, 256)
+    assert (sw, si) == (3, 2)

@@ -1,0 +1,352 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Tolerance (per output tensor): max|gpu - oracle| / max|oracle| <= 1e-4 for
+fp32 storage and <= 2e-2 for bf16 storage.  With integer inputs every partial
+sum is an exact integer, so there fp32 results must equal the oracle bit for
+bit and bf16 results must equal the oracle's exact value rounded once to
+nearest-even bf16.
+
+Small shapes compare every element; the full workload shapes compare sampled
+rows of dinp and dweight (computed one by one by the oracle) and all of dbias.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_layer_backward_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+# ---------------------------------------------------------------------------
+# helpers
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from linear_layer_backward_amd import mmb  # noqa: F401  (fails loudly if unbuilt)
+    return torch.device("cuda:0")
+
+
+def to_dev(x, dtype, dev, guard=0, fill=None):
+    """Upload values x (float32, representable in dtype) as a flat buffer.
+    With guard > 0 the buffer gets `guard` canary elements on each side; the
+    returned view covers the payload only."""
+    import torch
+    raw = wl.storage(np.asarray(x, np.float32).ravel(), dtype)
+    if dtype == "bf16":
+        t = torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(raw.copy())
+    if guard:
+        canary = torch.full((guard,), 12288.0 if fill is None else fill, dtype=t.dtype)
+        full = torch.cat([canary, t, canary]).to(dev)
+        return full, full[guard:guard + t.numel()]
+    return None, t.to(dev)
+
+
+def from_dev(t, dtype):
+    import torch
+    if dtype == "bf16":
+        raw = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        raw = t.detach().cpu().numpy()
+    return wl.from_storage(raw, dtype).astype(np.float64)
+
+
+def run(case, dev, dbias_fill=0.0, guard=0, stream=None):
+    """Run the library on a Case; returns (dinp, dweight, dbias) as float64
+    and, with guard > 0, the full guarded buffers for canary checks."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    dt = case.dtype
+    _, dout = to_dev(case.dout, dt, dev)
+    _, inp = to_dev(case.inp, dt, dev)
+    _, w = to_dev(case.weight, dt, dev)
+    gi_full, gi = to_dev(case.dinp0, dt, dev, guard)
+    gw_full, gw = to_dev(case.dweight0, dt, dev, guard)
+    gb_full = gb = None
+    if case.with_bias:
+        gb_full, gb = to_dev(np.full(case.OC, dbias_fill, np.float32), dt, dev, guard)
+    mmb.mmb_backward_stream(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC,
+                            mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32,
+                            stream if stream is not None else torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    out = (from_dev(gi, dt).reshape(case.BT, case.C), from_dev(gw, dt).reshape(case.OC, case.C),
+           from_dev(gb, dt) if gb is not None else None)
+    if guard:
+        return out, (gi_full, gw_full, gb_full)
+    return out
+
+
+def rel_err(g, r):
+    scale = np.max(np.abs(r))
+    diff = np.max(np.abs(g - r))
+    return diff / scale if scale > 0 else diff
+
+
+def assert_close(g, r, dtype, what):
+    e = rel_err(g, r)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    assert e <= TOL[dtype], f"{what}: max rel err {e:.3e} > {TOL[dtype]:.0e}"
+
+
+def round_bf16(x):
+    """Exact values (|x| < 2^24 integers) -> nearest-even bf16, as float64."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def check_full(case, got):
+    gi, gw, gb = got
+    ri, rw, rb = oracle.case_backward(case)
+    assert_close(gi, ri, case.dtype, "dinp")
+    assert_close(gw, rw, case.dtype, "dweight")
+    if case.with_bias:
+        assert_close(gb, rb, case.dtype, "dbias")
+
+
+def check_exact(case, got, rows=None, chans=None):
+    """Integer inputs: bit-exact comparison (bf16 after one rounding)."""
+    gi, gw, gb = got
+    if rows is None:
+        ri, rw, rb = oracle.case_backward(case)
+    else:
+        ri, rw, rb = sampled_oracle(case, rows, chans)
+        gi, gw = gi[rows], gw[chans]
+    fix = round_bf16 if case.dtype == "bf16" else (lambda v: v)
+    np.testing.assert_array_equal(gi, fix(ri))
+    np.testing.assert_array_equal(gw, fix(rw))
+    if case.with_bias:
+        np.testing.assert_array_equal(gb, fix(rb))
+
+
+def sampled_oracle(case, rows, chans):
+    ri = oracle.dinp(case.dout[rows], case.weight, case.dinp0[rows],
+                     B=1, T=len(rows), C=case.C, OC=case.OC)
+    rw = oracle.dweight(case.dout[:, chans], case.inp, case.dweight0[chans],
+                        B=case.B, T=case.T, C=case.C, OC=len(chans))
+    rb = oracle.dbias(case.dout, B=case.B, T=case.T, OC=case.OC) if case.with_bias else None
+    return ri, rw, rb
+
+
+def sample(n, edges, k, seed):
+    """Edge indices (tile boundaries, ends) plus k random ones, sorted."""
+    rng = np.random.default_rng(seed)
+    s = {e for e in edges if 0 <= e < n} | set(rng.integers(0, n, size=min(k, n)).tolist())
+    return np.array(sorted(s))
+
+
+def tile_edges(n, tile):
+    out = [0, 1, n - 1, n - 2]
+    for t in range(tile, n, tile):
+        out += [t - 1, t]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# small shapes: every element
+
+SMALL = [
+    # (B, T, C, OC, dtype): MFMA path, several tiles, ragged tails in M, N, K
+    (2, 16, 64, 192, "f32"),
+    (3, 100, 200, 328, "f32"),
+    (1, 300, 132, 260, "f32"),
+    (2, 150, 264, 400, "bf16"),
+    (1, 513, 200, 136, "bf16"),
+    (1, 1, 8, 8, "bf16"),
+    (1, 1, 4, 4, "f32"),
+    # generic path: C or OC not a multiple of the vector width
+    (2, 7, 65, 129, "f32"),
+    (3, 5, 33, 17, "bf16"),
+    (1, 3, 12, 10, "bf16"),
+]
+
+
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_random(dev, shape, bias):
+    B, T, C, OC, dt = shape
+    case = wl.random_case(B, T, C, OC, dt, seed=B * 7 + T, with_bias=bias)
+    check_full(case, run(case, dev))
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_integer_exact(dev, shape):
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=B + T + C)
+    check_exact(case, run(case, dev))
+
+
+@pytest.mark.parametrize("splits", [(2, 1), (3, 2), (5, 3), (1, 4)])
+@pytest.mark.parametrize("shape", [(3, 100, 200, 328, "f32"), (2, 150, 264, 400, "bf16")],
+                         ids=["f32", "bf16"])
+def test_forced_splits(dev, monkeypatch, shape, splits):
+    """The split-K / last-arriver path at every split count, exact and random."""
+    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", str(splits[0]))
+    monkeypatch.setenv("MMB_SPLITS_DINP", str(splits[1]))
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=3)
+    check_exact(case, run(case, dev))
+    case = wl.random_case(B, T, C, OC, dt, seed=4)
+    check_full(case, run(case, dev))
+
+
+def test_cfg1_tiny(dev):
+    case = wl.config_cases(1)[0]
+    check_full(case, run(case, dev))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_dbias_is_assigned(dev, dt):
+    """dbias starts as NaN and must be overwritten with the column sums."""
+    case = wl.random_case(2, 50, 64, 96, dt, seed=9)
+    gi, gw, gb = run(case, dev, dbias_fill=float("nan"))
+    check_full(case, (gi, gw, gb))
+
+
+@pytest.mark.parametrize("shape", [(2, 150, 264, 400, "bf16"), (3, 100, 200, 328, "f32"),
+                                   (2, 7, 65, 129, "f32")], ids=["bf16", "f32", "generic"])
+def test_guard_bands(dev, shape):
+    """Nothing outside the output tensors is written."""
+    B, T, C, OC, dt = shape
+    case = wl.random_case(B, T, C, OC, dt, seed=12)
+    got, fulls = run(case, dev, guard=4096)
+    check_full(case, got)
+    for f in fulls:
+        head = from_dev(f[:4096], dt)
+        tail = from_dev(f[-4096:], dt)
+        assert np.all(head == 12288.0) and np.all(tail == 12288.0)
+
+
+@pytest.mark.parametrize("split", [None, "4"])
+def test_deterministic(dev, monkeypatch, split):
+    if split:
+        monkeypatch.setenv("MMB_SPLITS_DWEIGHT", split)
+    case = wl.random_case(4, 128, 256, 512, "bf16", seed=13)
+    a = run(case, dev)
+    b = run(case, dev)
+    for x, y in zip(a, b):
+        assert x.tobytes() == y.tobytes()
+
+
+def test_unaligned_pointers_take_generic_path(dev):
+    """A buffer that starts one element past an allocation is not 16-byte
+    aligned: the call must still be right (generic path)."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    case = wl.random_case(2, 20, 64, 96, "f32", seed=14)
+    _, dout = to_dev(np.concatenate([[0.0], case.dout.ravel()]), "f32", dev)
+    dout = dout[1:]
+    _, inp = to_dev(case.inp, "f32", dev)
+    _, w = to_dev(case.weight, "f32", dev)
+    _, gi = to_dev(case.dinp0, "f32", dev)
+    _, gw = to_dev(case.dweight0, "f32", dev)
+    _, gb = to_dev(np.zeros(case.OC, np.float32), "f32", dev)
+    assert mmb.mmb_path(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, 0) == 0
+    mmb.mmb_backward(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, 0)
+    torch.cuda.synchronize()
+    check_full(case, (from_dev(gi, "f32").reshape(case.BT, case.C),
+                      from_dev(gw, "f32").reshape(case.OC, case.C), from_dev(gb, "f32")))
+
+
+def test_accumulates_across_calls(dev):
+    """Two calls add the gradient twice (beta = 1), exactly with integers."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    case = wl.integer_case(2, 64, 128, 192, "f32", seed=15)
+    _, dout = to_dev(case.dout, "f32", dev)
+    _, inp = to_dev(case.inp, "f32", dev)
+    _, w = to_dev(case.weight, "f32", dev)
+    _, gi = to_dev(case.dinp0, "f32", dev)
+    _, gw = to_dev(case.dweight0, "f32", dev)
+    _, gb = to_dev(np.zeros(case.OC, np.float32), "f32", dev)
+    for _ in range(2):
+        mmb.mmb_backward(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, 0)
+    torch.cuda.synchronize()
+    ri, rw, rb = oracle.case_backward(case)
+    np.testing.assert_array_equal(from_dev(gi, "f32").reshape(case.BT, case.C),
+                                  2 * ri - case.dinp0)
+    np.testing.assert_array_equal(from_dev(gw, "f32").reshape(case.OC, case.C),
+                                  2 * rw - case.dweight0)
+    np.testing.assert_array_equal(from_dev(gb, "f32"), rb)
+
+
+def test_side_stream(dev):
+    import torch
+    s = torch.cuda.Stream(dev)
+    case = wl.random_case(2, 150, 264, 400, "bf16", seed=16)
+    check_full(case, run(case, dev, stream=s))
+
+
+def test_tensor_binding(dev):
+    """mmb.backward infers shapes and dtype from torch tensors."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    case = wl.random_case(2, 64, 128, 256, "f32", seed=17)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    gi, gw, gb = t(case.dinp0), t(case.dweight0), t(np.zeros(case.OC, np.float32))
+    mmb.backward(gi, gw, gb, t(case.dout).view(case.B, case.T, case.OC), t(case.inp),
+                 t(case.weight))
+    torch.cuda.synchronize()
+    check_full(case, (gi.cpu().numpy().astype(np.float64), gw.cpu().numpy().astype(np.float64),
+                      gb.cpu().numpy().astype(np.float64)))
+
+
+# ---------------------------------------------------------------------------
+# full workload shapes: sampled rows
+
+def check_sampled(case, got, seed, exact=False):
+    gi, gw, gb = got
+    BM = 256 if case.dtype == "bf16" else 128
+    rows = sample(case.BT, tile_edges(case.BT, BM), 24, seed)
+    chans = sample(case.OC, tile_edges(case.OC, BM) + list(range(case.OC - 48, case.OC)), 24,
+                   seed + 1)
+    if exact:
+        check_exact(case, got, rows, chans)
+        return
+    ri, rw, rb = sampled_oracle(case, rows, chans)
+    assert_close(gi[rows], ri, case.dtype, "dinp (sampled rows)")
+    assert_close(gw[chans], rw, case.dtype, "dweight (sampled rows)")
+    if case.with_bias:
+        assert_close(gb, rb, case.dtype, "dbias")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_config(dev, cfg):
+    for case in wl.config_cases(cfg):
+        print(f"[parity] {case.name}", flush=True)
+        got = run(case, dev)
+        check_sampled(case, got, seed=cfg)
+        if cfg == 5:
+            # padded vocabulary rows of dweight stay exactly zero
+            assert np.all(got[1][wl.GPT2_VOCAB:] == 0.0)
+
+
+@pytest.mark.parametrize("shape", [(8, 1024, 768, 2304, "f32"), (8, 1024, 3072, 768, "f32"),
+                                   (16, 1024, 768, 3072, "bf16"), (8, 1024, 768, 50304, "bf16")],
+                         ids=["qkv", "fc_proj", "fc_bf16", "lm_head"])
+def test_full_shape_integer_exact(dev, shape):
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=OC, with_bias=OC != 50304, prefill=True)
+    print(f"[parity] {case.name}", flush=True)
+    check_sampled(case, run(case, dev), seed=5, exact=True)
+
+
+def test_plan_changes_between_calls(dev, monkeypatch):
+    """Shapes and split plans alternate on one stream; the workspace is
+    reused and regrown, and every result stays exact."""
+    seq = [((3, 100, 200, 328, "f32"), "5"), ((2, 150, 264, 400, "bf16"), "3"),
+           ((8, 64, 256, 512, "bf16"), "2"), ((3, 100, 200, 328, "f32"), "4"),
+           ((2, 150, 264, 400, "bf16"), "5")]
+    for n, ((B, T, C, OC, dt), sw) in enumerate(seq):
+        monkeypatch.setenv("MMB_SPLITS_DWEIGHT", sw)
+        case = wl.integer_case(B, T, C, OC, dt, seed=40 + n)
+        check_exact(case, run(case, dev))
