@@ -1,5 +1,6 @@
-// mmb_tiles.hip -- the MFMA path: both GEMMs of the linear-layer backward
-// pass and the bias reduction in one launch of output-tile work units.
+// mmb_tiles.hip -- fp32 MFMA tiles of the linear-layer backward pass: both
+// GEMMs and the bias reduction in one launch of output-tile work units (the
+// bf16 tiles live in mmb_tiles_bf16.hip).
 //
 // Operation (llm.c page "dev/cuda/matmul_backward.cu", launcher
 // matmul_backward1 and bias kernels):
@@ -7,55 +8,37 @@
 //   dweight [OC,C] += dout^T[OC,BT] . inp[BT,C]       (unit kind UNIT_DWEIGHT)
 //   dbias   [OC]    = column sums of dout             (inside dweight units
 //                                                      of output column tile 0)
+// The page's check runs its GEMMs in true fp32 (TF32 off); so do these:
+// v_mfma_f32_32x32x2_f32 multiplies and accumulates in fp32.
 //
 // gfx950 design:
-//  * One workgroup = 4 wave64s = one output tile (BM x BN), each wave a
-//    2 x 2 quarter of it built from 32x32 MFMA blocks (bf16: 32x32x16 with
-//    fp32 accumulators; fp32: 32x32x2 fp32, no reduced-precision products).
+//  * One workgroup = 4 wave64s = one 128 x 128 output tile, each wave a
+//    64 x 64 quarter (2 x 2 blocks of 32x32 MFMA).  64 KB of LDS, so two
+//    workgroups share a CU.
 //  * Operands are staged global -> registers -> LDS with a 2-stage ping-pong
 //    (the loads of stage k+1 are in flight while the MFMAs of stage k run;
-//    one barrier per stage).  LDS always holds K-contiguous rows of 128
-//    bytes, so every MFMA fragment is one ds_read_b128.  Operands stored
-//    K-strided in HBM (weight, inp, and dout for dweight) are transposed in
-//    registers, E x E elements per thread, on the way in.  The 16-byte chunk
-//    c of LDS row r lives at chunk c ^ (r & 7): conflict-free for the
-//    fragment reads (8 rows, same chunk) and the staging writes (1 row,
-//    8 chunks).
-//  * The MFMA "A" input is the N-side tile and "B" the M-side tile, so each
-//    lane's accumulator holds 4 consecutive output columns: 16-byte fp32 /
-//    8-byte bf16 epilogue accesses along the contiguous output dimension.
-//  * dweight's long reduction (K = B*T) is split over several units; each
-//    writes its fp32 partial tile to the workspace and takes a ticket; the
-//    last arriver adds the partials in split order (deterministic), adds the
-//    old output (beta = 1), rounds once, stores, and resets the ticket.
-//  * dbias: the dweight units of column tile 0 already stream the dout
-//    columns of their rows; each thread sums the dout values it stages, a
-//    3-step xor shuffle combines the 8 threads that share a column, and split
-//    partials go through the same last-arriver path.
-//  * Operands are read at 16-byte granularity; C and OC are multiples of the
-//    vector width on this path, so a vector is wholly inside or outside a
-//    ragged edge, which is zero-filled on load and masked on store.
-#include "mmb_internal.h"
-#include "mmb_numeric.h"
+//    one barrier per stage).  LDS holds K-contiguous rows of 128 bytes (32
+//    floats); the 16-byte chunk c of row r lives at c ^ (r & 7), so fragment
+//    reads (8 rows, one chunk) and staging writes (1 row, 8 chunks) are
+//    conflict-free.  Operands that are K-strided in memory (weight, inp, and
+//    dout for dweight) are transposed 4 x 4 in registers on the way in.
+//  * Each lane reads 4 consecutive K of a row with one ds_read_b128; the
+//    four MFMAs of a group of 8 K take element q of both operands (lane half
+//    h covers K = 8s + 4h + q), which covers all 8 K exactly once.
+//  * The MFMA "A" input is the N-side tile, so each lane's accumulators hold
+//    4 consecutive output columns (16-byte epilogue accesses).
+//  * Split K (dweight's K = B*T): partial tiles, tickets and the ordered
+//    last-arriver sum are the shared helpers of mmb_tile_common.h.
+//  * dbias: the dweight units of column tile 0 sum the dout values they
+//    stage; a 3-step xor shuffle combines the 8 threads sharing a column.
+#include "mmb_tile_common.h"
 
 namespace mmb {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;  // one LDS row: BK elements of one m or n
+constexpr int kRowBytes = 128;  // one LDS row: BK floats of one m or n  // one LDS row: BK elements of one m or n
 
 template <typename T> struct Cfg;
-template <> struct Cfg<bf16_t> {
-    static constexpr int BM = 256, BN = 192, BK = 64;
-    static constexpr int E = 8;               // elements per 16-byte vector
-    static constexpr int WM = 128, WN = 96;   // wave tile
-};
 template <> struct Cfg<float> {
     static constexpr int BM = 128, BN = 128, BK = 32;
     static constexpr int E = 4;
@@ -82,16 +65,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // ---- E x E transpose of one staged block ---------------------------------
 // in[r] holds E consecutive columns of K-row r; out[x] gets E consecutive
 // K-rows of column x.
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8], bf16_t) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int d = x >> 1;
-        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            out[x][p] = __builtin_amdgcn_perm(in[2 * p + 1][d], in[2 * p][d], sel);
-    }
-}
 __device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4], float) {
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -100,15 +73,6 @@ __device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&ou
 }
 
 // column sums of a staged block (dbias), fp32
-__device__ __forceinline__ void add_columns(const u32x4 (&in)[8], float (&s)[8], bf16_t) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            s[2 * d] += __uint_as_float(in[r][d] << 16);
-            s[2 * d + 1] += __uint_as_float(in[r][d] & 0xffff0000u);
-        }
-}
 __device__ __forceinline__ void add_columns(const u32x4 (&in)[4], float (&s)[4], float) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -154,27 +118,6 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, int wm
                             acc[mb][nb], 0, 0, 0);
         }
     }
-}
-
-// ---- epilogue helpers -----------------------------------------------------
-__device__ __forceinline__ void store4(float* d, f32x4 v, bool accumulate) {
-    f32x4 o = v;
-    if (accumulate) o += *(const f32x4*)d;
-    *(f32x4*)d = o;
-}
-__device__ __forceinline__ void store4(bf16_t* d, f32x4 v, bool accumulate) {
-    f32x4 o = v;
-    if (accumulate) {
-        const u32x2 old = *(const u32x2*)d;
-        o[0] += __uint_as_float(old[0] << 16);
-        o[1] += __uint_as_float(old[0] & 0xffff0000u);
-        o[2] += __uint_as_float(old[1] << 16);
-        o[3] += __uint_as_float(old[1] & 0xffff0000u);
-    }
-    u32x2 r;
-    r[0] = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-    r[1] = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-    *(u32x2*)d = r;
 }
 
 // ---- one work unit ---------------------------------------------------------
@@ -303,83 +246,27 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         }
     }
 
-    const int lr = lane & 31, half = lane >> 5;
+    const bool bias_owner = do_bias && kg == 0 && a_active;
     if (g.splits > 1) {
-        // 1. publish this split's partial tile (fragment order, 16-byte stores)
         const int tile = tile_m * g.tiles_n + tile_n;
-        float* wt = p.ws + g.ws_base + ((long long)tile * g.splits + split) * (BM * BN);
+        float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
+        publish_partial<Kt::MB, Kt::NB>(w0 + (long long)split * (BM * BN), acc, tid);
+        float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + xg * E;
+        if (bias_owner) {
 #pragma unroll
-        for (int mb = 0; mb < Kt::MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < Kt::NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
-                               acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
-                    *(f32x4*)(wt + ((mb * Kt::NB + nb) * 4 + q) * (kThreads * 4) + tid * 4) = v;
-                }
-        if (do_bias && kg == 0 && a_active) {
-            float* wb = p.ws_bias + ((long long)tile_m * g.splits + split) * BM + xg * E;
-#pragma unroll
-            for (int x = 0; x < E; ++x) wb[x] = bsum[x];
+            for (int x = 0; x < E; ++x) publish_bias(wb + split * BM + x, bsum[x]);
         }
-        // 2. take a ticket; the last of the tile's splits finishes it
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const int prev = atomicAdd(p.counters + g.tile_base + tile, 1);
-            *s_flag = (prev == g.splits - 1);
-        }
-        __syncthreads();
-        if (!*s_flag) return;
-        __threadfence();
-        // 3. sum the partials in split order
-        const float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
+        if (!arrive_last(p.counters + g.tile_base + tile, g.splits, s_flag)) return;
+        sum_partials<Kt::MB, Kt::NB>(w0, g.splits, BM * BN, acc, tid);
+        if (bias_owner) {
 #pragma unroll
-        for (int mb = 0; mb < Kt::MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < Kt::NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int off = ((mb * Kt::NB + nb) * 4 + q) * (kThreads * 4) + tid * 4;
-                    f32x4 mine = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
-                                  acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
-                    f32x4 s = split == 0 ? mine : *(const f32x4*)(w0 + off);
-                    for (int sp = 1; sp < g.splits; ++sp)
-                        s += sp == split ? mine : *(const f32x4*)(w0 + (long long)sp * (BM * BN) + off);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[mb][nb][4 * q + r] = s[r];
-                }
-        if (do_bias && kg == 0 && a_active) {
-            const float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + xg * E;
-#pragma unroll
-            for (int x = 0; x < E; ++x) {
-                float s = split == 0 ? bsum[x] : wb[x];
-                for (int sp = 1; sp < g.splits; ++sp)
-                    s += sp == split ? bsum[x] : wb[(long long)sp * BM + x];
-                bsum[x] = s;
-            }
+            for (int x = 0; x < E; ++x) bsum[x] = sum_bias(wb + x, g.splits, BM);
         }
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
-    // 4. output tile: D = old + acc (rounded once), dbias = sum
-#pragma unroll
-    for (int mb = 0; mb < Kt::MB; ++mb) {
-        const int m = m0 + wm0 + mb * 32 + lr;
-        if (m >= M) continue;
-#pragma unroll
-        for (int nb = 0; nb < Kt::NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn0 + nb * 32 + 8 * q + 4 * half;
-                if (n >= N) continue;
-                f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
-                           acc[mb][nb][4 * q + 3]};
-                store4(D + (long long)m * ldd + n, v, true);
-            }
-    }
-    if (do_bias && kg == 0 && a_active) {
+    write_tile<T, Kt::MB, Kt::NB>(D, ldd, M, N, m0 + wm0, n0 + wn0, acc, lane);
+    if (bias_owner) {
         T* db = (T*)p.dbias;
 #pragma unroll
         for (int x = 0; x < E; ++x) {
@@ -403,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void mmb_tiles_kernel(TilesParams p) {
 }  // namespace
 
 TileShape tile_shape(int dtype) {
-    if (dtype == 1) return TileShape{K<bf16_t>::BM, K<bf16_t>::BN, K<bf16_t>::BK};
+    if (dtype == 1) return TileShape{256, 192, tiles_bf16_bk()};
     return TileShape{K<float>::BM, K<float>::BN, K<float>::BK};
 }
 

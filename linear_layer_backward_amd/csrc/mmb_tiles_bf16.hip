@@ -7,28 +7,32 @@
 //
 // gfx950 design (one workgroup = 4 wave64s = one 256 x 192 output tile; each
 // wave owns a 128 x 96 quarter = 4 x 3 blocks of v_mfma_f32_32x32x16_bf16):
-//  * Staging: global -> VGPR -> LDS, two LDS stages of K depth 64 (64 KB
-//    each), loads of stage k+1 in flight during the MFMAs of stage k, one
-//    barrier per stage.  All loads are raw buffer loads: a lane whose 16-byte
-//    vector is outside the operand gets offset 2^31 and reads zeros, so the
-//    loop has no branches.
+//  * Staging: operands go from HBM straight into LDS with buffer loads in LDS
+//    mode (16 bytes per lane, no VGPR staging), through a ring of NS stages
+//    of K depth 32 (32 KB each).  NS-1 stages are in flight while one is
+//    consumed; each wave waits for its own loads with an explicit vmcnt and
+//    one barrier per stage publishes the stage and retires the previous one.
+//    These loads are issued from inline assembly because the compiler would
+//    otherwise wait for every outstanding LDS load before any LDS read.
+//  * A lane whose 16-byte vector lies outside the operand gets buffer offset
+//    2^31 and writes zeros; rows past the end fall outside the buffer range.
 //  * LDS keeps each operand in its memory orientation:
-//      - dout for dinp (K-contiguous rows): [256 rows][64 k], 128-byte rows,
-//        16-byte chunk c stored at c ^ (row & 7); MFMA fragments are one
-//        ds_read_b128 per lane.
-//      - weight, inp and dout-for-dweight (M/N-contiguous rows): [64 k][256
+//      - dout for dinp (K-contiguous): [256 rows][32 k], 64-byte rows, chunk
+//        c stored at c ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); fragments are
+//        ds_read_b128.
+//      - weight, inp and dout-for-dweight (M/N-contiguous): [32 k][256
 //        columns], 512-byte rows, chunk c stored at c ^ {0,10,4,14}[row & 3];
-//        MFMA fragments are two ds_read_b64_tr_b16 per lane, the gfx950 LDS
+//        fragments are two ds_read_b64_tr_b16 per lane, the gfx950 LDS
 //        transpose read (lane l of each 16-lane group receives element l%4
-//        of the 8 bytes read by lane 4e + (l%16)/4, e = 0..3, giving four
+//        of the 8 bytes read by lane 4e + (l%16)/4, e = 0..3, i.e. four
 //        consecutive K values of one column).  No VALU transposes.
-//    Both swizzles keep the 16-lane groups of the transpose reads and the
-//    8-lane groups of the 16-byte writes on distinct banks.
+//    Both swizzles keep the 8-lane groups of 16-byte reads and the 16-lane
+//    groups of transpose reads on distinct banks.
 //  * The MFMA "A" input is the N-side fragment, so each lane's accumulator
 //    registers hold 4 consecutive output columns (8-byte bf16 epilogue).
-//  * dbias: dweight units of column tile 0 sum the dout vectors they stage
-//    (fp32), combine lanes l and l+32 by a shuffle and the 4 waves through
-//    LDS in a fixed order.
+//  * dbias: dweight units of column tile 0 also read their dout stage from
+//    LDS and sum it in fp32; lanes l and l+32 combine by a shuffle and the
+//    4 waves through LDS in a fixed order.
 //  * Split K (dweight's K = B*T): fp32 partial tiles in the workspace, the
 //    last arriver adds them in split order, adds the old output and rounds
 //    once to bf16.
@@ -37,37 +41,64 @@
 namespace mmb {
 namespace {
 
-constexpr int BM = 256, BN = 192, BK = 64;
+constexpr int BM = 256, BN = 192, BK = 32;
 constexpr int WM = 128, WN = 96, MB = WM / 32, NB = WN / 32;
-constexpr int KC_PITCH = 128;   // K-contiguous LDS row: BK bf16
-constexpr int MN_PITCH = 512;   // M/N-contiguous LDS row: up to 256 bf16
-constexpr int REGION = 32768;   // one operand of one stage
+constexpr int NS = 4;            // LDS stages in the ring
+constexpr int KC_PITCH = 64;     // K-contiguous LDS row: BK bf16
+constexpr int MN_PITCH = 512;    // M/N-contiguous LDS row: up to 256 bf16
+constexpr int REGION = 16384;    // one operand of one stage
 constexpr int STAGE = 2 * REGION;
-constexpr int LDS_BYTES = 2 * STAGE;
+constexpr int LDS_BYTES = NS * STAGE;
+constexpr int LOADS_PER_STAGE = 8;  // 16-byte-per-lane loads per wave per stage
 static_assert(BM * KC_PITCH == REGION && BK * MN_PITCH == REGION, "regions");
+static_assert(REGION / (4 * 1024) * 2 == LOADS_PER_STAGE, "loads per wave");
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // chunk XOR of M/N-contiguous rows, by row & 3: {0, 10, 4, 14}
 __device__ __forceinline__ int sw_mn(int row) { return (0xE4A0 >> ((row & 3) << 2)) & 0xF; }
-
-__device__ __forceinline__ int kc_addr(int row, int chunk) {
-    return row * KC_PITCH + ((chunk ^ (row & 7)) << 4);
-}
-__device__ __forceinline__ int mn_addr(int row, int chunk) {
-    return row * MN_PITCH + ((chunk ^ sw_mn(row)) << 4);
-}
+// chunk XOR of K-contiguous rows: distinct over any 8 rows of equal parity
+// and any 16 rows of equal row % 4 (both 32- and 64-bank LDS)
+__device__ __forceinline__ int sw_kc(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ bf16x4 tr_read(const char* region, int byte) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_char*)region + byte));
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(size_t)((const lds_char*)p);
+}
+
+// Buffer descriptor words (gfx9 raw buffer, dword3 0x00020000) over
+// [base, base + bytes), num_records clamped below 2^31.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, long long bytes) {
+    const uint64_t a = (uint64_t)base;
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), n, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(i32x4 r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most n of this wave's loads are outstanding (n uniform).
+__device__ __forceinline__ void wait_loads(int n) {
+    if (n >= 3 * LOADS_PER_STAGE) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (n >= 2 * LOADS_PER_STAGE) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n >= LOADS_PER_STAGE) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // MFMA fragment (8 consecutive K of one row) of a K-contiguous region:
 // lane l reads row xb + (l & 31), K chunk 2s + (l >> 5).
 __device__ __forceinline__ bf16x8 frag_kc(const char* region, int xb, int s, int lane) {
     const int row = xb + (lane & 31);
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)(region + kc_addr(row, 2 * s + (lane >> 5))));
+    const int chunk = (2 * s + (lane >> 5)) ^ sw_kc(row);
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(region + row * KC_PITCH + (chunk << 4)));
 }
 
 // The same fragment from an M/N-contiguous region with two transpose reads:
@@ -97,6 +128,7 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const int m0 = tile_m * BM, n0 = tile_n * BN;
     const int kt0 = (int)((long long)split * g.kiters / g.splits);
     const int kt1 = (int)((long long)(split + 1) * g.kiters / g.splits);
+    const int nk = kt1 - kt0;
 
     const bf16_t* A = (const bf16_t*)p.dout;
     const bf16_t* Bp = (const bf16_t*)(AK ? p.weight : p.inp);
@@ -106,75 +138,49 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const long long b_elems = AK ? (long long)p.OC * p.C : (long long)p.BT * p.C;
     const bool do_bias = !AK && p.dbias != nullptr && tile_n == 0;
 
-    // Staging geometry, fixed per thread.  Row masking comes from the buffer
-    // range (every operand ends at its last valid K row, or for dinp's A at
-    // row M); column masking from a precomputed out-of-range column offset,
-    // so the load loop has no selects for the compiler to turn into branches.
-    //   A, K-contiguous:  rows (tid>>3) + 32j, chunk tid&7 (K masked by AND)
-    //   A, M-contiguous:  K-rows (tid>>5) + 8j, chunk tid&31
-    //   B (waves 0-2):    K-rows tid/24 + 8j, chunk tid%24
-    const int a_c = AK ? (tid & 7) : (tid & 31);
-    const int a_r = AK ? (tid >> 3) : (tid >> 5);
-    const bool b_on = wave < 3;                     // wave-uniform
-    const int b_c = tid % 24, b_r = tid / 24;
-    const uint32_t a_coff = AK ? (uint32_t)(a_c * 16)
-                               : (m0 + 8 * a_c < M ? (uint32_t)((m0 + 8 * a_c) * 2) : kOOB);
-    const uint32_t b_coff = n0 + 8 * b_c < N ? (uint32_t)((n0 + 8 * b_c) * 2) : kOOB;
-    const uint32_t a_rstride = (uint32_t)((AK ? 32 : 8) * lda * 2);
-    const uint32_t a_roff = (uint32_t)(a_r * lda * 2);
-    const uint32_t b_rstride = (uint32_t)(8 * ldb * 2);
-    const uint32_t b_roff = (uint32_t)(b_r * ldb * 2);
-
-    u32x4 ra[8], rb[8];
-    float bsum[8];
+    // Load geometry.  Wave w's i-th load of a region fills its 1 KB block
+    // 4w + i; lane p lands at byte 16p of the block, so the lane fetches the
+    // global vector that belongs there under the swizzle.
+    //   K-contiguous A: block rows 16(4w+i) + p/4, physical chunk p%4
+    //   M/N-contiguous: block rows 2(4w+i) + p/32, physical chunk p%32
+    uint32_t a_off[4], b_off[4];
+    int a_kc = 0;   // K-contiguous A: K offset (elements) of this lane's vector
 #pragma unroll
-    for (int x = 0; x < 8; ++x) bsum[x] = 0.f;
-
-    auto load = [&](int kt) {
-        const int k0 = kt * BK;
-        {
-            const long long off0 = AK ? (long long)m0 * lda + k0 : (long long)k0 * lda;
-            const auto r = make_rsrc(A + off0, (a_elems - off0) * 2);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ra[j] = buffer_load16(r, a_roff + j * a_rstride + a_coff, 0);
-            if constexpr (AK) {
-                // K tail inside a row: zero the vectors at or past K
-                const uint32_t keep = (uint32_t)((k0 + 8 * a_c - Kd) >> 31);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ra[j] &= keep;
-            }
-        }
-        if (b_on) {
-            const long long off0 = (long long)k0 * ldb;
-            const auto r = make_rsrc(Bp + off0, (b_elems - off0) * 2);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) rb[j] = buffer_load16(r, b_roff + j * b_rstride + b_coff, 0);
-        }
-    };
-
-    auto store = [&](int stage) {
-        char* sa = smem + stage * STAGE;
-        char* sb = sa + REGION;
+    for (int i = 0; i < 4; ++i) {
         if constexpr (AK) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) *(u32x4*)(sa + kc_addr(a_r + 32 * j, a_c)) = ra[j];
+            const int row = 64 * wave + 16 * i + (lane >> 2);
+            const int c = (lane & 3) ^ sw_kc(row);
+            a_kc = 8 * c;
+            a_off[i] = (uint32_t)(row * lda * 2 + c * 16);
         } else {
-            if (do_bias) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        bsum[2 * d] += __uint_as_float(ra[j][d] << 16);
-                        bsum[2 * d + 1] += __uint_as_float(ra[j][d] & 0xffff0000u);
-                    }
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) *(u32x4*)(sa + mn_addr(a_r + 8 * j, a_c)) = ra[j];
+            const int row = 2 * (4 * wave + i) + (lane >> 5);
+            const int c = (lane & 31) ^ sw_mn(row);
+            const int col = m0 + 8 * c;
+            a_off[i] = col < M ? (uint32_t)((row * lda + col) * 2) : kOOB;
         }
-        if (b_on) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) *(u32x4*)(sb + mn_addr(b_r + 8 * j, b_c)) = rb[j];
+        {
+            const int row = 2 * (4 * wave + i) + (lane >> 5);
+            const int c = (lane & 31) ^ sw_mn(row);
+            const int col = n0 + 8 * c;
+            b_off[i] = (c < BN / 8 && col < N) ? (uint32_t)((row * ldb + col) * 2) : kOOB;
         }
+    }
+    const uint32_t smem_lds = lds_offset(smem);
+
+    auto issue = [&](int kt, int stage) {
+        const int k0 = kt * BK;
+        const uint32_t la = smem_lds + stage * STAGE + wave * 4096;
+        const uint32_t lb = la + REGION;
+        const long long oa = AK ? (long long)m0 * lda + k0 : (long long)k0 * lda;
+        const i32x4 ra = rsrc_words(A + oa, (a_elems - oa) * 2);
+        // K tail inside a K-contiguous row: vectors at or past K read zeros
+        const uint32_t kmask = AK ? (~(uint32_t)((k0 + a_kc - Kd) >> 31) & kOOB) : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(ra, a_off[i] | kmask, la + i * 1024);
+        const long long ob = (long long)k0 * ldb;
+        const i32x4 rb = rsrc_words(Bp + ob, (b_elems - ob) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(rb, b_off[i], lb + i * 1024);
     };
 
     f32x16 acc[MB][NB];
@@ -185,43 +191,92 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    float bsum[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) bsum[x] = 0.f;
+    // dbias: thread t sums column chunk t & 31 over K-rows (t >> 5) + 8j
+    const int bias_c = tid & 31, bias_r = tid >> 5;
+    const int bias_byte = bias_r * MN_PITCH + ((bias_c ^ sw_mn(bias_r)) << 4);
+
     const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
 
-    load(kt0);
-    store(0);
-    __syncthreads();
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int cur = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
-        if (more) load(kt + 1);
-        const char* sa = smem + cur * STAGE;
+    // Fragments of one 16-deep substep.
+    struct Frag {
+        bf16x8 a[NB];   // N side (MFMA input A)
+        bf16x8 b[MB];   // M side (MFMA input B)
+    };
+    auto read_sub = [&](int stage, int k, Frag& f) {
+        const char* sa = smem + stage * STAGE;
         const char* sb = sa + REGION;
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            bf16x8 fa[NB], fb[MB];
+        for (int nb = 0; nb < NB; ++nb) f.a[nb] = frag_mn(sb, wn0 + nb * 32, k, lane);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) fa[nb] = frag_mn(sb, wn0 + nb * 32, s, lane);
+        for (int mb = 0; mb < MB; ++mb)
+            f.b[mb] = AK ? frag_kc(sa, wm0 + mb * 32, k, lane) : frag_mn(sa, wm0 + mb * 32, k, lane);
+    };
+    auto bias_add = [&](int stage) {
+        const char* sa = smem + stage * STAGE;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                fb[mb] = AK ? frag_kc(sa, wm0 + mb * 32, s, lane) : frag_mn(sa, wm0 + mb * 32, s, lane);
+        for (int j = 0; j < BK / 8; ++j) {
+            const u32x4 v = *(const u32x4*)(sa + bias_byte + j * 8 * MN_PITCH);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[nb], fb[mb], acc[mb][nb],
-                                                                          0, 0, 0);
+            for (int d = 0; d < 4; ++d) {
+                bsum[2 * d] += __uint_as_float(v[d] << 16);
+                bsum[2 * d + 1] += __uint_as_float(v[d] & 0xffff0000u);
+            }
         }
-        if (more) store(cur ^ 1);
+    };
+    auto mma_sub = [&](const Frag& f) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[nb], f.b[mb], acc[mb][nb],
+                                                                      0, 0, 0);
+    };
+
+    // Ring of NS stages, NS-1 loaded ahead.  Iteration `it`: read the second
+    // substep of stage it while the MFMAs of its first substep run; then one
+    // barrier publishes stage it+1 (each wave has waited for its own loads
+    // of it) and retires stage it-1 (all its fragments were read before),
+    // whose buffer takes the loads of stage it+NS-1; then the first substep
+    // of stage it+1 is read while the MFMAs of the second substep of it run.
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+        if (i < nk) issue(kt0 + i, i);
+    Frag fa, fb;
+    if (nk > 0) {
+        const int issued = nk < NS - 1 ? nk : NS - 1;
+        wait_loads((issued - 1) * LOADS_PER_STAGE);
         __syncthreads();
+        read_sub(0, 0, fa);
+        if (do_bias) bias_add(0);
+    }
+    for (int it = 0; it < nk; ++it) {
+        read_sub(it % NS, 1, fb);
+        mma_sub(fa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + 1 < nk) {
+            const int ahead = nk - it - 2 < NS - 3 ? nk - it - 2 : NS - 3;
+            wait_loads(ahead * LOADS_PER_STAGE);
+            __syncthreads();
+            if (it + NS - 1 < nk) issue(kt0 + it + NS - 1, (it + NS - 1) % NS);
+            __builtin_amdgcn_sched_barrier(0);
+            read_sub((it + 1) % NS, 0, fa);
+            if (do_bias) bias_add((it + 1) % NS);
+        }
+        mma_sub(fb);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // dbias of this unit's 256 columns: lanes l, l^32 share a column chunk;
-    // the 4 waves meet in LDS (the stages are free after the last barrier)
+    // the 4 waves meet in LDS once every wave is done with the ring
     float bias = 0.f;
     if (do_bias) {
         float* red = (float*)smem;
 #pragma unroll
         for (int x = 0; x < 8; ++x) bsum[x] += __shfl_xor(bsum[x], 32);
+        __syncthreads();
         if (lane < 32) {
 #pragma unroll
             for (int x = 0; x < 8; ++x) red[wave * BM + lane * 8 + x] = bsum[x];
@@ -234,15 +289,11 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         const int tile = tile_m * g.tiles_n + tile_n;
         float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
         publish_partial<MB, NB>(w0 + (long long)split * (BM * BN), acc, tid);
-        float* wb = p.ws_bias + (long long)tile_m * g.splits * BM;
-        if (do_bias) wb[split * BM + tid] = bias;
+        float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + tid;
+        if (do_bias) publish_bias(wb + split * BM, bias);
         if (!arrive_last(p.counters + g.tile_base + tile, g.splits, s_flag)) return;
-        sum_partials<MB, NB>(w0, g.splits, split, BM * BN, acc, tid);
-        if (do_bias) {
-            float s = split == 0 ? bias : wb[tid];
-            for (int sp = 1; sp < g.splits; ++sp) s += sp == split ? bias : wb[sp * BM + tid];
-            bias = s;
-        }
+        sum_partials<MB, NB>(w0, g.splits, BM * BN, acc, tid);
+        if (do_bias) bias = sum_bias(wb, g.splits, BM);
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
@@ -252,15 +303,19 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
 
 __global__ __launch_bounds__(kThreads, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-    __shared__ int s_flag;
+    // the split-K ticket flag lives in the ring, used only after the K loop
+    // (the dbias reduction uses the first 4 KB)
+    int* s_flag = (int*)(smem + 8192);
     const int4 u = p.units[blockIdx.x];
     if (u.x == UNIT_DINP)
-        run_unit<true>(p, p.g[UNIT_DINP], u, smem, &s_flag);
+        run_unit<true>(p, p.g[UNIT_DINP], u, smem, s_flag);
     else
-        run_unit<false>(p, p.g[UNIT_DWEIGHT], u, smem, &s_flag);
+        run_unit<false>(p, p.g[UNIT_DWEIGHT], u, smem, s_flag);
 }
 
 }  // namespace
+
+int tiles_bf16_bk() { return BK; }
 
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s) {
     if (p.n_units <= 0) return hipSuccess;
