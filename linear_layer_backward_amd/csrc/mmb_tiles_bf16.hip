@@ -8,19 +8,21 @@
 // gfx950 design (one workgroup = 4 wave64s = one 256 x 192 output tile; each
 // wave owns a 128 x 96 quarter = 4 x 3 blocks of v_mfma_f32_32x32x16_bf16):
 //  * Staging: operands go from HBM straight into LDS with buffer loads in LDS
-//    mode (16 bytes per lane, no VGPR staging), through a ring of NS stages
-//    of K depth 32 (32 KB each).  NS-1 stages are in flight while one is
-//    consumed; each wave waits for its own loads with an explicit vmcnt and
-//    one barrier per stage publishes the stage and retires the previous one.
-//    These loads are issued from inline assembly because the compiler would
-//    otherwise wait for every outstanding LDS load before any LDS read.
+//    mode (16 bytes per lane, no VGPR staging), two stages of K depth 64
+//    (64 KB each): the loads of stage k+1 fly while the 48 MFMAs of stage k
+//    run.  K depth 64 makes every K-contiguous row one full 128-byte line
+//    (64-byte segments move at less than half the rate through this path).
+//    Each wave waits for its own loads with an explicit vmcnt; one barrier
+//    per stage publishes it and retires the previous one.  These loads are
+//    issued from inline assembly because the compiler would otherwise wait
+//    for every outstanding LDS load before any LDS read.
 //  * A lane whose 16-byte vector lies outside the operand gets buffer offset
 //    2^31 and writes zeros; rows past the end fall outside the buffer range.
 //  * LDS keeps each operand in its memory orientation:
-//      - dout for dinp (K-contiguous): [256 rows][32 k], 64-byte rows, chunk
-//        c stored at c ^ ((row >> 1) & 3) ^ ((row >> 3) & 1); fragments are
+//      - dout for dinp (K-contiguous): [256 rows][64 k], 128-byte rows, chunk
+//        c stored at c ^ (row & 7) ^ ((row >> 3) & 1); fragments are
 //        ds_read_b128.
-//      - weight, inp and dout-for-dweight (M/N-contiguous): [32 k][256
+//      - weight, inp and dout-for-dweight (M/N-contiguous): [64 k][256
 //        columns], 512-byte rows, chunk c stored at c ^ {0,10,4,14}[row & 3];
 //        fragments are two ds_read_b64_tr_b16 per lane, the gfx950 LDS
 //        transpose read (lane l of each 16-lane group receives element l%4
@@ -41,27 +43,33 @@
 namespace mmb {
 namespace {
 
-constexpr int BM = 256, BN = 192, BK = 32;
+constexpr int BM = 256, BN = 192, BK = 64;
 constexpr int WM = 128, WN = 96, MB = WM / 32, NB = WN / 32;
-constexpr int NS = 4;            // LDS stages in the ring
-constexpr int KC_PITCH = 64;     // K-contiguous LDS row: BK bf16
-constexpr int MN_PITCH = 512;    // M/N-contiguous LDS row: up to 256 bf16
-constexpr int REGION = 16384;    // one operand of one stage
-constexpr int STAGE = 2 * REGION;
-constexpr int LDS_BYTES = NS * STAGE;
-constexpr int LOADS_PER_STAGE = 8;  // 16-byte-per-lane loads per wave per stage
-static_assert(BM * KC_PITCH == REGION && BK * MN_PITCH == REGION, "regions");
-static_assert(REGION / (4 * 1024) * 2 == LOADS_PER_STAGE, "loads per wave");
+constexpr int KC_PITCH = 128;    // K-contiguous LDS row: BK bf16 (one 128-byte line)
+constexpr int MN_PITCH = 512;    // M-contiguous LDS row of A: BM bf16
+constexpr int NB_PITCH = 384;    // N-contiguous LDS row of B: BN bf16
+constexpr int A_REGION = 32768;  // A operand of one stage
+constexpr int B_REGION = BK * NB_PITCH;   // 24 KB
+constexpr int STAGE = A_REGION + B_REGION;
+constexpr int PF_SLOT = 2 * STAGE;        // 1 KB sink for the L2 prefetch loads
+constexpr int LDS_BYTES = PF_SLOT + 1024;
+constexpr int A_LOADS = A_REGION / (4 * 1024);   // 1 KB loads per wave per stage
+constexpr int B_LOADS = B_REGION / (4 * 1024);
+static_assert(BM * KC_PITCH == A_REGION && BK * MN_PITCH == A_REGION, "A region");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// chunk XOR of M/N-contiguous rows, by row & 3: {0, 10, 4, 14}
+// chunk XOR of 512-byte M-contiguous rows, by row & 3: {0, 10, 4, 14}
 __device__ __forceinline__ int sw_mn(int row) { return (0xE4A0 >> ((row & 3) << 2)) & 0xF; }
-// chunk XOR of K-contiguous rows: distinct over any 8 rows of equal parity
-// and any 16 rows of equal row % 4 (both 32- and 64-bank LDS)
-__device__ __forceinline__ int sw_kc(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// chunk XOR of 384-byte N-contiguous rows, by row & 3: {0, 2, 4, 6}; XOR
+// below 8 keeps every chunk inside its row's 24
+__device__ __forceinline__ int sw_nb(int row) { return (row & 3) << 1; }
+// chunk XOR of K-contiguous rows: distinct over any 8 consecutive rows and
+// over the 8 rows of equal parity among any 16 (32- and 64-bank LDS)
+__device__ __forceinline__ int sw_kc(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ bf16x4 tr_read(const char* region, int byte) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_char*)region + byte));
@@ -85,13 +93,16 @@ __device__ __forceinline__ void dma16(i32x4 r, uint32_t voff, uint32_t lds) {
                  :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
 }
 
-// Wait until at most n of this wave's loads are outstanding (n uniform).
-__device__ __forceinline__ void wait_loads(int n) {
-    if (n >= 3 * LOADS_PER_STAGE) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else if (n >= 2 * LOADS_PER_STAGE) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (n >= LOADS_PER_STAGE) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// 4 bytes per lane into LDS at lds + 4 * lane: only used to pull lines into
+// the caches ahead of the real loads.
+__device__ __forceinline__ void touch4(i32x4 r, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
 }
+
+// Wait until this wave has at most n loads outstanding.
+__device__ __forceinline__ void wait_loads_but2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
+__device__ __forceinline__ void wait_loads_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // MFMA fragment (8 consecutive K of one row) of a K-contiguous region:
 // lane l reads row xb + (l & 31), K chunk 2s + (l >> 5).
@@ -104,13 +115,15 @@ __device__ __forceinline__ bf16x8 frag_kc(const char* region, int xb, int s, int
 // The same fragment from an M/N-contiguous region with two transpose reads:
 // lane L of group G = L/16 addresses row 16s + 8(G/2) + 4h + (L/4)%4, columns
 // xb + 16(G%2) + 4(L%4) .. +3 (h = 0, 1).
+template <int PITCH>
 __device__ __forceinline__ bf16x8 frag_mn(const char* region, int xb, int s, int lane) {
     const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
     const int row = 16 * s + 8 * (G >> 1) + e;
     const int col = xb + 16 * (G & 1) + 4 * q;
-    const int byte = row * MN_PITCH + ((((col >> 3) ^ sw_mn(row)) << 4) | (((col >> 2) & 1) << 3));
+    const int sw = PITCH == MN_PITCH ? sw_mn(row) : sw_nb(row);
+    const int byte = row * PITCH + ((((col >> 3) ^ sw) << 4) | (((col >> 2) & 1) << 3));
     const bf16x4 lo = tr_read(region, byte);
-    const bf16x4 hi = tr_read(region, byte + 4 * MN_PITCH);
+    const bf16x4 hi = tr_read(region, byte + 4 * PITCH);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -138,49 +151,82 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const long long b_elems = AK ? (long long)p.OC * p.C : (long long)p.BT * p.C;
     const bool do_bias = !AK && p.dbias != nullptr && tile_n == 0;
 
-    // Load geometry.  Wave w's i-th load of a region fills its 1 KB block
-    // 4w + i; lane p lands at byte 16p of the block, so the lane fetches the
-    // global vector that belongs there under the swizzle.
-    //   K-contiguous A: block rows 16(4w+i) + p/4, physical chunk p%4
-    //   M/N-contiguous: block rows 2(4w+i) + p/32, physical chunk p%32
-    uint32_t a_off[4], b_off[4];
-    int a_kc = 0;   // K-contiguous A: K offset (elements) of this lane's vector
+    // Load geometry.  Wave w's i-th load of a region fills 1 KB block
+    // (loads per wave) * w + i; lane p lands at byte 16p of the block, so the
+    // lane fetches the global vector that belongs there under the swizzle.
+    //   K-contiguous A: block rows 8(8w+i) + p/8, physical chunk p%8
+    //   M-contiguous A: block rows 2(8w+i) + p/32, physical chunk p%32
+    //   B (384-byte rows): byte 1024(6w+i) + 16p of the region
+    uint32_t a_off[A_LOADS], b_off[B_LOADS];
+    int a_kc[A_LOADS];   // K-contiguous A: K offset of the lane's vector in load i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < A_LOADS; ++i) {
         if constexpr (AK) {
-            const int row = 64 * wave + 16 * i + (lane >> 2);
-            const int c = (lane & 3) ^ sw_kc(row);
-            a_kc = 8 * c;
+            const int row = 64 * wave + 8 * i + (lane >> 3);
+            const int c = (lane & 7) ^ sw_kc(row);
+            a_kc[i] = 8 * c;
             a_off[i] = (uint32_t)(row * lda * 2 + c * 16);
         } else {
-            const int row = 2 * (4 * wave + i) + (lane >> 5);
+            const int row = 2 * (8 * wave + i) + (lane >> 5);
             const int c = (lane & 31) ^ sw_mn(row);
             const int col = m0 + 8 * c;
             a_off[i] = col < M ? (uint32_t)((row * lda + col) * 2) : kOOB;
         }
-        {
-            const int row = 2 * (4 * wave + i) + (lane >> 5);
-            const int c = (lane & 31) ^ sw_mn(row);
-            const int col = n0 + 8 * c;
-            b_off[i] = (c < BN / 8 && col < N) ? (uint32_t)((row * ldb + col) * 2) : kOOB;
-        }
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+        const int byte = 1024 * (B_LOADS * wave + i) + 16 * lane;
+        const int row = byte / NB_PITCH;
+        const int c = ((byte % NB_PITCH) >> 4) ^ sw_nb(row);
+        const int col = n0 + 8 * c;
+        b_off[i] = col < N ? (uint32_t)((row * ldb + col) * 2) : kOOB;
+    }
+    // L2 prefetch geometry: one 4-byte touch per 128-byte line of a stage,
+    // one load per wave per operand.
+    //   K-contiguous A: row 64w + p (one line per row)
+    //   M-contiguous A: row 16w + p/4, line p%4 (4 lines per 512-byte row)
+    //   B: row 16w + p/3, line p%3 (3 lines per 384-byte row), lanes < 48
+    uint32_t a_pf, b_pf;
+    if constexpr (AK) {
+        a_pf = (uint32_t)((64 * wave + lane) * lda * 2);
+    } else {
+        const int col = m0 + 64 * (lane & 3);
+        a_pf = col < M ? (uint32_t)(((16 * wave + (lane >> 2)) * lda + col) * 2) : kOOB;
+    }
+    {
+        const int col = n0 + 64 * (lane % 3);
+        b_pf = (lane < 48 && col < N) ? (uint32_t)(((16 * wave + lane / 3) * ldb + col) * 2) : kOOB;
     }
     const uint32_t smem_lds = lds_offset(smem);
 
+    auto a_origin = [&](int kt) { return AK ? (long long)m0 * lda + kt * BK : (long long)kt * BK * lda; };
     auto issue = [&](int kt, int stage) {
         const int k0 = kt * BK;
-        const uint32_t la = smem_lds + stage * STAGE + wave * 4096;
-        const uint32_t lb = la + REGION;
-        const long long oa = AK ? (long long)m0 * lda + k0 : (long long)k0 * lda;
+        const uint32_t la = smem_lds + stage * STAGE + wave * (A_LOADS * 1024);
+        const uint32_t lb = smem_lds + stage * STAGE + A_REGION + wave * (B_LOADS * 1024);
+        const long long oa = a_origin(kt);
         const i32x4 ra = rsrc_words(A + oa, (a_elems - oa) * 2);
         // K tail inside a K-contiguous row: vectors at or past K read zeros
-        const uint32_t kmask = AK ? (~(uint32_t)((k0 + a_kc - Kd) >> 31) & kOOB) : 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(ra, a_off[i] | kmask, la + i * 1024);
+        for (int i = 0; i < A_LOADS; ++i) {
+            const uint32_t kmask = AK ? oob_if_ge(k0 + a_kc[i], Kd) : 0u;
+            dma16(ra, a_off[i] | kmask, la + i * 1024);
+        }
         const long long ob = (long long)k0 * ldb;
         const i32x4 rb = rsrc_words(Bp + ob, (b_elems - ob) * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(rb, b_off[i], lb + i * 1024);
+        for (int i = 0; i < B_LOADS; ++i) dma16(rb, b_off[i], lb + i * 1024);
+    };
+    // Pull stage kt's lines into the caches (two loads per wave, always
+    // issued so that the wait counts stay fixed; past the end they read
+    // nothing).
+    auto prefetch = [&](int kt) {
+        const uint32_t sink = smem_lds + PF_SLOT;
+        const long long oa = a_origin(kt);
+        const long long ob = (long long)kt * BK * ldb;
+        const bool live = kt < kt1;
+        touch4(rsrc_words(A + oa, live ? (a_elems - oa) * 2 : 0), a_pf, sink);
+        touch4(rsrc_words(Bp + ob, live ? (b_elems - ob) * 2 : 0), b_pf, sink);
     };
 
     f32x16 acc[MB][NB];
@@ -207,12 +253,13 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     };
     auto read_sub = [&](int stage, int k, Frag& f) {
         const char* sa = smem + stage * STAGE;
-        const char* sb = sa + REGION;
+        const char* sb = sa + A_REGION;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.a[nb] = frag_mn(sb, wn0 + nb * 32, k, lane);
+        for (int nb = 0; nb < NB; ++nb) f.a[nb] = frag_mn<NB_PITCH>(sb, wn0 + nb * 32, k, lane);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-            f.b[mb] = AK ? frag_kc(sa, wm0 + mb * 32, k, lane) : frag_mn(sa, wm0 + mb * 32, k, lane);
+            f.b[mb] = AK ? frag_kc(sa, wm0 + mb * 32, k, lane)
+                         : frag_mn<MN_PITCH>(sa, wm0 + mb * 32, k, lane);
     };
     auto bias_add = [&](int stage) {
         const char* sa = smem + stage * STAGE;
@@ -235,39 +282,34 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
                                                                       0, 0, 0);
     };
 
-    // Ring of NS stages, NS-1 loaded ahead.  Iteration `it`: read the second
-    // substep of stage it while the MFMAs of its first substep run; then one
-    // barrier publishes stage it+1 (each wave has waited for its own loads
-    // of it) and retires stage it-1 (all its fragments were read before),
-    // whose buffer takes the loads of stage it+NS-1; then the first substep
-    // of stage it+1 is read while the MFMAs of the second substep of it run.
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-        if (i < nk) issue(kt0 + i, i);
-    Frag fa, fb;
+    // Two stages: iteration `it` waits for its own loads of stage it, and one
+    // barrier publishes stage it (all waves' loads) and retires stage it-1,
+    // whose buffer then takes the loads of stage it+1; the lines of stage
+    // it+2 are pulled into the caches at the same time, so those loads find
+    // them one iteration later.  Inside the stage the fragments of substep
+    // k+1 are read while the MFMAs of substep k run.
     if (nk > 0) {
-        const int issued = nk < NS - 1 ? nk : NS - 1;
-        wait_loads((issued - 1) * LOADS_PER_STAGE);
-        __syncthreads();
-        read_sub(0, 0, fa);
-        if (do_bias) bias_add(0);
+        issue(kt0, 0);
+        prefetch(kt0 + 1);
     }
     for (int it = 0; it < nk; ++it) {
-        read_sub(it % NS, 1, fb);
-        mma_sub(fa);
+        const int stage = it & 1;
+        wait_loads_but2();   // all but this wave's two newest (prefetch) loads
+        __syncthreads();
+        if (it + 1 < nk) issue(kt0 + it + 1, stage ^ 1);
+        prefetch(kt0 + it + 2);
         __builtin_amdgcn_sched_barrier(0);
-        if (it + 1 < nk) {
-            const int ahead = nk - it - 2 < NS - 3 ? nk - it - 2 : NS - 3;
-            wait_loads(ahead * LOADS_PER_STAGE);
-            __syncthreads();
-            if (it + NS - 1 < nk) issue(kt0 + it + NS - 1, (it + NS - 1) % NS);
-            __builtin_amdgcn_sched_barrier(0);
-            read_sub((it + 1) % NS, 0, fa);
-            if (do_bias) bias_add((it + 1) % NS);
+        Frag f[2];
+        read_sub(stage, 0, f[0]);
+        if (do_bias) bias_add(stage);
+#pragma unroll
+        for (int k = 0; k < BK / 16; ++k) {
+            if (k + 1 < BK / 16) read_sub(stage, k + 1, f[(k + 1) & 1]);
+            mma_sub(f[k & 1]);
         }
-        mma_sub(fb);
         __builtin_amdgcn_sched_barrier(0);
     }
+    wait_loads_all();   // no load may land in LDS after the workgroup moves on
 
     // dbias of this unit's 256 columns: lanes l, l^32 share a column chunk;
     // the 4 waves meet in LDS once every wave is done with the ring
