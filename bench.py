@@ -31,7 +31,8 @@ METRIC = "matmul-backward TFLOP/s (dinp+dweight+dbias) at GPT-2 fc shape; % MFMA
 # MI355X dense peaks (AMD published): bf16 MFMA 2.5 PFLOP/s (256 CUs x 2.4 GHz
 # x 4096 flop/clk/CU = 2516.6 TFLOP/s), fp32 MFMA 157.3 TFLOP/s
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
-KERNEL_NAME = "mmb_tiles_kernel"
+# the one kernel a step launches, per compute type
+KERNEL_NAME = {"bf16": "mmb_tiles_bf16_kernel", "f32": "mmb_tiles_kernel"}
 
 
 def source_digest() -> str:
@@ -43,10 +44,10 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: int):
+def measured_traffic(kernel: str, cfg: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_cfg{cfg}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_cfg{cfg}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -180,7 +181,8 @@ def main(argv=None):
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    traffic = measured_traffic(args.config)
+    kernel = KERNEL_NAME[dtype]
+    traffic = measured_traffic(kernel, args.config)
 
     out = {
         "metric": METRIC,
@@ -201,7 +203,7 @@ def main(argv=None):
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel": KERNEL_NAME,
+                     "traffic": traffic, "kernel": kernel,
                      "launch_ms": round(launch_ms, 5)},
         "wall_s": round(wall, 3),
     }

@@ -104,6 +104,11 @@ int mmb_path(const void* dinp, const void* dweight, const void* dbias,
 int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
                    int* splits, int* units, int max_units);
 
+/* Output-tile shape of the MFMA path for `dtype`: shape[0] rows (M),
+ * shape[1] columns (N), shape[2] the K depth of one pipeline stage.
+ * Host only.  Returns MMB_OK or MMB_ERR_DTYPE / MMB_ERR_NULL. */
+int mmb_tile_shape(int dtype, int* shape);
+
 /* Synchronise every device the library has used, then free its workspaces.
  * The next call allocates again. */
 int mmb_release(void);

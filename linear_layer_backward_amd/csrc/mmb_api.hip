@@ -472,6 +472,16 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
     return (int)p.units.size();
 }
 
+int mmb_tile_shape(int dtype, int* shape) {
+    if (dtype != MMB_FP32 && dtype != MMB_BF16) return MMB_ERR_DTYPE;
+    if (!shape) return MMB_ERR_NULL;
+    const mmb::TileShape ts = mmb::tile_shape(dtype);
+    shape[0] = ts.BM;
+    shape[1] = ts.BN;
+    shape[2] = ts.BK;
+    return MMB_OK;
+}
+
 int mmb_release(void) {
     std::lock_guard<std::mutex> lock(mmb::g_mu);
     int prev = 0;

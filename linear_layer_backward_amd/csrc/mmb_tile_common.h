@@ -88,29 +88,34 @@ __device__ __forceinline__ void write_tile(T* D, long long ldd, int M, int N, in
     const int lr = lane & 31, half = lane >> 5;
     const long long base = (long long)m0 * ldd + n0;
     const auto r = make_rsrc(D + base, ((long long)M * ldd - base) * (long long)sizeof(T));
-    typename OutVec<T>::type old[MB][NB][4];
-    uint32_t off[MB][NB][4];
+    auto offset = [&](int mb, int nb, int q) {
+        const int m = mb * 32 + lr, n = nb * 32 + 8 * q + 4 * half;
+        return (uint32_t)((m * ldd + n) * (long long)sizeof(T)) | oob_if_ge(m0 + m, M) |
+               oob_if_ge(n0 + n, N);
+    };
+    // one row of blocks per batch of loads bounds the registers in flight
+    constexpr int CH = 1;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb0 = 0; mb0 < MB; mb0 += CH) {
+        typename OutVec<T>::type old[CH][NB][4];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int i = 0; i < CH; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = mb * 32 + lr, n = nb * 32 + 8 * q + 4 * half;
-                off[mb][nb][q] = (uint32_t)((m * ldd + n) * (long long)sizeof(T)) |
-                                 oob_if_ge(m0 + m, M) | oob_if_ge(n0 + n, N);
-                old[mb][nb][q] = out_load(r, off[mb][nb][q], T{});
-            }
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+                for (int q = 0; q < 4; ++q) old[i][nb][q] = out_load(r, offset(mb0 + i, nb, q), T{});
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int i = 0; i < CH; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
-                                 acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
-                out_store(r, off[mb][nb][q], old[mb][nb][q], v);
-            }
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int mb = mb0 + i;
+                    const f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
+                                     acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
+                    out_store(r, offset(mb, nb, q), old[i][nb][q], v);
+                }
+    }
 }
 
 // ---- split-K ---------------------------------------------------------------
@@ -144,14 +149,14 @@ __device__ __forceinline__ bool arrive_last(int* counter, int splits, int* s_fla
 
 // acc <- p_0 + p_1 + ... + p_{S-1}, every partial (this workgroup's own
 // included) read back with agent-coherent loads and added in split order, so
-// the bits do not depend on which split arrives last.  Half of the tile is
-// fetched per batch of loads.
+// the bits do not depend on which split arrives last.  Up to 8 groups of 4
+// floats are fetched per batch of loads.
 template <int MB, int NB>
 __device__ __forceinline__ void sum_partials(const float* w0, int splits, int tile_floats,
                                              f32x16 (&acc)[MB][NB], int tid) {
     constexpr int NG = MB * NB * 4;          // 4-float groups per thread
-    constexpr int BATCH = NG / 2;
-    static_assert(NG % 2 == 0, "two batches");
+    constexpr int BATCH = NG >= 32 ? 8 : NG / 2;
+    static_assert(NG % BATCH == 0, "whole batches");
 #pragma unroll
     for (int b0 = 0; b0 < NG; b0 += BATCH) {
         f32x4 sum[BATCH];

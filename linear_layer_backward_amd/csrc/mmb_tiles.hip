@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void mmb_tiles_kernel(TilesParams p) {
 }  // namespace
 
 TileShape tile_shape(int dtype) {
-    if (dtype == 1) return TileShape{256, 192, tiles_bf16_bk()};
+    if (dtype == 1) return TileShape{256, tiles_bf16_bn(), tiles_bf16_bk()};
     return TileShape{K<float>::BM, K<float>::BN, K<float>::BK};
 }
 

@@ -358,6 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void mmb_tiles_bf16_kernel(TilesParams
 }  // namespace
 
 int tiles_bf16_bk() { return BK; }
+int tiles_bf16_bn() { return BN; }
 
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s) {
     if (p.n_units <= 0) return hipSuccess;

@@ -47,6 +47,8 @@ _lib.mmb_strerror.argtypes = [_i]
 _lib.mmb_strerror.restype = ctypes.c_char_p
 _lib.mmb_plan_units.argtypes = [_i] * 7 + [ctypes.POINTER(_i), ctypes.POINTER(_i), _i]
 _lib.mmb_plan_units.restype = _i
+_lib.mmb_tile_shape.argtypes = [_i, ctypes.POINTER(_i)]
+_lib.mmb_tile_shape.restype = _i
 _lib.mmb_release.argtypes = []
 _lib.mmb_release.restype = _i
 
@@ -113,6 +115,15 @@ def mmb_plan_units(B, T, C, OC, dtype, has_bias, num_cus):
     buf = (_i * (4 * n))()
     _lib.mmb_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, buf, n)
     return (sp[0], sp[1]), [tuple(buf[4 * k:4 * k + 4]) for k in range(n)]
+
+
+def mmb_tile_shape(dtype):
+    """(BM, BN, BK) of the MFMA tiles for dtype.  Host only."""
+    sh = (_i * 3)()
+    st = _lib.mmb_tile_shape(int(dtype), sh)
+    if st != 0:
+        raise MmbError(st)
+    return sh[0], sh[1], sh[2]
 
 
 def torch_dtype_code(dt) -> int:

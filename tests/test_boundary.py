@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("mmb_backward", "mmb_backward_stream", "mmb_check_args", "mmb_strerror",
-              "mmb_release", "mmb_path", "mmb_plan_units"):
+              "mmb_release", "mmb_path", "mmb_plan_units", "mmb_tile_shape"):
         assert f in names
 
 
@@ -135,7 +135,7 @@ def test_path_choice(mmb):
 def test_plan_covers_every_tile_and_split_once(mmb, shape, cus):
     B, T, C, OC, dt, bias = shape
     (sw, si), units = mmb.mmb_plan_units(B, T, C, OC, dt, bias, cus)
-    BM, BN, BK = (256, 192, 64) if dt == 1 else (128, 128, 32)
+    BM, BN, BK = mmb.mmb_tile_shape(dt)
     cd = lambda a, b: -(-a // b)
     expect = set()
     for s in range(sw):
@@ -149,6 +149,14 @@ def test_plan_covers_every_tile_and_split_once(mmb, shape, cus):
     assert len(units) == len(expect)
     assert set(units) == expect
     assert 1 <= sw <= cd(B * T, BK) and 1 <= si <= cd(OC, BK)
+
+
+def test_tile_shape(mmb):
+    assert mmb.mmb_tile_shape(0) == (128, 128, 32)
+    bm, bn, bk = mmb.mmb_tile_shape(1)
+    assert bm % 32 == 0 and bn % 32 == 0 and bk % 16 == 0
+    with pytest.raises(mmb.MmbError):
+        mmb.mmb_tile_shape(7)
 
 
 def test_plan_split_override(mmb, monkeypatch):
