@@ -58,6 +58,48 @@ def measured_traffic(kernel: str, cfg: int):
     return float(b.group(1))
 
 
+def _counter_mean(run_dir: str, counter: str, kernel: str):
+    """Mean per-dispatch value of one rocprofv3 counter for kernels whose
+    name contains `kernel`, from the counter_collection CSVs under run_dir."""
+    import csv
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] == counter and kernel in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel} under {run_dir}")
+    return float(np.mean(vals)), len(vals)
+
+
+def summarize_counters(cfg: int, dirs, copy_mib: int) -> str:
+    """Text summary of two FETCH_SIZE / WRITE_SIZE passes over the workload and
+    the same two passes over a plain copy of copy_mib MiB: the copy kernel's
+    readings fix the KiB-per-counter-unit scale of each counter."""
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
+    dtype = "bf16" if cfg >= 4 else "f32"
+    kernel = KERNEL_NAME[dtype]
+    copy_kib = copy_mib * 1024.0
+    cf, ncf = _counter_mean(cal_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
+    cw, ncw = _counter_mean(cal_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
+    kf, nkf = _counter_mean(fetch_dir, "FETCH_SIZE", kernel)
+    kw, nkw = _counter_mean(write_dir, "WRITE_SIZE", kernel)
+    sf, sw = copy_kib / cf, copy_kib / cw
+    fetch_b, write_b = kf * sf * 1024, kw * sw * 1024
+    lines = [
+        f"kernel: {kernel}",
+        f"workload: config {cfg}",
+        f"source_digest: {source_digest()}",
+        f"copy calibration: {copy_mib} MiB each way; FETCH_SIZE {cf:.1f} ({ncf} dispatches), "
+        f"WRITE_SIZE {cw:.1f} ({ncw}); scale fetch {sf:.4f}, write {sw:.4f}",
+        f"kernel FETCH_SIZE mean {kf:.1f} over {nkf} dispatches -> {fetch_b:.4e} bytes",
+        f"kernel WRITE_SIZE mean {kw:.1f} over {nkw} dispatches -> {write_b:.4e} bytes",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.6e}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def upload(case, dev):
     import torch
     from linear_layer_backward_amd import workloads as wl
@@ -118,7 +160,16 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
+                    help="print the HBM-traffic summary from rocprofv3 --pmc output dirs: "
+                         "workload FETCH_SIZE, workload WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
+                         "(the copy run made with --copy-calibration MIB)")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        print(summarize_counters(args.config, args.summarize_counters,
+                                 args.copy_calibration or 256), end="")
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the "

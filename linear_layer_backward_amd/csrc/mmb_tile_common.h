@@ -120,11 +120,11 @@ __device__ __forceinline__ void write_tile(T* D, long long ldd, int M, int N, in
 
 // ---- split-K ---------------------------------------------------------------
 // A workgroup's partial tile (fp32), in fragment order: thread tid's group q
-// of block (mb, nb) lives at float ((mb * NB + nb) * 4 + q) * 1024 + tid * 4,
-// so each wave store writes 1 KB contiguously.
-template <int MB, int NB>
+// of block (mb, nb) lives at float ((mb * NB + nb) * 4 + q) * 4 * NT + tid * 4
+// (NT threads per workgroup), so each wave store writes 1 KB contiguously.
+template <int MB, int NB, int NT>
 __device__ __forceinline__ void publish_partial(float* wt, const f32x16 (&acc)[MB][NB], int tid) {
-    const auto r = make_rsrc(wt, (long long)MB * NB * 4 * kThreads * 16);
+    const auto r = make_rsrc(wt, (long long)MB * NB * 4 * NT * 16);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -133,7 +133,7 @@ __device__ __forceinline__ void publish_partial(float* wt, const f32x16 (&acc)[M
             for (int q = 0; q < 4; ++q) {
                 const f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
                                  acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
-                store16_agent(r, (uint32_t)((((mb * NB + nb) * 4 + q) * kThreads + tid) * 16), v);
+                store16_agent(r, (uint32_t)((((mb * NB + nb) * 4 + q) * NT + tid) * 16), v);
             }
 }
 
@@ -151,7 +151,7 @@ __device__ __forceinline__ bool arrive_last(int* counter, int splits, int* s_fla
 // included) read back with agent-coherent loads and added in split order, so
 // the bits do not depend on which split arrives last.  Up to 8 groups of 4
 // floats are fetched per batch of loads.
-template <int MB, int NB>
+template <int MB, int NB, int NT>
 __device__ __forceinline__ void sum_partials(const float* w0, int splits, int tile_floats,
                                              f32x16 (&acc)[MB][NB], int tid) {
     constexpr int NG = MB * NB * 4;          // 4-float groups per thread
@@ -165,7 +165,7 @@ __device__ __forceinline__ void sum_partials(const float* w0, int splits, int ti
             f32x4 v[BATCH];
 #pragma unroll
             for (int g = 0; g < BATCH; ++g)
-                v[g] = load16_agent(r, (uint32_t)(((b0 + g) * kThreads + tid) * 16));
+                v[g] = load16_agent(r, (uint32_t)(((b0 + g) * NT + tid) * 16));
 #pragma unroll
             for (int g = 0; g < BATCH; ++g) sum[g] = sp == 0 ? v[g] : sum[g] + v[g];
         }

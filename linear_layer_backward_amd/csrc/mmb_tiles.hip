@@ -250,14 +250,14 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     if (g.splits > 1) {
         const int tile = tile_m * g.tiles_n + tile_n;
         float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
-        publish_partial<Kt::MB, Kt::NB>(w0 + (long long)split * (BM * BN), acc, tid);
+        publish_partial<Kt::MB, Kt::NB, kThreads>(w0 + (long long)split * (BM * BN), acc, tid);
         float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + xg * E;
         if (bias_owner) {
 #pragma unroll
             for (int x = 0; x < E; ++x) publish_bias(wb + split * BM + x, bsum[x]);
         }
         if (!arrive_last(p.counters + g.tile_base + tile, g.splits, s_flag)) return;
-        sum_partials<Kt::MB, Kt::NB>(w0, g.splits, BM * BN, acc, tid);
+        sum_partials<Kt::MB, Kt::NB, kThreads>(w0, g.splits, BM * BN, acc, tid);
         if (bias_owner) {
 #pragma unroll
             for (int x = 0; x < E; ++x) bsum[x] = sum_bias(wb + x, g.splits, BM);

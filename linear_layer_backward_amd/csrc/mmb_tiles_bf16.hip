@@ -5,17 +5,23 @@
 // Operation: llm.c page "dev/cuda/matmul_backward.cu", launcher
 // matmul_backward1 (the two GEMMs) and the bias kernels (column sums of dout).
 //
-// gfx950 design (one workgroup = 4 wave64s = one 256 x 192 output tile; each
-// wave owns a 128 x 96 quarter = 4 x 3 blocks of v_mfma_f32_32x32x16_bf16):
+// gfx950 design (one workgroup = 8 wave64s = one 256 x 256 output tile; wave
+// w owns the 128 x 64 block at rows 128 (w & 1), columns 64 (w >> 1), i.e.
+// 4 x 2 blocks of v_mfma_f32_32x32x16_bf16):
+//  * Two waves per SIMD.  A single wave cannot keep the matrix unit busy:
+//    between its own MFMAs it also has to issue the LDS reads, the loads and
+//    their waits; a second wave on the same SIMD issues MFMAs while the
+//    first one waits.
 //  * Staging: operands go from HBM straight into LDS with buffer loads in LDS
 //    mode (16 bytes per lane, no VGPR staging), two stages of K depth 64
-//    (64 KB each): the loads of stage k+1 fly while the 48 MFMAs of stage k
-//    run.  K depth 64 makes every K-contiguous row one full 128-byte line
-//    (64-byte segments move at less than half the rate through this path).
-//    Each wave waits for its own loads with an explicit vmcnt; one barrier
-//    per stage publishes it and retires the previous one.  These loads are
-//    issued from inline assembly because the compiler would otherwise wait
-//    for every outstanding LDS load before any LDS read.
+//    (64 KB each).  K depth 64 makes every K-contiguous row one full 128-byte
+//    line.  The loads of a stage are issued two stages ahead; each wave waits
+//    for its own loads with an explicit vmcnt and one barrier per stage
+//    publishes them.  The barrier sits before the last 16-deep substep of a
+//    stage, so the next stage's first fragments are read while that
+//    substep's MFMAs run.  The loads are issued from inline assembly because
+//    the compiler would otherwise wait for every outstanding LDS load before
+//    any LDS read.
 //  * A lane whose 16-byte vector lies outside the operand gets buffer offset
 //    2^31 and writes zeros; rows past the end fall outside the buffer range.
 //  * LDS keeps each operand in its memory orientation:
@@ -34,7 +40,7 @@
 //    registers hold 4 consecutive output columns (8-byte bf16 epilogue).
 //  * dbias: dweight units of column tile 0 also read their dout stage from
 //    LDS and sum it in fp32; lanes l and l+32 combine by a shuffle and the
-//    4 waves through LDS in a fixed order.
+//    8 waves through LDS in a fixed order.
 //  * Split K (dweight's K = B*T): fp32 partial tiles in the workspace, the
 //    last arriver adds them in split order, adds the old output and rounds
 //    once to bf16.
@@ -43,30 +49,26 @@
 namespace mmb {
 namespace {
 
-constexpr int BM = 256, BN = 192, BK = 64;
-constexpr int WM = 128, WN = 96, MB = WM / 32, NB = WN / 32;
+constexpr int NT = 512, NW = NT / 64;          // 8 waves, two per SIMD
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int WM = 128, WN = 64, MB = WM / 32, NB = WN / 32;
 constexpr int KC_PITCH = 128;    // K-contiguous LDS row: BK bf16 (one 128-byte line)
-constexpr int MN_PITCH = 512;    // M-contiguous LDS row of A: BM bf16
-constexpr int NB_PITCH = 384;    // N-contiguous LDS row of B: BN bf16
-constexpr int A_REGION = 32768;  // A operand of one stage
-constexpr int B_REGION = BK * NB_PITCH;   // 24 KB
-constexpr int STAGE = A_REGION + B_REGION;
-constexpr int PF_SLOT = 2 * STAGE;        // 1 KB sink for the L2 prefetch loads
+constexpr int MN_PITCH = 512;    // M/N-contiguous LDS row: 256 bf16
+constexpr int REGION = 32768;    // one operand of one stage
+constexpr int STAGE = 2 * REGION;
+constexpr int PF_SLOT = 2 * STAGE;          // 1 KB sink for the L2 prefetch loads
 constexpr int LDS_BYTES = PF_SLOT + 1024;
-constexpr int A_LOADS = A_REGION / (4 * 1024);   // 1 KB loads per wave per stage
-constexpr int B_LOADS = B_REGION / (4 * 1024);
-static_assert(BM * KC_PITCH == A_REGION && BK * MN_PITCH == A_REGION, "A region");
+constexpr int LOADS = REGION / (NW * 1024); // 1 KB loads per wave per operand per stage
+static_assert(BM * KC_PITCH == REGION && BK * MN_PITCH == REGION, "regions");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+static_assert(MB * NB * 16 * NT == BM * BN, "accumulators cover the tile");
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// chunk XOR of 512-byte M-contiguous rows, by row & 3: {0, 10, 4, 14}
+// chunk XOR of 512-byte M/N-contiguous rows, by row & 3: {0, 10, 4, 14}
 __device__ __forceinline__ int sw_mn(int row) { return (0xE4A0 >> ((row & 3) << 2)) & 0xF; }
-// chunk XOR of 384-byte N-contiguous rows, by row & 3: {0, 2, 4, 6}; XOR
-// below 8 keeps every chunk inside its row's 24
-__device__ __forceinline__ int sw_nb(int row) { return (row & 3) << 1; }
 // chunk XOR of K-contiguous rows: distinct over any 8 consecutive rows and
 // over the 8 rows of equal parity among any 16 (32- and 64-bank LDS)
 __device__ __forceinline__ int sw_kc(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -87,6 +89,11 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, long long bytes) {
     return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), n, 0x00020000};
 }
 
+// The compiler reserves m0 and warns when an asm statement clobbers it;
+// these statements set it themselves right before the one instruction that
+// reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 // 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
 __device__ __forceinline__ void dma16(i32x4 r, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
@@ -99,10 +106,14 @@ __device__ __forceinline__ void touch4(i32x4 r, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
-// Wait until this wave has at most n loads outstanding.
-__device__ __forceinline__ void wait_loads_but2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
-__device__ __forceinline__ void wait_loads_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until this wave has at most N loads outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 // MFMA fragment (8 consecutive K of one row) of a K-contiguous region:
 // lane l reads row xb + (l & 31), K chunk 2s + (l >> 5).
@@ -115,15 +126,13 @@ __device__ __forceinline__ bf16x8 frag_kc(const char* region, int xb, int s, int
 // The same fragment from an M/N-contiguous region with two transpose reads:
 // lane L of group G = L/16 addresses row 16s + 8(G/2) + 4h + (L/4)%4, columns
 // xb + 16(G%2) + 4(L%4) .. +3 (h = 0, 1).
-template <int PITCH>
 __device__ __forceinline__ bf16x8 frag_mn(const char* region, int xb, int s, int lane) {
     const int G = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
     const int row = 16 * s + 8 * (G >> 1) + e;
     const int col = xb + 16 * (G & 1) + 4 * q;
-    const int sw = PITCH == MN_PITCH ? sw_mn(row) : sw_nb(row);
-    const int byte = row * PITCH + ((((col >> 3) ^ sw) << 4) | (((col >> 2) & 1) << 3));
+    const int byte = row * MN_PITCH + ((((col >> 3) ^ sw_mn(row)) << 4) | (((col >> 2) & 1) << 3));
     const bf16x4 lo = tr_read(region, byte);
-    const bf16x4 hi = tr_read(region, byte + 4 * PITCH);
+    const bf16x4 hi = tr_read(region, byte + 4 * MN_PITCH);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -152,81 +161,78 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const bool do_bias = !AK && p.dbias != nullptr && tile_n == 0;
 
     // Load geometry.  Wave w's i-th load of a region fills 1 KB block
-    // (loads per wave) * w + i; lane p lands at byte 16p of the block, so the
-    // lane fetches the global vector that belongs there under the swizzle.
-    //   K-contiguous A: block rows 8(8w+i) + p/8, physical chunk p%8
-    //   M-contiguous A: block rows 2(8w+i) + p/32, physical chunk p%32
-    //   B (384-byte rows): byte 1024(6w+i) + 16p of the region
-    uint32_t a_off[A_LOADS], b_off[B_LOADS];
-    int a_kc[A_LOADS];   // K-contiguous A: K offset of the lane's vector in load i
+    // LOADS * w + i; lane p lands at byte 16p of the block, so the lane
+    // fetches the global vector that belongs there under the swizzle.
+    //   K-contiguous A: block rows 8 * block + p/8, physical chunk p%8
+    //   M/N-contiguous: block rows 2 * block + p/32, physical chunk p%32
+    uint32_t a_off[LOADS], b_off[LOADS];
+    int a_kc[LOADS];   // K-contiguous A: K offset of the lane's vector in load i
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
+    for (int i = 0; i < LOADS; ++i) {
+        const int blk = LOADS * wave + i;
+        const int row = 2 * blk + (lane >> 5);
         if constexpr (AK) {
-            const int row = 64 * wave + 8 * i + (lane >> 3);
-            const int c = (lane & 7) ^ sw_kc(row);
+            const int krow = 8 * blk + (lane >> 3);
+            const int c = (lane & 7) ^ sw_kc(krow);
             a_kc[i] = 8 * c;
-            a_off[i] = (uint32_t)(row * lda * 2 + c * 16);
+            a_off[i] = (uint32_t)(krow * lda * 2 + c * 16);
         } else {
-            const int row = 2 * (8 * wave + i) + (lane >> 5);
-            const int c = (lane & 31) ^ sw_mn(row);
-            const int col = m0 + 8 * c;
+            const int col = m0 + 8 * ((lane & 31) ^ sw_mn(row));
             a_off[i] = col < M ? (uint32_t)((row * lda + col) * 2) : kOOB;
         }
-    }
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-        const int byte = 1024 * (B_LOADS * wave + i) + 16 * lane;
-        const int row = byte / NB_PITCH;
-        const int c = ((byte % NB_PITCH) >> 4) ^ sw_nb(row);
-        const int col = n0 + 8 * c;
+        const int col = n0 + 8 * ((lane & 31) ^ sw_mn(row));
         b_off[i] = col < N ? (uint32_t)((row * ldb + col) * 2) : kOOB;
     }
-    // L2 prefetch geometry: one 4-byte touch per 128-byte line of a stage,
-    // one load per wave per operand.
-    //   K-contiguous A: row 64w + p (one line per row)
-    //   M-contiguous A: row 16w + p/4, line p%4 (4 lines per 512-byte row)
-    //   B: row 16w + p/3, line p%3 (3 lines per 384-byte row), lanes < 48
-    uint32_t a_pf, b_pf;
-    if constexpr (AK) {
-        a_pf = (uint32_t)((64 * wave + lane) * lda * 2);
-    } else {
-        const int col = m0 + 64 * (lane & 3);
-        a_pf = col < M ? (uint32_t)(((16 * wave + (lane >> 2)) * lda + col) * 2) : kOOB;
-    }
+    // L2 prefetch geometry: one 4-byte touch per 128-byte line of a stage;
+    // waves 0-3 cover A, waves 4-7 cover B, one load per wave per stage.
+    //   K-contiguous A: row 64(w % 4) + p (one line per row)
+    //   M/N-contiguous: row 16(w % 4) + p/4, line p%4 (4 lines per 512-byte row)
+    const bool pf_a = wave < 4;
+    uint32_t pf_off;
     {
-        const int col = n0 + 64 * (lane % 3);
-        b_pf = (lane < 48 && col < N) ? (uint32_t)(((16 * wave + lane / 3) * ldb + col) * 2) : kOOB;
+        const int w4 = wave & 3;
+        const int row = 16 * w4 + (lane >> 2);
+        const int col = 64 * (lane & 3);
+        if (pf_a) {
+            if constexpr (AK) pf_off = (uint32_t)((64 * w4 + lane) * lda * 2);
+            else pf_off = m0 + col < M ? (uint32_t)((row * lda + m0 + col) * 2) : kOOB;
+        } else {
+            pf_off = n0 + col < N ? (uint32_t)((row * ldb + n0 + col) * 2) : kOOB;
+        }
     }
     const uint32_t smem_lds = lds_offset(smem);
 
     auto a_origin = [&](int kt) { return AK ? (long long)m0 * lda + kt * BK : (long long)kt * BK * lda; };
+    // Stage kt into LDS buffer `stage`; a stage past the end (kt >= kt1)
+    // still issues its loads, over an empty range, so that every wave's
+    // count of outstanding loads follows one fixed pattern.
     auto issue = [&](int kt, int stage) {
+        const bool live = kt < kt1;
         const int k0 = kt * BK;
-        const uint32_t la = smem_lds + stage * STAGE + wave * (A_LOADS * 1024);
-        const uint32_t lb = smem_lds + stage * STAGE + A_REGION + wave * (B_LOADS * 1024);
+        const uint32_t la = smem_lds + stage * STAGE + wave * (LOADS * 1024);
+        const uint32_t lb = la + REGION;
         const long long oa = a_origin(kt);
-        const i32x4 ra = rsrc_words(A + oa, (a_elems - oa) * 2);
+        const i32x4 ra = rsrc_words(A + oa, live ? (a_elems - oa) * 2 : 0);
         // K tail inside a K-contiguous row: vectors at or past K read zeros
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
+        for (int i = 0; i < LOADS; ++i) {
             const uint32_t kmask = AK ? oob_if_ge(k0 + a_kc[i], Kd) : 0u;
             dma16(ra, a_off[i] | kmask, la + i * 1024);
         }
         const long long ob = (long long)k0 * ldb;
-        const i32x4 rb = rsrc_words(Bp + ob, (b_elems - ob) * 2);
+        const i32x4 rb = rsrc_words(Bp + ob, live ? (b_elems - ob) * 2 : 0);
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) dma16(rb, b_off[i], lb + i * 1024);
+        for (int i = 0; i < LOADS; ++i) dma16(rb, b_off[i], lb + i * 1024);
     };
-    // Pull stage kt's lines into the caches (two loads per wave, always
-    // issued so that the wait counts stay fixed; past the end they read
-    // nothing).
+    // Pull stage kt's lines into the caches (one load per wave; past the end
+    // it reads nothing).
     auto prefetch = [&](int kt) {
-        const uint32_t sink = smem_lds + PF_SLOT;
+        const bool live = kt < kt1;
         const long long oa = a_origin(kt);
         const long long ob = (long long)kt * BK * ldb;
-        const bool live = kt < kt1;
-        touch4(rsrc_words(A + oa, live ? (a_elems - oa) * 2 : 0), a_pf, sink);
-        touch4(rsrc_words(Bp + ob, live ? (b_elems - ob) * 2 : 0), b_pf, sink);
+        const i32x4 r = pf_a ? rsrc_words(A + oa, live ? (a_elems - oa) * 2 : 0)
+                             : rsrc_words(Bp + ob, live ? (b_elems - ob) * 2 : 0);
+        touch4(r, pf_off, smem_lds + PF_SLOT);
     };
 
     f32x16 acc[MB][NB];
@@ -240,7 +246,7 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     float bsum[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) bsum[x] = 0.f;
-    // dbias: thread t sums column chunk t & 31 over K-rows (t >> 5) + 8j
+    // dbias: thread t sums column chunk t & 31 over K-rows (t >> 5) + 16j
     const int bias_c = tid & 31, bias_r = tid >> 5;
     const int bias_byte = bias_r * MN_PITCH + ((bias_c ^ sw_mn(bias_r)) << 4);
 
@@ -253,19 +259,18 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     };
     auto read_sub = [&](int stage, int k, Frag& f) {
         const char* sa = smem + stage * STAGE;
-        const char* sb = sa + A_REGION;
+        const char* sb = sa + REGION;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.a[nb] = frag_mn<NB_PITCH>(sb, wn0 + nb * 32, k, lane);
+        for (int nb = 0; nb < NB; ++nb) f.a[nb] = frag_mn(sb, wn0 + nb * 32, k, lane);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-            f.b[mb] = AK ? frag_kc(sa, wm0 + mb * 32, k, lane)
-                         : frag_mn<MN_PITCH>(sa, wm0 + mb * 32, k, lane);
+            f.b[mb] = AK ? frag_kc(sa, wm0 + mb * 32, k, lane) : frag_mn(sa, wm0 + mb * 32, k, lane);
     };
     auto bias_add = [&](int stage) {
         const char* sa = smem + stage * STAGE;
 #pragma unroll
-        for (int j = 0; j < BK / 8; ++j) {
-            const u32x4 v = *(const u32x4*)(sa + bias_byte + j * 8 * MN_PITCH);
+        for (int j = 0; j < BK / 16; ++j) {
+            const u32x4 v = *(const u32x4*)(sa + bias_byte + j * 16 * MN_PITCH);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 bsum[2 * d] += __uint_as_float(v[d] << 16);
@@ -282,37 +287,45 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
                                                                       0, 0, 0);
     };
 
-    // Two stages: iteration `it` waits for its own loads of stage it, and one
-    // barrier publishes stage it (all waves' loads) and retires stage it-1,
-    // whose buffer then takes the loads of stage it+1; the lines of stage
-    // it+2 are pulled into the caches at the same time, so those loads find
-    // them one iteration later.  Inside the stage the fragments of substep
-    // k+1 are read while the MFMAs of substep k run.
+    // Ring of two stages.  Loads per wave, in issue order: stage 0, stage 1,
+    // touch of stage 2, then per iteration `it` the loads of stage it+2 and
+    // the touch of stage it+3.  Iteration it runs the substeps of stage it
+    // (buffer it & 1); before its last substep every wave waits for its own
+    // loads of stage it+1 (only the newest touch may still fly), and one
+    // barrier makes stage it+1 visible and retires buffer it & 1, which then
+    // takes the loads of stage it+2 while the last substep runs.
     if (nk > 0) {
         issue(kt0, 0);
-        prefetch(kt0 + 1);
-    }
-    for (int it = 0; it < nk; ++it) {
-        const int stage = it & 1;
-        wait_loads_but2();   // all but this wave's two newest (prefetch) loads
+        issue(kt0 + 1, 1);
+        prefetch(kt0 + 2);
+        wait_loads<2 * LOADS + 1>();   // stage 0 landed (this wave's part)
         __syncthreads();
-        if (it + 1 < nk) issue(kt0 + it + 1, stage ^ 1);
-        prefetch(kt0 + it + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        Frag f[2];
-        read_sub(stage, 0, f[0]);
-        if (do_bias) bias_add(stage);
-#pragma unroll
-        for (int k = 0; k < BK / 16; ++k) {
-            if (k + 1 < BK / 16) read_sub(stage, k + 1, f[(k + 1) & 1]);
-            mma_sub(f[k & 1]);
+        Frag f0, f1;
+        read_sub(0, 0, f0);
+        for (int it = 0; it < nk; ++it) {
+            const int cur = it & 1;
+            if (do_bias) bias_add(cur);
+            read_sub(cur, 1, f1);
+            mma_sub(f0);
+            read_sub(cur, 2, f0);
+            mma_sub(f1);
+            read_sub(cur, 3, f1);
+            mma_sub(f0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_loads<1>();           // stage it+1 landed (this wave's part)
+            __syncthreads();
+            issue(kt0 + it + 2, cur);
+            prefetch(kt0 + it + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 1 < nk) read_sub(cur ^ 1, 0, f0);
+            mma_sub(f1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
-    wait_loads_all();   // no load may land in LDS after the workgroup moves on
+    wait_loads<0>();   // no load may land in LDS after the workgroup moves on
 
     // dbias of this unit's 256 columns: lanes l, l^32 share a column chunk;
-    // the 4 waves meet in LDS once every wave is done with the ring
+    // the 8 waves meet in LDS once every wave is done with the ring
     float bias = 0.f;
     if (do_bias) {
         float* red = (float*)smem;
@@ -324,29 +337,33 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             for (int x = 0; x < 8; ++x) red[wave * BM + lane * 8 + x] = bsum[x];
         }
         __syncthreads();
-        bias = ((red[tid] + red[BM + tid]) + red[2 * BM + tid]) + red[3 * BM + tid];
+        if (tid < BM) {
+            bias = red[tid];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) bias += red[w * BM + tid];
+        }
     }
 
     if (g.splits > 1) {
         const int tile = tile_m * g.tiles_n + tile_n;
         float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
-        publish_partial<MB, NB>(w0 + (long long)split * (BM * BN), acc, tid);
+        publish_partial<MB, NB, NT>(w0 + (long long)split * (BM * BN), acc, tid);
         float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + tid;
-        if (do_bias) publish_bias(wb + split * BM, bias);
+        if (do_bias && tid < BM) publish_bias(wb + split * BM, bias);
         if (!arrive_last(p.counters + g.tile_base + tile, g.splits, s_flag)) return;
-        sum_partials<MB, NB>(w0, g.splits, BM * BN, acc, tid);
-        if (do_bias) bias = sum_bias(wb, g.splits, BM);
+        sum_partials<MB, NB, NT>(w0, g.splits, BM * BN, acc, tid);
+        if (do_bias && tid < BM) bias = sum_bias(wb, g.splits, BM);
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
     write_tile<bf16_t, MB, NB>(D, ldd, M, N, m0 + wm0, n0 + wn0, acc, lane);
-    if (do_bias && m0 + tid < M) ((bf16_t*)p.dbias)[m0 + tid] = from_f32<bf16_t>(bias);
+    if (do_bias && tid < BM && m0 + tid < M) ((bf16_t*)p.dbias)[m0 + tid] = from_f32<bf16_t>(bias);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
+__global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
     // the split-K ticket flag lives in the ring, used only after the K loop
-    // (the dbias reduction uses the first 4 KB)
+    // (the dbias reduction uses the first 8 KB)
     int* s_flag = (int*)(smem + 8192);
     const int4 u = p.units[blockIdx.x];
     if (u.x == UNIT_DINP)
@@ -362,7 +379,7 @@ int tiles_bf16_bn() { return BN; }
 
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s) {
     if (p.n_units <= 0) return hipSuccess;
-    hipLaunchKernelGGL(mmb_tiles_bf16_kernel, dim3(p.n_units), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(mmb_tiles_bf16_kernel, dim3(p.n_units), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
