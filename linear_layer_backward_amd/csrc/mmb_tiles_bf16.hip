@@ -12,18 +12,18 @@
 //    between its own MFMAs it also has to issue the LDS reads, the loads and
 //    their waits; a second wave on the same SIMD issues MFMAs while the
 //    first one waits.
-//  * Staging: operands go from HBM straight into LDS with buffer loads in LDS
-//    mode (16 bytes per lane, no VGPR staging), two stages of K depth 64
-//    (64 KB each).  K depth 64 makes every K-contiguous row one full 128-byte
-//    line.  The loads of a stage are issued two stages ahead; each wave waits
-//    for its own loads with an explicit vmcnt and one barrier per stage
-//    publishes them.  The barrier sits before the last 16-deep substep of a
-//    stage, so the next stage's first fragments are read while that
-//    substep's MFMAs run.  The loads are issued from inline assembly because
-//    the compiler would otherwise wait for every outstanding LDS load before
-//    any LDS read.
+//  * Staging: each wave moves 8 KB of every 64 KB stage (K depth 64) from
+//    HBM to registers with 16-byte buffer loads and from there to LDS; two
+//    LDS stages plus the stage in flight in registers.  The loads of a stage
+//    are spread over the whole iteration before the one that writes them to
+//    LDS, so every load has an iteration to land and the memory pipeline
+//    sees a steady stream instead of one burst per stage (a wave whose load
+//    cannot issue stalls, MFMAs included).  K depth 64 makes every
+//    K-contiguous row one full 128-byte line.  One barrier per stage, before
+//    its last 16-deep substep, publishes the next stage, so that stage's
+//    first fragments are read while the last substep's MFMAs run.
 //  * A lane whose 16-byte vector lies outside the operand gets buffer offset
-//    2^31 and writes zeros; rows past the end fall outside the buffer range.
+//    2^31 and loads zeros; rows past the end fall outside the buffer range.
 //  * LDS keeps each operand in its memory orientation:
 //      - dout for dinp (K-contiguous): [256 rows][64 k], 128-byte rows, chunk
 //        c stored at c ^ (row & 7) ^ ((row >> 3) & 1); fragments are
@@ -56,8 +56,7 @@ constexpr int KC_PITCH = 128;    // K-contiguous LDS row: BK bf16 (one 128-byte 
 constexpr int MN_PITCH = 512;    // M/N-contiguous LDS row: 256 bf16
 constexpr int REGION = 32768;    // one operand of one stage
 constexpr int STAGE = 2 * REGION;
-constexpr int PF_SLOT = 2 * STAGE;          // 1 KB sink for the L2 prefetch loads
-constexpr int LDS_BYTES = PF_SLOT + 1024;
+constexpr int LDS_BYTES = 2 * STAGE;
 constexpr int LOADS = REGION / (NW * 1024); // 1 KB loads per wave per operand per stage
 static_assert(BM * KC_PITCH == REGION && BK * MN_PITCH == REGION, "regions");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -65,7 +64,6 @@ static_assert(MB * NB * 16 * NT == BM * BN, "accumulators cover the tile");
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) char lds_char;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // chunk XOR of 512-byte M/N-contiguous rows, by row & 3: {0, 10, 4, 14}
 __device__ __forceinline__ int sw_mn(int row) { return (0xE4A0 >> ((row & 3) << 2)) & 0xF; }
@@ -76,37 +74,6 @@ __device__ __forceinline__ int sw_kc(int row) { return (row & 7) ^ ((row >> 3) &
 __device__ __forceinline__ bf16x4 tr_read(const char* region, int byte) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_char*)region + byte));
 }
-
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-    return (uint32_t)(size_t)((const lds_char*)p);
-}
-
-// Buffer descriptor words (gfx9 raw buffer, dword3 0x00020000) over
-// [base, base + bytes), num_records clamped below 2^31.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, long long bytes) {
-    const uint64_t a = (uint64_t)base;
-    const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
-    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), n, 0x00020000};
-}
-
-// The compiler reserves m0 and warns when an asm statement clobbers it;
-// these statements set it themselves right before the one instruction that
-// reads it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma16(i32x4 r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
-}
-
-// 4 bytes per lane into LDS at lds + 4 * lane: only used to pull lines into
-// the caches ahead of the real loads.
-__device__ __forceinline__ void touch4(i32x4 r, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Wait until this wave has at most N loads outstanding.
 template <int N>
@@ -183,56 +150,31 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         const int col = n0 + 8 * ((lane & 31) ^ sw_mn(row));
         b_off[i] = col < N ? (uint32_t)((row * ldb + col) * 2) : kOOB;
     }
-    // L2 prefetch geometry: one 4-byte touch per 128-byte line of a stage;
-    // waves 0-3 cover A, waves 4-7 cover B, one load per wave per stage.
-    //   K-contiguous A: row 64(w % 4) + p (one line per row)
-    //   M/N-contiguous: row 16(w % 4) + p/4, line p%4 (4 lines per 512-byte row)
-    const bool pf_a = wave < 4;
-    uint32_t pf_off;
-    {
-        const int w4 = wave & 3;
-        const int row = 16 * w4 + (lane >> 2);
-        const int col = 64 * (lane & 3);
-        if (pf_a) {
-            if constexpr (AK) pf_off = (uint32_t)((64 * w4 + lane) * lda * 2);
-            else pf_off = m0 + col < M ? (uint32_t)((row * lda + m0 + col) * 2) : kOOB;
-        } else {
-            pf_off = n0 + col < N ? (uint32_t)((row * ldb + n0 + col) * 2) : kOOB;
-        }
-    }
-    const uint32_t smem_lds = lds_offset(smem);
 
     auto a_origin = [&](int kt) { return AK ? (long long)m0 * lda + kt * BK : (long long)kt * BK * lda; };
-    // Stage kt into LDS buffer `stage`; a stage past the end (kt >= kt1)
-    // still issues its loads, over an empty range, so that every wave's
-    // count of outstanding loads follows one fixed pattern.
-    auto issue = [&](int kt, int stage) {
+    // Global -> register staging of stage kt, chunk pair j (load j of each
+    // operand).  A stage past the end (kt >= kt1) still issues its loads, over
+    // an empty range (they return zeros), so that every wave's count of
+    // outstanding loads follows one fixed pattern.
+    u32x4 stg_a[LOADS], stg_b[LOADS];
+    auto load_pair = [&](int kt, int j) {
         const bool live = kt < kt1;
         const int k0 = kt * BK;
-        const uint32_t la = smem_lds + stage * STAGE + wave * (LOADS * 1024);
-        const uint32_t lb = la + REGION;
         const long long oa = a_origin(kt);
-        const i32x4 ra = rsrc_words(A + oa, live ? (a_elems - oa) * 2 : 0);
+        const auto ra = make_rsrc(A + oa, live ? (a_elems - oa) * 2 : 0);
         // K tail inside a K-contiguous row: vectors at or past K read zeros
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const uint32_t kmask = AK ? oob_if_ge(k0 + a_kc[i], Kd) : 0u;
-            dma16(ra, a_off[i] | kmask, la + i * 1024);
-        }
+        const uint32_t kmask = AK ? oob_if_ge(k0 + a_kc[j], Kd) : 0u;
+        stg_a[j] = buffer_load16(ra, a_off[j] | kmask, 0);
         const long long ob = (long long)k0 * ldb;
-        const i32x4 rb = rsrc_words(Bp + ob, live ? (b_elems - ob) * 2 : 0);
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) dma16(rb, b_off[i], lb + i * 1024);
+        const auto rb = make_rsrc(Bp + ob, live ? (b_elems - ob) * 2 : 0);
+        stg_b[j] = buffer_load16(rb, b_off[j], 0);
     };
-    // Pull stage kt's lines into the caches (one load per wave; past the end
-    // it reads nothing).
-    auto prefetch = [&](int kt) {
-        const bool live = kt < kt1;
-        const long long oa = a_origin(kt);
-        const long long ob = (long long)kt * BK * ldb;
-        const i32x4 r = pf_a ? rsrc_words(A + oa, live ? (a_elems - oa) * 2 : 0)
-                             : rsrc_words(Bp + ob, live ? (b_elems - ob) * 2 : 0);
-        touch4(r, pf_off, smem_lds + PF_SLOT);
+    // Registers -> LDS buffer `stage`: load j of wave w fills 1 KB block
+    // LOADS * w + j of each operand region, lane p at byte 16p.
+    auto store_pair = [&](int stage, int j) {
+        char* la = smem + stage * STAGE + (LOADS * wave + j) * 1024 + 16 * lane;
+        *(u32x4*)la = stg_a[j];
+        *(u32x4*)(la + REGION) = stg_b[j];
     };
 
     f32x16 acc[MB][NB];
@@ -287,42 +229,50 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
                                                                       0, 0, 0);
     };
 
-    // Ring of two stages.  Loads per wave, in issue order: stage 0, stage 1,
-    // touch of stage 2, then per iteration `it` the loads of stage it+2 and
-    // the touch of stage it+3.  Iteration it runs the substeps of stage it
-    // (buffer it & 1); before its last substep every wave waits for its own
-    // loads of stage it+1 (only the newest touch may still fly), and one
-    // barrier makes stage it+1 visible and retires buffer it & 1, which then
-    // takes the loads of stage it+2 while the last substep runs.
+    // Ring of two LDS stages plus one stage in registers.  Iteration `it`
+    // runs the substeps of stage it (LDS buffer it & 1).  Before substep j it
+    // writes load pair j of stage it+1 from registers into the other buffer
+    // (free since the previous barrier) and reloads those registers with
+    // pair j of stage it+2, so every load has one whole iteration to land
+    // and the loads are spread over the iteration.  One barrier, before the
+    // last substep, makes stage it+1 visible and retires buffer it & 1.
+    // Loads per wave in issue order: pairs 0..3 of each stage; when pair j
+    // of stage it+1 is needed, the 6 loads issued after it may still fly.
     if (nk > 0) {
-        issue(kt0, 0);
-        issue(kt0 + 1, 1);
-        prefetch(kt0 + 2);
-        wait_loads<2 * LOADS + 1>();   // stage 0 landed (this wave's part)
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) load_pair(kt0, j);
+        wait_loads<0>();
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) store_pair(0, j);
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) load_pair(kt0 + 1, j);
         __syncthreads();
         Frag f0, f1;
         read_sub(0, 0, f0);
         for (int it = 0; it < nk; ++it) {
             const int cur = it & 1;
             if (do_bias) bias_add(cur);
-            read_sub(cur, 1, f1);
-            mma_sub(f0);
-            read_sub(cur, 2, f0);
-            mma_sub(f1);
-            read_sub(cur, 3, f1);
-            mma_sub(f0);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_loads<1>();           // stage it+1 landed (this wave's part)
+            // substeps 0..2: pair j of stage it+1 to LDS, pair j of stage it+2
+            // into the registers, fragments of substep j+1, MFMAs of substep j
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                wait_loads<2 * (LOADS - 1)>();
+                store_pair(cur ^ 1, j);
+                load_pair(kt0 + it + 2, j);
+                read_sub(cur, j + 1, (j & 1) ? f0 : f1);
+                mma_sub((j & 1) ? f1 : f0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_loads<2 * (LOADS - 1)>();
+            store_pair(cur ^ 1, 3);
+            load_pair(kt0 + it + 2, 3);
             __syncthreads();
-            issue(kt0 + it + 2, cur);
-            prefetch(kt0 + it + 3);
-            __builtin_amdgcn_sched_barrier(0);
             if (it + 1 < nk) read_sub(cur ^ 1, 0, f0);
             mma_sub(f1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    wait_loads<0>();   // no load may land in LDS after the workgroup moves on
+    wait_loads<0>();
 
     // dbias of this unit's 256 columns: lanes l, l^32 share a column chunk;
     // the 8 waves meet in LDS once every wave is done with the ring
