@@ -79,14 +79,17 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 struct DeviceInfo {
     int cus = 0;
     int xcds = 1;
+    int slots = 1;   // resident workgroups of the tile kernel per CU
 };
 
-// Dispatch model of a grid with one resident workgroup per CU: workgroup i
-// goes to XCD i % xcds, and each XCD starts its workgroups in order on
-// whichever of its CUs frees first.  Returns the makespan in cost units.
+// Dispatch model of a grid with `slots` resident workgroups per CU:
+// workgroup i goes to XCD i % xcds, and each XCD starts its workgroups in
+// order on whichever of its workgroup slots frees first.  Returns the
+// makespan in cost units (one unit: one K iteration of a workgroup that
+// shares its CU with slots - 1 others).
 double simulate(const std::vector<int4>& units, const std::vector<double>& cost,
                 const DeviceInfo& dev) {
-    const int per = std::max(1, dev.cus / dev.xcds);
+    const int per = std::max(1, dev.cus / dev.xcds) * std::max(1, dev.slots);
     double worst = 0;
     std::vector<double> slots(per);
     for (int x = 0; x < dev.xcds; ++x) {
@@ -197,7 +200,8 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     g[UNIT_DINP] = GemmPlan{BT, C, OC, cdiv(BT, ts.BM), cdiv(C, ts.BN), 1, cdiv(OC, ts.BK), 0, 0};
 
     const CostModel cm;
-    const double t_iter = iter_us(dtype, ts) / cm.mfma_efficiency;
+    // workgroups sharing a CU share its MFMA rate
+    const double t_iter = iter_us(dtype, ts) * std::max(1, dev.slots) / cm.mfma_efficiency;
     int best_sw = 1, best_si = 1;
     double best = 1e300;
     const int max_sw = std::min(16, g[UNIT_DWEIGHT].kiters);
@@ -318,6 +322,7 @@ int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
     DeviceInfo di;
     int st = device_info(dev, &di);
     if (st != MMB_OK) return st;
+    di.slots = tiles_resident(dtype);
     Plan p = build_plan(dtype, BT, C, OC, bias, di, fsw, fsi);
     p.forced_sw = fsw;
     p.forced_si = fsi;
@@ -455,6 +460,7 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
     mmb::DeviceInfo di;
     di.cus = num_cus;
     di.xcds = num_cus >= 128 ? 8 : 1;
+    di.slots = mmb::tiles_resident(dtype);
     const mmb::Plan p = mmb::build_plan(dtype, B * T, C, OC, has_bias != 0, di,
                                         mmb::env_int("MMB_SPLITS_DWEIGHT"),
                                         mmb::env_int("MMB_SPLITS_DINP"));

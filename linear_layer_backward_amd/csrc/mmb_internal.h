@@ -47,6 +47,10 @@ hipError_t launch_tiles(int dtype, const TilesParams& p, hipStream_t s);
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s);
 int tiles_bf16_bk();   // K depth of one stage of the bf16 tiles
 int tiles_bf16_bn();   // output columns of one bf16 tile
+// Workgroups of the MFMA tile kernel for `dtype` that fit on one CU at once
+// (LDS and register limits of the kernel as built).
+int tiles_resident(int dtype);
+int tiles_bf16_resident();
 hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
                           const void* dout, const void* inp, const void* weight,
                           int BT, int C, int OC, hipStream_t s);

@@ -31,12 +31,14 @@
 //    last-arriver sum are the shared helpers of mmb_tile_common.h.
 //  * dbias: the dweight units of column tile 0 sum the dout values they
 //    stage; a 3-step xor shuffle combines the 8 threads sharing a column.
+#include <algorithm>
+
 #include "mmb_tile_common.h"
 
 namespace mmb {
 namespace {
 
-constexpr int kRowBytes = 128;  // one LDS row: BK floats of one m or n  // one LDS row: BK elements of one m or n
+constexpr int kRowBytes = 128;  // one LDS row: BK floats of one m or n
 
 template <typename T> struct Cfg;
 template <> struct Cfg<float> {
@@ -292,6 +294,13 @@ __global__ __launch_bounds__(kThreads) void mmb_tiles_kernel(TilesParams p) {
 TileShape tile_shape(int dtype) {
     if (dtype == 1) return TileShape{256, tiles_bf16_bn(), tiles_bf16_bk()};
     return TileShape{K<float>::BM, K<float>::BN, K<float>::BK};
+}
+
+// fp32: two workgroups per CU (LDS, and at most 128 registers per lane for
+// two waves per SIMD)
+int tiles_resident(int dtype) {
+    if (dtype == 1) return tiles_bf16_resident();
+    return std::min(2, (160 * 1024) / (K<float>::LDS_BYTES + 16));
 }
 
 hipError_t launch_tiles(int dtype, const TilesParams& p, hipStream_t s) {

@@ -390,6 +390,8 @@ __global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
 
 int tiles_bf16_bk() { return BK; }
 int tiles_bf16_bn() { return BN; }
+// one workgroup per CU: the ring and the epilogue tile take most of the 160 KB LDS
+int tiles_bf16_resident() { return (160 * 1024) / LDS_BYTES; }
 
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s) {
     if (p.n_units <= 0) return hipSuccess;
