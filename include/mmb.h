@@ -95,12 +95,15 @@ int mmb_path(const void* dinp, const void* dweight, const void* dbias,
              int B, int T, int C, int OC, int dtype);
 
 /* Host-only view of the work plan the MFMA path would use on a device with
- * `num_cus` compute units (8 XCDs when num_cus >= 128): writes the split
- * counts {dweight, dinp} to splits[2] and, when `units` is not NULL, up to
- * max_units launch-ordered work units as 4 ints each {kind (0 = dweight,
- * 1 = dinp), tile_m, tile_n, split}.  Returns the number of units, or a
- * negative mmb_status.  Honours the MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP
- * environment overrides like mmb_backward.  Makes no HIP call. */
+ * `num_cus` compute units (8 XCDs when num_cus >= 128): writes the largest
+ * split count of each GEMM's tiles {dweight, dinp} to splits[2] and, when
+ * `units` is not NULL, up to max_units launch-ordered work units as 8 ints
+ * each {kind (0 = dweight, 1 = dinp), tile_m, tile_n, split, kt0, kt1,
+ * splits of this tile, first workspace slot of this tile}: the unit covers
+ * K iterations [kt0, kt1) of its output tile.  Returns the number of units,
+ * or a negative mmb_status.  Honours the MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP
+ * environment overrides (one split count for every tile of that GEMM) like
+ * mmb_backward.  Makes no HIP call. */
 int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
                    int* splits, int* units, int max_units);
 

@@ -15,7 +15,9 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <queue>
 #include <tuple>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/mmb.h"
@@ -82,87 +84,119 @@ struct DeviceInfo {
     int slots = 1;   // resident workgroups of the tile kernel per CU
 };
 
-// Dispatch model of a grid with `slots` resident workgroups per CU:
-// workgroup i goes to XCD i % xcds, and each XCD starts its workgroups in
-// order on whichever of its workgroup slots frees first.  Returns the
-// makespan in cost units (one unit: one K iteration of a workgroup that
-// shares its CU with slots - 1 others).
-double simulate(const std::vector<int4>& units, const std::vector<double>& cost,
-                const DeviceInfo& dev) {
-    const int per = std::max(1, dev.cus / dev.xcds) * std::max(1, dev.slots);
-    double worst = 0;
-    std::vector<double> slots(per);
-    for (int x = 0; x < dev.xcds; ++x) {
-        std::fill(slots.begin(), slots.end(), 0.0);
-        for (size_t i = x; i < units.size(); i += dev.xcds) {
-            auto it = std::min_element(slots.begin(), slots.end());
-            *it += cost[i];
-        }
-        worst = std::max(worst, *std::max_element(slots.begin(), slots.end()));
-    }
-    return worst;
-}
+struct Unit {
+    int4 a;   // {kind, tile_m, tile_n, split}
+    int4 b;   // {kt0, kt1, splits of the tile, first workspace slot of the tile}
+};
 
 struct Plan {
     TilesParams proto;            // pointers filled per call
-    std::vector<int4> units;      // launch order
+    std::vector<Unit> units;      // launch order
     int4* d_units = nullptr;      // device copy (owned by the plan cache)
+    int max_splits[2] = {1, 1};   // largest split count of each GEMM's tiles
     long long ws_floats = 0;
     long long ws_bias_floats = 0;
     int n_counters = 0;
     int forced_sw = 0, forced_si = 0;
 };
 
-// Order of one GEMM's units for L2 reuse inside an XCD: tiles that share an
-// operand slab are adjacent.  dinp units share dout rows along tile_n;
-// dweight units share the inp rows of one split and the dout columns of one
-// tile_m, so they are ordered (split, tile_m, tile_n).
-void gemm_units(int kind, const GemmPlan& g, std::vector<int4>& out) {
-    if (kind == UNIT_DINP) {
-        for (int m = 0; m < g.tiles_m; ++m)
-            for (int s = 0; s < g.splits; ++s)
-                for (int n = 0; n < g.tiles_n; ++n) out.push_back(make_int4(kind, m, n, s));
-    } else {
-        for (int s = 0; s < g.splits; ++s)
-            for (int m = 0; m < g.tiles_m; ++m)
-                for (int n = 0; n < g.tiles_n; ++n) out.push_back(make_int4(kind, m, n, s));
+// Cost of the pieces of a unit, in microseconds, for the tile kernels as
+// built (measured on MI355X: per-workgroup K-iteration time with `slots`
+// workgroups per CU, the first-stage load, the beta = 1 epilogue, publishing
+// one fp32 partial tile and reading one back in the fix-up).
+struct CostModel {
+    double t_iter[2];              // [UNIT_DWEIGHT], [UNIT_DINP]
+    double prologue, epilogue, publish, fix_per_partial;
+    double partial_bytes_per_us;   // workspace traffic the whole GPU absorbs
+};
+
+// MMB_PLAN_MODEL="t_dweight,t_dinp,prologue,epilogue,publish,fix,bytes_per_us"
+// replaces the constants (tuning aid for other devices or kernels).
+CostModel cost_model(int dtype) {
+    CostModel cm = dtype == MMB_BF16 ? CostModel{{1.83, 1.63}, 3.0, 10.0, 2.4, 2.1, 8.0e6}
+                                     : CostModel{{5.7, 4.6}, 2.0, 5.0, 1.2, 1.0, 8.0e6};
+    if (const char* v = std::getenv("MMB_PLAN_MODEL")) {
+        double x[7];
+        if (std::sscanf(v, "%lf,%lf,%lf,%lf,%lf,%lf,%lf", &x[0], &x[1], &x[2], &x[3], &x[4], &x[5],
+                        &x[6]) == 7)
+            cm = CostModel{{x[0], x[1]}, x[2], x[3], x[4], x[5], x[6]};
     }
+    return cm;
 }
 
-int unit_iters(const GemmPlan& g, int split) {
-    const long long k0 = (long long)split * g.kiters / g.splits;
-    const long long k1 = (long long)(split + 1) * g.kiters / g.splits;
-    return (int)(k1 - k0);
-}
+// Per-tile split counts of the two GEMMs (row-major tile index).
+struct Layout {
+    std::vector<int> splits[2];
+};
 
-// Launch order: each XCD receives a contiguous run of the longer GEMM's units
-// followed by a contiguous run of the shorter one's (longest first inside an
-// XCD), interleaved so that workgroup i lands on XCD i % xcds.
-std::vector<int4> order_units(const GemmPlan g[2], const DeviceInfo& dev) {
-    std::vector<int4> a, b;
-    const double la = (double)g[UNIT_DWEIGHT].kiters / g[UNIT_DWEIGHT].splits;
-    const double lb = (double)g[UNIT_DINP].kiters / g[UNIT_DINP].splits;
-    const int first = la >= lb ? UNIT_DWEIGHT : UNIT_DINP;
-    gemm_units(first, g[first], a);
-    gemm_units(1 - first, g[1 - first], b);
+// Launch order.  Inside one GEMM, tiles with fewer splits (longer units)
+// come first; among equal ones, dweight units are ordered (split, tile_m,
+// tile_n) so that units running together share the inp rows of one K range
+// and the dout columns of one tile_m, and dinp units (tile_m, split, tile_n)
+// so that they share dout rows.  Each XCD then receives a contiguous run of
+// the GEMM with the longer units followed by a contiguous run of the other,
+// interleaved so that workgroup i lands on XCD i % xcds.
+std::vector<Unit> make_units(const GemmPlan g[2], const Layout& L, const DeviceInfo& dev) {
+    std::vector<Unit> per[2];
+    int slot = 0;
+    std::vector<int> slot_of[2];
+    for (int k = 0; k < 2; ++k) {
+        slot_of[k].assign(L.splits[k].size(), 0);
+        for (size_t t = 0; t < L.splits[k].size(); ++t) {
+            slot_of[k][t] = slot;
+            if (L.splits[k][t] > 1) slot += L.splits[k][t];
+        }
+    }
+    for (int k = 0; k < 2; ++k) {
+        const GemmPlan& G = g[k];
+        std::vector<int> levels(L.splits[k].begin(), L.splits[k].end());
+        std::sort(levels.begin(), levels.end());
+        levels.erase(std::unique(levels.begin(), levels.end()), levels.end());
+        for (int S : levels) {
+            auto emit = [&](int m, int n, int s) {
+                const int t = m * G.tiles_n + n;
+                if (L.splits[k][t] != S) return;
+                const int kt0 = (int)((long long)s * G.kiters / S);
+                const int kt1 = (int)((long long)(s + 1) * G.kiters / S);
+                per[k].push_back(Unit{make_int4(k, m, n, s), make_int4(kt0, kt1, S, slot_of[k][t])});
+            };
+            if (k == UNIT_DINP) {
+                for (int m = 0; m < G.tiles_m; ++m)
+                    for (int s = 0; s < S; ++s)
+                        for (int n = 0; n < G.tiles_n; ++n) emit(m, n, s);
+            } else {
+                for (int s = 0; s < S; ++s)
+                    for (int m = 0; m < G.tiles_m; ++m)
+                        for (int n = 0; n < G.tiles_n; ++n) emit(m, n, s);
+            }
+        }
+    }
+    auto longest = [&](int k) {
+        int x = 0;
+        for (const Unit& u : per[k]) x = std::max(x, u.b.y - u.b.x);
+        return x;
+    };
+    const int first = longest(UNIT_DWEIGHT) >= longest(UNIT_DINP) ? UNIT_DWEIGHT : UNIT_DINP;
+    const std::vector<Unit>& a = per[first];
+    const std::vector<Unit>& b = per[1 - first];
     const int X = dev.xcds;
     const size_t n = a.size() + b.size();
-    std::vector<std::vector<int4>> seq(X);
+    std::vector<std::vector<Unit>> seq(X);
     size_t pa = 0, pb = 0;
-    bool ok = true;
     for (int x = 0; x < X; ++x) {
-        const long long cnt = (long long)(n / X) + ((size_t)x < n % X ? 1 : 0);
-        const long long ca = (long long)(a.size() / X) + ((size_t)x < a.size() % X ? 1 : 0);
-        const long long cb = cnt - ca;
-        if (cb < 0 || pb + cb > b.size()) { ok = false; break; }
+        const size_t cnt = n / X + ((size_t)x < n % X ? 1 : 0);
+        size_t ca = a.size() / X + ((size_t)x < a.size() % X ? 1 : 0);
+        ca = std::min(ca, cnt);
+        size_t cb = std::min(cnt - ca, b.size() - pb);
+        ca = cnt - cb;
         seq[x].insert(seq[x].end(), a.begin() + pa, a.begin() + pa + ca);
         seq[x].insert(seq[x].end(), b.begin() + pb, b.begin() + pb + cb);
         pa += ca;
         pb += cb;
     }
-    std::vector<int4> out;
+    std::vector<Unit> out;
     out.reserve(n);
-    if (!ok || pa != a.size() || pb != b.size()) {
+    if (pa != a.size() || pb != b.size()) {
         out = a;
         out.insert(out.end(), b.begin(), b.end());
         return out;
@@ -171,23 +205,65 @@ std::vector<int4> order_units(const GemmPlan g[2], const DeviceInfo& dev) {
     return out;
 }
 
-// Cost model, in units of one K-iteration of a full tile on one CU.  A unit
-// costs its iterations plus a fixed prologue/epilogue.  Split tiles add
-// their partials' traffic: every partial tile is written once and read once
-// by the tile's last arriver; that traffic competes for HBM with everything
-// else, so it is charged to the makespan at an effective bandwidth.
-struct CostModel {
-    double unit_overhead = 1.5;
-    double hbm_bytes_per_us = 4.0e6;   // effective, below the 8 TB/s peak
-    double mfma_efficiency = 0.7;
-};
+// Dispatch model of a grid with `slots` resident workgroups per CU:
+// workgroup i goes to XCD i % xcds, and each XCD starts its workgroups in
+// order on whichever of its workgroup slots frees first.  The last unit to
+// finish of a split tile also reads every partial back and writes the tile.
+// Returns the makespan (us) plus the time the whole GPU needs to move the
+// workspace traffic; the finish time of every unit in `fin` if not NULL.
+double simulate(const std::vector<Unit>& units, const CostModel& cm, const DeviceInfo& dev,
+                std::vector<double>* fin) {
+    const int per = std::max(1, dev.cus / dev.xcds) * std::max(1, dev.slots);
+    std::vector<double> d(units.size()), f(units.size());
+    for (size_t i = 0; i < units.size(); ++i) {
+        const Unit& u = units[i];
+        d[i] = cm.prologue + (u.b.y - u.b.x) * cm.t_iter[u.a.x] + (u.b.z > 1 ? cm.publish : cm.epilogue);
+    }
+    auto run = [&]() {
+        double span = 0;
+        for (int x = 0; x < dev.xcds; ++x) {
+            std::priority_queue<double, std::vector<double>, std::greater<double>> q;
+            for (int c = 0; c < per; ++c) q.push(0.0);
+            for (size_t i = x; i < units.size(); i += dev.xcds) {
+                f[i] = q.top() + d[i];
+                q.pop();
+                q.push(f[i]);
+                span = std::max(span, f[i]);
+            }
+        }
+        return span;
+    };
+    run();
+    // last arrivers of split tiles (tile_m and tile_n are below 2^16 here)
+    std::unordered_map<long long, size_t> last;
+    last.reserve(units.size());
+    for (size_t i = 0; i < units.size(); ++i) {
+        const Unit& u = units[i];
+        if (u.b.z <= 1) continue;
+        const long long key = ((long long)u.a.x << 40) | ((long long)u.a.y << 20) | u.a.z;
+        auto it = last.find(key);
+        if (it == last.end()) last.emplace(key, i);
+        else if (f[i] > f[it->second]) it->second = i;
+    }
+    for (const auto& kv : last) {
+        const Unit& u = units[kv.second];
+        d[kv.second] += u.b.z * cm.fix_per_partial + cm.epilogue;
+    }
+    const double span = run();
+    if (fin) *fin = f;
+    return span;
+}
 
-double iter_us(int dtype, const TileShape& ts) {
-    // per-CU dense MFMA rate on gfx950 at 2.4 GHz: 4096 (bf16) / 256 (fp32)
-    // flops per clock
-    const double flops = 2.0 * ts.BM * ts.BN * ts.BK;
-    const double per_clk = dtype == MMB_BF16 ? 4096.0 : 256.0;
-    return flops / per_clk / 2400.0;
+double plan_cost(const GemmPlan g[2], const Layout& L, const DeviceInfo& dev, const CostModel& cm,
+                 double tile_bytes, std::vector<Unit>* units_out, std::vector<double>* fin) {
+    std::vector<Unit> u = make_units(g, L, dev);
+    double partials = 0;
+    for (int k = 0; k < 2; ++k)
+        for (int s : L.splits[k])
+            if (s > 1) partials += s;
+    const double t = simulate(u, cm, dev, fin) + 2.0 * partials * tile_bytes / cm.partial_bytes_per_us;
+    if (units_out) *units_out = std::move(u);
+    return t;
 }
 
 Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& dev,
@@ -195,70 +271,90 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     const TileShape ts = tile_shape(dtype);
     GemmPlan g[2];
     // dweight[OC,C] += dout^T[OC,BT] . inp[BT,C]
-    g[UNIT_DWEIGHT] = GemmPlan{OC, C, BT, cdiv(OC, ts.BM), cdiv(C, ts.BN), 1, cdiv(BT, ts.BK), 0, 0};
+    g[UNIT_DWEIGHT] = GemmPlan{OC, C, BT, cdiv(OC, ts.BM), cdiv(C, ts.BN), cdiv(BT, ts.BK), 0};
     // dinp[BT,C] += dout[BT,OC] . weight[OC,C]
-    g[UNIT_DINP] = GemmPlan{BT, C, OC, cdiv(BT, ts.BM), cdiv(C, ts.BN), 1, cdiv(OC, ts.BK), 0, 0};
+    g[UNIT_DINP] = GemmPlan{BT, C, OC, cdiv(BT, ts.BM), cdiv(C, ts.BN), cdiv(OC, ts.BK), 0};
+    g[UNIT_DINP].tile_base = g[UNIT_DWEIGHT].tiles_m * g[UNIT_DWEIGHT].tiles_n;
+    const int ntiles[2] = {g[0].tiles_m * g[0].tiles_n, g[1].tiles_m * g[1].tiles_n};
+    const CostModel cm = cost_model(dtype);
+    const double tile_bytes = 4.0 * ts.BM * ts.BN;
+    const int max_s[2] = {std::min(16, g[UNIT_DWEIGHT].kiters), std::min(8, g[UNIT_DINP].kiters)};
 
-    const CostModel cm;
-    // workgroups sharing a CU share its MFMA rate
-    const double t_iter = iter_us(dtype, ts) * std::max(1, dev.slots) / cm.mfma_efficiency;
-    int best_sw = 1, best_si = 1;
+    // MMB_PLAN_TRACE=1 prints the modelled cost of every candidate to stderr
+    const bool trace = std::getenv("MMB_PLAN_TRACE") != nullptr;
+    // 1. one split count per GEMM
+    Layout best_L;
     double best = 1e300;
-    const int max_sw = std::min(16, g[UNIT_DWEIGHT].kiters);
-    const int max_si = std::min(8, g[UNIT_DINP].kiters);
-    for (int sw = 1; sw <= max_sw; ++sw) {
-        for (int si = 1; si <= max_si; ++si) {
-            if (force_sw > 0 && sw != force_sw) continue;
-            if (force_si > 0 && si != force_si) continue;
-            GemmPlan h[2] = {g[0], g[1]};
-            h[UNIT_DWEIGHT].splits = sw;
-            h[UNIT_DINP].splits = si;
-            std::vector<int4> u = order_units(h, dev);
-            std::vector<double> cost(u.size());
-            for (size_t i = 0; i < u.size(); ++i)
-                cost[i] = unit_iters(h[u[i].x], u[i].w) + cm.unit_overhead;
-            double t = simulate(u, cost, dev);
-            double partial_bytes = 0;
-            for (int k = 0; k < 2; ++k)
-                if (h[k].splits > 1)
-                    partial_bytes += 2.0 * h[k].splits * h[k].tiles_m * h[k].tiles_n * ts.BM *
-                                     ts.BN * 4.0;
-            t += partial_bytes / cm.hbm_bytes_per_us / t_iter;
+    for (int sw = 1; sw <= max_s[0]; ++sw) {
+        for (int si = 1; si <= max_s[1]; ++si) {
+            if (force_sw > 0 && sw != std::min(force_sw, max_s[0])) continue;
+            if (force_si > 0 && si != std::min(force_si, max_s[1])) continue;
+            Layout L;
+            L.splits[UNIT_DWEIGHT].assign(ntiles[0], sw);
+            L.splits[UNIT_DINP].assign(ntiles[1], si);
+            const double t = plan_cost(g, L, dev, cm, tile_bytes, nullptr, nullptr);
+            if (trace) std::fprintf(stderr, "mmb plan: dweight splits %d dinp splits %d cost %.2f us\n", sw, si, t);
             if (t < best - 1e-9) {
                 best = t;
-                best_sw = sw;
-                best_si = si;
+                best_L = L;
             }
         }
     }
-    if (force_sw > 0) best_sw = std::min(force_sw, max_sw);
-    if (force_si > 0) best_si = std::min(force_si, max_si);
-    g[UNIT_DWEIGHT].splits = best_sw;
-    g[UNIT_DINP].splits = best_si;
+    // 2. unless forced: cut the tiles whose units finish last into more
+    // units while the modelled makespan keeps falling
+    if (force_sw <= 0 && force_si <= 0) {
+        std::vector<Unit> u;
+        std::vector<double> fin;
+        for (int round = 0; round < 64; ++round) {
+            plan_cost(g, best_L, dev, cm, tile_bytes, &u, &fin);
+            std::vector<size_t> order(u.size());
+            for (size_t i = 0; i < u.size(); ++i) order[i] = i;
+            std::sort(order.begin(), order.end(), [&](size_t x, size_t y) { return fin[x] > fin[y]; });
+            bool improved = false;
+            std::vector<std::pair<int, int>> tried;
+            for (size_t c = 0; c < order.size() && c < 8 && !improved; ++c) {
+                const Unit& x = u[order[c]];
+                const int k = x.a.x, t = x.a.y * g[k].tiles_n + x.a.z;
+                if (std::find(tried.begin(), tried.end(), std::make_pair(k, t)) != tried.end()) continue;
+                tried.push_back({k, t});
+                const int S = best_L.splits[k][t];
+                const int S2 = std::min(max_s[k], S + std::max(1, S / 2));
+                if (S2 <= S) continue;
+                Layout L = best_L;
+                // every tile of this GEMM with the same split count and a
+                // unit among the last to finish is cut the same way
+                L.splits[k][t] = S2;
+                const double tc = plan_cost(g, L, dev, cm, tile_bytes, nullptr, nullptr);
+                if (trace)
+                    std::fprintf(stderr, "mmb plan: %s tile %d splits %d -> %d cost %.2f us\n",
+                                 k == UNIT_DINP ? "dinp" : "dweight", t, S, S2, tc);
+                if (tc < best * 0.999) {
+                    best = tc;
+                    best_L = L;
+                    improved = true;
+                }
+            }
+            if (!improved) break;
+        }
+    }
 
     Plan p;
     std::memset(&p.proto, 0, sizeof(p.proto));
-    long long ws = 0;
-    int tiles = 0;
-    for (int k = 0; k < 2; ++k) {
-        g[k].tile_base = tiles;
-        g[k].ws_base = ws;
-        if (g[k].splits > 1) {
-            tiles += g[k].tiles_m * g[k].tiles_n;
-            ws += (long long)g[k].tiles_m * g[k].tiles_n * g[k].splits * ts.BM * ts.BN;
+    p.units = make_units(g, best_L, dev);
+    long long slots = 0;
+    for (int k = 0; k < 2; ++k)
+        for (int s : best_L.splits[k]) {
+            p.max_splits[k] = std::max(p.max_splits[k], s);
+            if (s > 1) slots += s;
         }
-    }
-    p.ws_floats = ws;
-    p.ws_bias_floats = bias && g[UNIT_DWEIGHT].splits > 1
-                           ? (long long)g[UNIT_DWEIGHT].tiles_m * g[UNIT_DWEIGHT].splits * ts.BM
-                           : 0;
-    p.n_counters = tiles;
+    p.ws_floats = slots * ts.BM * ts.BN;
+    p.ws_bias_floats = bias ? slots * ts.BM : 0;
+    p.n_counters = ntiles[0] + ntiles[1];
     p.proto.BT = BT;
     p.proto.C = C;
     p.proto.OC = OC;
     p.proto.g[0] = g[0];
     p.proto.g[1] = g[1];
-    p.units = order_units(g, dev);
     p.proto.n_units = (int)p.units.size();
     return p;
 }
@@ -326,13 +422,14 @@ int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
     Plan p = build_plan(dtype, BT, C, OC, bias, di, fsw, fsi);
     p.forced_sw = fsw;
     p.forced_si = fsi;
-    const size_t ub = p.units.size() * sizeof(int4);
+    const size_t ub = p.units.size() * sizeof(Unit);
     if (hipMalloc(&p.d_units, ub) != hipSuccess) return MMB_ERR_NOMEM;
     if (hipMemcpy(p.d_units, p.units.data(), ub, hipMemcpyHostToDevice) != hipSuccess) {
         (void)hipFree(p.d_units);
         return MMB_ERR_HIP;
     }
     p.proto.units = p.d_units;
+    static_assert(sizeof(Unit) == 2 * sizeof(int4), "two int4 per unit");
     auto res = g_plans.emplace(key, std::move(p));
     *out = &res.first->second;
     return MMB_OK;
@@ -464,15 +561,14 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
     const mmb::Plan p = mmb::build_plan(dtype, B * T, C, OC, has_bias != 0, di,
                                         mmb::env_int("MMB_SPLITS_DWEIGHT"),
                                         mmb::env_int("MMB_SPLITS_DINP"));
-    splits[0] = p.proto.g[mmb::UNIT_DWEIGHT].splits;
-    splits[1] = p.proto.g[mmb::UNIT_DINP].splits;
+    splits[0] = p.max_splits[mmb::UNIT_DWEIGHT];
+    splits[1] = p.max_splits[mmb::UNIT_DINP];
     if (units) {
         const int n = std::min<int>(max_units, (int)p.units.size());
         for (int i = 0; i < n; ++i) {
-            units[4 * i + 0] = p.units[i].x;
-            units[4 * i + 1] = p.units[i].y;
-            units[4 * i + 2] = p.units[i].z;
-            units[4 * i + 3] = p.units[i].w;
+            const int4 a = p.units[i].a, b = p.units[i].b;
+            const int v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            for (int j = 0; j < 8; ++j) units[8 * i + j] = v[j];
         }
     }
     return (int)p.units.size();

@@ -7,17 +7,19 @@
 
 namespace mmb {
 
-// One unit of work of the tiled kernel: a (tile_m, tile_n) output tile of one
-// GEMM over the K-iteration range of split `split`.
+// One unit of work of the tiled kernel: the K iterations [kt0, kt1) of a
+// (tile_m, tile_n) output tile of one GEMM.  A tile is cut into `splits`
+// units (its own count: tiles of one GEMM may differ); the units of a split
+// tile publish fp32 partial sums to workspace slots slot .. slot+splits-1
+// (slot counts whole tiles) and the last to arrive finishes the tile.
+// Encoded as two int4: {kind, tile_m, tile_n, split}, {kt0, kt1, splits, slot}.
 enum UnitKind : int { UNIT_DWEIGHT = 0, UNIT_DINP = 1 };
 
 struct GemmPlan {
     int M, N, K;          // D[M,N] += A[M,K] . B[K,N]
     int tiles_m, tiles_n; // ceil(M/BM), ceil(N/BN)
-    int splits;           // K split into this many ranges (1 = no split)
     int kiters;           // ceil(K/BK)
     int tile_base;        // index of tile (0,0) in the counter array
-    long long ws_base;    // float offset of this GEMM's partial tiles in the workspace
 };
 
 // Everything the tiled kernel needs, passed by value.
@@ -30,11 +32,11 @@ struct TilesParams {
     const void* weight;
     int BT, C, OC;
     GemmPlan g[2];        // [UNIT_DWEIGHT], [UNIT_DINP]
-    const int4* units;    // {kind, tile_m, tile_n, split}, in launch order
+    const int4* units;    // two int4 per unit (see above), in launch order
     int n_units;
-    float* ws;            // split-K partial tiles (fp32)
-    float* ws_bias;       // split-K partial dbias rows (fp32)
-    int* counters;        // one arrival counter per split tile, zero at rest
+    float* ws;            // split-K partial tiles (fp32), one tile per slot
+    float* ws_bias;       // split-K partial dbias rows (fp32), BM floats per slot
+    int* counters;        // one arrival counter per tile, zero at rest
 };
 
 // Tile shapes of the MFMA kernels (rows x cols of the output tile, K depth of

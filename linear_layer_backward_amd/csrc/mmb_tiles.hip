@@ -127,7 +127,7 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, int wm
 // otherwise it is M-contiguous (dweight: A = dout^T).  B is always
 // N-contiguous (weight for dinp, inp for dweight).
 template <typename T, bool AK>
-__device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u,
+__device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u, int4 v,
                                          char* smem, int* s_flag) {
     using Kt = K<T>;
     constexpr int BM = Kt::BM, BN = Kt::BN, BK = Kt::BK, E = Kt::E;
@@ -135,8 +135,9 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const int tile_m = u.y, tile_n = u.z, split = u.w;
     const int M = g.M, N = g.N, Kd = g.K;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int kt0 = (int)((long long)split * g.kiters / g.splits);
-    const int kt1 = (int)((long long)(split + 1) * g.kiters / g.splits);
+    // K iterations [kt0, kt1) of a tile cut into `splits` units; the tile's
+    // partial sums (if any) start at workspace slot `slot`
+    const int kt0 = v.x, kt1 = v.y, splits = v.z, slot = v.w;
 
     const T* A = (const T*)p.dout;                       // ld = OC either way
     const T* Bop = (const T*)(AK ? p.weight : p.inp);    // ld = C
@@ -249,20 +250,20 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     }
 
     const bool bias_owner = do_bias && kg == 0 && a_active;
-    if (g.splits > 1) {
+    if (splits > 1) {
         const int tile = tile_m * g.tiles_n + tile_n;
-        float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
+        float* w0 = p.ws + (long long)slot * (BM * BN);
         publish_partial<Kt::MB, Kt::NB, kThreads>(w0 + (long long)split * (BM * BN), acc, tid);
-        float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + xg * E;
+        float* wb = p.ws_bias + (long long)slot * BM + xg * E;
         if (bias_owner) {
 #pragma unroll
             for (int x = 0; x < E; ++x) publish_bias(wb + split * BM + x, bsum[x]);
         }
-        if (!arrive_last(p.counters + g.tile_base + tile, g.splits, s_flag)) return;
-        sum_partials<Kt::MB, Kt::NB, kThreads>(w0, g.splits, BM * BN, acc, tid);
+        if (!arrive_last(p.counters + g.tile_base + tile, splits, s_flag)) return;
+        sum_partials<Kt::MB, Kt::NB, kThreads>(w0, splits, BM * BN, acc, tid);
         if (bias_owner) {
 #pragma unroll
-            for (int x = 0; x < E; ++x) bsum[x] = sum_bias(wb + x, g.splits, BM);
+            for (int x = 0; x < E; ++x) bsum[x] = sum_bias(wb + x, splits, BM);
         }
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
@@ -282,11 +283,11 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void mmb_tiles_kernel(TilesParams p) {
     __shared__ __attribute__((aligned(16))) char smem[K<T>::LDS_BYTES];
     __shared__ int s_flag;
-    const int4 u = p.units[blockIdx.x];
+    const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
     if (u.x == UNIT_DINP)
-        run_unit<T, true>(p, p.g[UNIT_DINP], u, smem, &s_flag);
+        run_unit<T, true>(p, p.g[UNIT_DINP], u, v, smem, &s_flag);
     else
-        run_unit<T, false>(p, p.g[UNIT_DWEIGHT], u, smem, &s_flag);
+        run_unit<T, false>(p, p.g[UNIT_DWEIGHT], u, v, smem, &s_flag);
 }
 
 }  // namespace

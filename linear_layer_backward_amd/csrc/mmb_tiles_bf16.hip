@@ -172,15 +172,16 @@ __device__ __forceinline__ void write_tile_lds(bf16_t* D, long long ldd, int M, 
 // (weight for dinp, inp for dweight).  Leading dimensions: dout OC, weight
 // and inp C, output C.
 template <bool AK>
-__device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u,
+__device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u, int4 v,
                                          char* smem, int* s_flag) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int tile_m = u.y, tile_n = u.z, split = u.w;
     const int M = g.M, N = g.N, Kd = g.K;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
-    const int kt0 = (int)((long long)split * g.kiters / g.splits);
-    const int kt1 = (int)((long long)(split + 1) * g.kiters / g.splits);
+    // K iterations [kt0, kt1) of a tile cut into `splits` units; the tile's
+    // partial sums (if any) start at workspace slot `slot`
+    const int kt0 = v.x, kt1 = v.y, splits = v.z, slot = v.w;
     const int nk = kt1 - kt0;
 
     const bf16_t* A = (const bf16_t*)p.dout;
@@ -358,15 +359,15 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         }
     }
 
-    if (g.splits > 1) {
+    if (splits > 1) {
         const int tile = tile_m * g.tiles_n + tile_n;
-        float* w0 = p.ws + g.ws_base + (long long)tile * g.splits * (BM * BN);
+        float* w0 = p.ws + (long long)slot * (BM * BN);
         publish_partial<MB, NB, NT>(w0 + (long long)split * (BM * BN), acc, tid);
-        float* wb = p.ws_bias + (long long)tile_m * g.splits * BM + tid;
+        float* wb = p.ws_bias + (long long)slot * BM + tid;
         if (do_bias && tid < BM) publish_bias(wb + split * BM, bias);
-        if (!arrive_last(p.counters + g.tile_base + tile, g.splits, s_flag)) return;
-        sum_partials<MB, NB, NT>(w0, g.splits, BM * BN, acc, tid);
-        if (do_bias && tid < BM) bias = sum_bias(wb, g.splits, BM);
+        if (!arrive_last(p.counters + g.tile_base + tile, splits, s_flag)) return;
+        sum_partials<MB, NB, NT>(w0, splits, BM * BN, acc, tid);
+        if (do_bias && tid < BM) bias = sum_bias(wb, splits, BM);
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
@@ -379,11 +380,11 @@ __global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
     // the split-K ticket flag lives in the ring, used only after the K loop
     // (the dbias reduction uses the first 8 KB)
     int* s_flag = (int*)(smem + 8192);
-    const int4 u = p.units[blockIdx.x];
+    const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
     if (u.x == UNIT_DINP)
-        run_unit<true>(p, p.g[UNIT_DINP], u, smem, s_flag);
+        run_unit<true>(p, p.g[UNIT_DINP], u, v, smem, s_flag);
     else
-        run_unit<false>(p, p.g[UNIT_DWEIGHT], u, smem, s_flag);
+        run_unit<false>(p, p.g[UNIT_DWEIGHT], u, v, smem, s_flag);
 }
 
 }  // namespace

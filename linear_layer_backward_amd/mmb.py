@@ -106,15 +106,16 @@ def mmb_release() -> None:
 
 
 def mmb_plan_units(B, T, C, OC, dtype, has_bias, num_cus):
-    """(splits {dweight, dinp}, list of (kind, tile_m, tile_n, split)) of the
+    """(largest split counts {dweight, dinp}, list of units (kind, tile_m,
+    tile_n, split, kt0, kt1, splits of the tile, first workspace slot)) of the
     plan for a device with num_cus compute units.  Host only."""
     sp = (_i * 2)()
     n = _lib.mmb_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, None, 0)
     if n < 0:
         raise MmbError(n)
-    buf = (_i * (4 * n))()
+    buf = (_i * (8 * n))()
     _lib.mmb_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, buf, n)
-    return (sp[0], sp[1]), [tuple(buf[4 * k:4 * k + 4]) for k in range(n)]
+    return (sp[0], sp[1]), [tuple(buf[8 * k:8 * k + 8]) for k in range(n)]
 
 
 def mmb_tile_shape(dtype):

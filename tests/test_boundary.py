@@ -137,18 +137,33 @@ def test_plan_covers_every_tile_and_split_once(mmb, shape, cus):
     (sw, si), units = mmb.mmb_plan_units(B, T, C, OC, dt, bias, cus)
     BM, BN, BK = mmb.mmb_tile_shape(dt)
     cd = lambda a, b: -(-a // b)
-    expect = set()
-    for s in range(sw):
-        for m in range(cd(OC, BM)):
-            for n in range(cd(C, BN)):
-                expect.add((0, m, n, s))
-    for s in range(si):
-        for m in range(cd(B * T, BM)):
-            for n in range(cd(C, BN)):
-                expect.add((1, m, n, s))
-    assert len(units) == len(expect)
-    assert set(units) == expect
-    assert 1 <= sw <= cd(B * T, BK) and 1 <= si <= cd(OC, BK)
+    kiters = {0: cd(B * T, BK), 1: cd(OC, BK)}
+    tiles = {0: (cd(OC, BM), cd(C, BN)), 1: (cd(B * T, BM), cd(C, BN))}
+    by_tile = {}
+    for u in units:
+        kind, m, n, s, kt0, kt1, S, slot = u
+        assert 0 <= m < tiles[kind][0] and 0 <= n < tiles[kind][1]
+        by_tile.setdefault((kind, m, n), []).append(u)
+    assert len(by_tile) == sum(a * b for a, b in tiles.values())
+    used = []
+    for (kind, m, n), us in by_tile.items():
+        S = us[0][6]
+        assert all(u[6] == S for u in us) and all(u[7] == us[0][7] for u in us)
+        assert sorted(u[3] for u in us) == list(range(S))
+        # the K ranges of the tile's units partition [0, kiters) in split order
+        rng = sorted((u[3], u[4], u[5]) for u in us)
+        assert rng[0][1] == 0 and rng[-1][2] == kiters[kind]
+        assert all(a[2] == b[1] for a, b in zip(rng, rng[1:]))
+        assert all(lo < hi for _, lo, hi in rng)
+        if S > 1:
+            used.append((us[0][7], S))
+    # split tiles own disjoint runs of workspace slots
+    used.sort()
+    assert all(a + s <= b for (a, s), (b, _) in zip(used, used[1:]))
+    assert used == [] or used[0][0] == 0
+    maxs = {k: max((u[6] for u in units if u[0] == k), default=1) for k in (0, 1)}
+    assert (sw, si) == (maxs[0], maxs[1])
+    assert 1 <= sw <= kiters[0] and 1 <= si <= kiters[1]
 
 
 def test_tile_shape(mmb):
@@ -164,3 +179,4 @@ def test_plan_split_override(mmb, monkeypatch):
     monkeypatch.setenv("MMB_SPLITS_DINP", "2")
     (sw, si), units = mmb.mmb_plan_units(2, 150, 264, 400, 1, True, 256)
     assert (sw, si) == (3, 2)
+    assert all(u[6] == (3 if u[0] == 0 else 2) for u in units)
