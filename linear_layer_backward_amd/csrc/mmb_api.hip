@@ -209,10 +209,8 @@ std::vector<Unit> make_units(const GemmPlan g[2], const Layout& L, const DeviceI
 // workgroup i goes to XCD i % xcds, and each XCD starts its workgroups in
 // order on whichever of its workgroup slots frees first.  The last unit to
 // finish of a split tile also reads every partial back and writes the tile.
-// Returns the makespan (us) plus the time the whole GPU needs to move the
-// workspace traffic; the finish time of every unit in `fin` if not NULL.
-double simulate(const std::vector<Unit>& units, const CostModel& cm, const DeviceInfo& dev,
-                std::vector<double>* fin) {
+// Returns the makespan (us).
+double simulate(const std::vector<Unit>& units, const CostModel& cm, const DeviceInfo& dev) {
     const int per = std::max(1, dev.cus / dev.xcds) * std::max(1, dev.slots);
     std::vector<double> d(units.size()), f(units.size());
     for (size_t i = 0; i < units.size(); ++i) {
@@ -249,21 +247,19 @@ double simulate(const std::vector<Unit>& units, const CostModel& cm, const Devic
         const Unit& u = units[kv.second];
         d[kv.second] += u.b.z * cm.fix_per_partial + cm.epilogue;
     }
-    const double span = run();
-    if (fin) *fin = f;
-    return span;
+    return run();
 }
 
+// Makespan of a layout plus the time the whole GPU needs for its workspace
+// traffic (each partial tile written once and read once).
 double plan_cost(const GemmPlan g[2], const Layout& L, const DeviceInfo& dev, const CostModel& cm,
-                 double tile_bytes, std::vector<Unit>* units_out, std::vector<double>* fin) {
+                 double tile_bytes) {
     std::vector<Unit> u = make_units(g, L, dev);
     double partials = 0;
     for (int k = 0; k < 2; ++k)
         for (int s : L.splits[k])
             if (s > 1) partials += s;
-    const double t = simulate(u, cm, dev, fin) + 2.0 * partials * tile_bytes / cm.partial_bytes_per_us;
-    if (units_out) *units_out = std::move(u);
-    return t;
+    return simulate(u, cm, dev) + 2.0 * partials * tile_bytes / cm.partial_bytes_per_us;
 }
 
 Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& dev,
@@ -282,7 +278,7 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
 
     // MMB_PLAN_TRACE=1 prints the modelled cost of every candidate to stderr
     const bool trace = std::getenv("MMB_PLAN_TRACE") != nullptr;
-    // 1. one split count per GEMM
+    // one split count per GEMM (the unit encoding allows a count per tile)
     Layout best_L;
     double best = 1e300;
     for (int sw = 1; sw <= max_s[0]; ++sw) {
@@ -292,7 +288,7 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
             Layout L;
             L.splits[UNIT_DWEIGHT].assign(ntiles[0], sw);
             L.splits[UNIT_DINP].assign(ntiles[1], si);
-            const double t = plan_cost(g, L, dev, cm, tile_bytes, nullptr, nullptr);
+            const double t = plan_cost(g, L, dev, cm, tile_bytes);
             if (trace) std::fprintf(stderr, "mmb plan: dweight splits %d dinp splits %d cost %.2f us\n", sw, si, t);
             if (t < best - 1e-9) {
                 best = t;
@@ -300,44 +296,6 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
             }
         }
     }
-    // 2. unless forced: cut the tiles whose units finish last into more
-    // units while the modelled makespan keeps falling
-    if (force_sw <= 0 && force_si <= 0) {
-        std::vector<Unit> u;
-        std::vector<double> fin;
-        for (int round = 0; round < 64; ++round) {
-            plan_cost(g, best_L, dev, cm, tile_bytes, &u, &fin);
-            std::vector<size_t> order(u.size());
-            for (size_t i = 0; i < u.size(); ++i) order[i] = i;
-            std::sort(order.begin(), order.end(), [&](size_t x, size_t y) { return fin[x] > fin[y]; });
-            bool improved = false;
-            std::vector<std::pair<int, int>> tried;
-            for (size_t c = 0; c < order.size() && c < 8 && !improved; ++c) {
-                const Unit& x = u[order[c]];
-                const int k = x.a.x, t = x.a.y * g[k].tiles_n + x.a.z;
-                if (std::find(tried.begin(), tried.end(), std::make_pair(k, t)) != tried.end()) continue;
-                tried.push_back({k, t});
-                const int S = best_L.splits[k][t];
-                const int S2 = std::min(max_s[k], S + std::max(1, S / 2));
-                if (S2 <= S) continue;
-                Layout L = best_L;
-                // every tile of this GEMM with the same split count and a
-                // unit among the last to finish is cut the same way
-                L.splits[k][t] = S2;
-                const double tc = plan_cost(g, L, dev, cm, tile_bytes, nullptr, nullptr);
-                if (trace)
-                    std::fprintf(stderr, "mmb plan: %s tile %d splits %d -> %d cost %.2f us\n",
-                                 k == UNIT_DINP ? "dinp" : "dweight", t, S, S2, tc);
-                if (tc < best * 0.999) {
-                    best = tc;
-                    best_L = L;
-                    improved = true;
-                }
-            }
-            if (!improved) break;
-        }
-    }
-
     Plan p;
     std::memset(&p.proto, 0, sizeof(p.proto));
     p.units = make_units(g, best_L, dev);
