@@ -51,26 +51,33 @@ __device__ __forceinline__ f32x4 load16_agent(__amdgpu_buffer_rsrc_t r, uint32_t
 
 // ---- output tile --------------------------------------------------------------
 // Block (mb, nb) register r of lane l holds D[m0 + mb*32 + (l & 31)]
-// [n0 + nb*32 + 8*(r/4) + 4*(l/32) + r%4].  D = old + acc, rounded once.  All
-// old values are loaded first (one round trip), then the sums are stored;
-// rows >= M and columns >= N are masked through out-of-range offsets.
-template <typename T> struct OutVec;
-template <> struct OutVec<float> { typedef u32x4 type; };
-template <> struct OutVec<bf16_t> { typedef u32x2 type; };
+// [n0 + nb*32 + 8*(r/4) + 4*(l/32) + r%4] (m0, n0: the wave's block origin);
+// D = old + acc, rounded once.
+//
+// The tile is staged through LDS, so that global memory sees whole rows:
+// the old tile (BM x BN elements of T) is loaded with 16-byte vectors, one
+// row of BN elements per BN * sizeof(T) / 16 lanes, into LDS (rows padded
+// by 16 bytes so that the 32 rows of one MFMA output block fall on distinct
+// banks); every lane adds its accumulators to the old values of its fragment
+// positions (wave block at rows wm0.., columns wn0..) and rounds once in
+// place; the tile then goes back in the same row-contiguous pattern.  Stored
+// straight from the MFMA layout, one wave instruction touches 32 rows and 16
+// or 32 bytes of each.  Rows >= M and 16-byte groups >= N are masked through
+// out-of-range offsets (N is a multiple of the 16-byte group on this path).
+// `smem` holds at least out_lds_bytes<T, BM, BN>() bytes; the call begins
+// with a barrier, after which the caller's earlier LDS contents are dead.
+template <typename T, int BM, int BN>
+constexpr int out_pitch() { return BN * (int)sizeof(T) + 16; }
+template <typename T, int BM, int BN>
+constexpr int out_lds_bytes() { return BM * out_pitch<T, BM, BN>(); }
 
-__device__ __forceinline__ u32x4 out_load(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+__device__ __forceinline__ void add_round_store(char* pos, const f32x4& v, float) {
+    f32x4 o = *(const f32x4*)pos;
+    o += v;
+    *(f32x4*)pos = o;
 }
-__device__ __forceinline__ u32x2 out_load(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16_t) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-}
-__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 old,
-                                          f32x4 v) {
-    const f32x4 o = __builtin_bit_cast(f32x4, old) + v;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), r, off, 0, 0);
-}
-__device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 old,
-                                          f32x4 v) {
+__device__ __forceinline__ void add_round_store(char* pos, const f32x4& v, bf16_t) {
+    const u32x2 old = *(const u32x2*)pos;
     f32x4 o = v;
     o[0] += __uint_as_float(old[0] << 16);
     o[1] += __uint_as_float(old[0] & 0xffff0000u);
@@ -79,42 +86,53 @@ __device__ __forceinline__ void out_store(__amdgpu_buffer_rsrc_t r, uint32_t off
     u32x2 w;
     w[0] = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
     w[1] = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    *(u32x2*)pos = w;
 }
 
-template <typename T, int MB, int NB>
-__device__ __forceinline__ void write_tile(T* D, long long ldd, int M, int N, int m0, int n0,
-                                           const f32x16 (&acc)[MB][NB], int lane) {
-    const int lr = lane & 31, half = lane >> 5;
+template <typename T, int MB, int NB, int NT, int BM, int BN>
+__device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N, int m0, int n0,
+                                               const f32x16 (&acc)[MB][NB], char* smem, int tid,
+                                               int lane, int wm0, int wn0) {
+    constexpr int PITCH = out_pitch<T, BM, BN>();
+    constexpr int VEC = 16 / (int)sizeof(T);          // elements per 16-byte group
+    constexpr int CHUNKS = BN / VEC;                   // 16-byte groups per row
+    static_assert(NT % CHUNKS == 0 && BM % (NT / CHUNKS) == 0, "whole rows per pass");
+    constexpr int ROWS_PER_PASS = NT / CHUNKS;
+    constexpr int PASSES = BM / ROWS_PER_PASS;
     const long long base = (long long)m0 * ldd + n0;
     const auto r = make_rsrc(D + base, ((long long)M * ldd - base) * (long long)sizeof(T));
-    auto offset = [&](int mb, int nb, int q) {
-        const int m = mb * 32 + lr, n = nb * 32 + 8 * q + 4 * half;
-        return (uint32_t)((m * ldd + n) * (long long)sizeof(T)) | oob_if_ge(m0 + m, M) |
-               oob_if_ge(n0 + n, N);
+    const int ch = tid % CHUNKS, row0 = tid / CHUNKS;
+    const uint32_t col_mask = oob_if_ge(n0 + VEC * ch, N);
+    auto goff = [&](int row) {
+        return (uint32_t)((row * ldd + VEC * ch) * (long long)sizeof(T)) | col_mask |
+               oob_if_ge(m0 + row, M);
     };
-    // one row of blocks per batch of loads bounds the registers in flight
-    constexpr int CH = 1;
+    __syncthreads();
+    u32x4 v[PASSES];
 #pragma unroll
-    for (int mb0 = 0; mb0 < MB; mb0 += CH) {
-        typename OutVec<T>::type old[CH][NB][4];
+    for (int i = 0; i < PASSES; ++i) v[i] = buffer_load16(r, goff(row0 + ROWS_PER_PASS * i), 0);
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
+    for (int i = 0; i < PASSES; ++i)
+        *(u32x4*)(smem + (row0 + ROWS_PER_PASS * i) * PITCH + 16 * ch) = v[i];
+    __syncthreads();
+    const int lr = lane & 31, half = lane >> 5;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) old[i][nb][q] = out_load(r, offset(mb0 + i, nb, q), T{});
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
+            for (int q = 0; q < 4; ++q) {
+                const int row = wm0 + mb * 32 + lr, col = wn0 + nb * 32 + 8 * q + 4 * half;
+                const f32x4 a = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                 acc[mb][nb][4 * q + 3]};
+                add_round_store(smem + row * PITCH + (int)sizeof(T) * col, a, T{});
+            }
+    __syncthreads();
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int mb = mb0 + i;
-                    const f32x4 v = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1],
-                                     acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]};
-                    out_store(r, offset(mb, nb, q), old[i][nb][q], v);
-                }
+    for (int i = 0; i < PASSES; ++i) {
+        const int row = row0 + ROWS_PER_PASS * i;
+        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * PITCH + 16 * ch), r,
+                                              goff(row), 0, 0);
     }
 }
 

@@ -53,7 +53,9 @@ struct K {
     static constexpr int WM = Cfg<T>::WM, WN = Cfg<T>::WN;
     static constexpr int MB = WM / 32, NB = WN / 32;        // 32x32 blocks per wave
     static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    // the ring, or the whole output tile in the epilogue
+    static constexpr int OUT_BYTES = out_lds_bytes<T, BM, BN>();
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES > OUT_BYTES ? 2 * STAGE_BYTES : OUT_BYTES;
     static constexpr int A_KC_PER = BM * 8 / kThreads;      // K-contiguous A: vectors/thread
     static_assert(BK * (int)sizeof(T) == kRowBytes, "row = 8 vectors of 16 bytes");
     static_assert(BM == 2 * WM && BN == 2 * WN, "2 x 2 waves");
@@ -268,7 +270,8 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
-    write_tile<T, Kt::MB, Kt::NB>(D, ldd, M, N, m0 + wm0, n0 + wn0, acc, lane);
+    write_tile_lds<T, Kt::MB, Kt::NB, kThreads, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
+                                                       wm0, wn0);
     if (bias_owner) {
         T* db = (T*)p.dbias;
 #pragma unroll

@@ -56,10 +56,9 @@ constexpr int KC_PITCH = 128;    // K-contiguous LDS row: BK bf16 (one 128-byte 
 constexpr int MN_PITCH = 512;    // M/N-contiguous LDS row: 256 bf16
 constexpr int REGION = 32768;    // one operand of one stage
 constexpr int STAGE = 2 * REGION;
-// epilogue: the whole output tile as bf16 in LDS, rows padded by 16 bytes
-// so that the 32 rows of one MFMA output block fall on distinct banks
-constexpr int OUT_PITCH = BN * 2 + 16;
-constexpr int LDS_BYTES = 2 * STAGE > BM * OUT_PITCH ? 2 * STAGE : BM * OUT_PITCH;
+// the ring, or the whole output tile in the epilogue
+constexpr int OUT_BYTES = out_lds_bytes<bf16_t, BM, BN>();
+constexpr int LDS_BYTES = 2 * STAGE > OUT_BYTES ? 2 * STAGE : OUT_BYTES;
 constexpr int LOADS = REGION / (NW * 1024); // 1 KB loads per wave per operand per stage
 static_assert(BM * KC_PITCH == REGION && BK * MN_PITCH == REGION, "regions");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -104,67 +103,6 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* region, int xb, int s, int
     const bf16x4 lo = tr_read(region, byte);
     const bf16x4 hi = tr_read(region, byte + 4 * MN_PITCH);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Output tile D[m0 .. m0+255][n0 .. n0+255] = round(old + acc), staged in
-// LDS so that global memory sees whole rows: the old tile is loaded with
-// 16-byte vectors (one 512-byte row per 32 lanes) into LDS, every lane adds
-// its accumulators to the old values of its fragment positions and rounds
-// once to bf16 in place, and the tile goes back to global memory in the
-// same row-contiguous pattern.  (Stored straight from the MFMA layout, one
-// wave instruction touches 32 rows and 16 bytes of each.)  Rows >= M and
-// 16-byte column groups >= N are masked through out-of-range offsets (N is
-// a multiple of 8 on this path).
-__device__ __forceinline__ void write_tile_lds(bf16_t* D, long long ldd, int M, int N, int m0,
-                                               int n0, const f32x16 (&acc)[MB][NB], char* smem,
-                                               int tid, int lane, int wm0, int wn0) {
-    constexpr int CHUNKS = BN * 2 / 16;           // 16-byte groups per row
-    constexpr int ROWS_PER_PASS = NT / CHUNKS;
-    constexpr int PASSES = BM / ROWS_PER_PASS;
-    const long long base = (long long)m0 * ldd + n0;
-    const auto r = make_rsrc(D + base, ((long long)M * ldd - base) * (long long)sizeof(bf16_t));
-    const int ch = tid % CHUNKS, row0 = tid / CHUNKS;
-    const uint32_t col_mask = oob_if_ge(n0 + 8 * ch, N);
-    auto goff = [&](int row) {
-        return (uint32_t)((row * ldd + 8 * ch) * 2) | col_mask | oob_if_ge(m0 + row, M);
-    };
-    __syncthreads();   // LDS is free: every wave is done with the ring and the reductions
-    u32x4 v[PASSES];
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) v[i] = buffer_load16(r, goff(row0 + ROWS_PER_PASS * i), 0);
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i)
-        *(u32x4*)(smem + (row0 + ROWS_PER_PASS * i) * OUT_PITCH + 16 * ch) = v[i];
-    __syncthreads();
-    const int lr = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = wm0 + mb * 32 + lr, col = wn0 + nb * 32 + 8 * q + 4 * half;
-                u32x2* pos = (u32x2*)(smem + row * OUT_PITCH + 2 * col);
-                const u32x2 old = *pos;
-                float o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = acc[mb][nb][4 * q + e];
-                o[0] += __uint_as_float(old[0] << 16);
-                o[1] += __uint_as_float(old[0] & 0xffff0000u);
-                o[2] += __uint_as_float(old[1] << 16);
-                o[3] += __uint_as_float(old[1] & 0xffff0000u);
-                u32x2 w;
-                w[0] = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-                w[1] = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-                *pos = w;
-            }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-        const int row = row0 + ROWS_PER_PASS * i;
-        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * OUT_PITCH + 16 * ch), r,
-                                              goff(row), 0, 0);
-    }
 }
 
 // AK: A (M side) is K-contiguous in memory (dinp: dout rows); otherwise it
@@ -371,7 +309,7 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
-    write_tile_lds(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
+    write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
     if (do_bias && tid < BM && m0 + tid < M) ((bf16_t*)p.dbias)[m0 + tid] = from_f32<bf16_t>(bias);
 }
 
