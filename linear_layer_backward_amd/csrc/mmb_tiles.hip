@@ -100,27 +100,17 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, int wm
 #pragma unroll
         for (int mb = 0; mb < Kt::MB; ++mb)
             fb[mb] = *(const u32x4*)(sa + swz(wm0 + mb * 32 + lr, chunk));
-        if constexpr (sizeof(T) == 2) {
+        // lane half h holds k = 8s + 4h + q in element q: MFMA q reduces over
+        // the pair {8s + q, 8s + 4 + q}; all four cover the 8 k.
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int mb = 0; mb < Kt::MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < Kt::NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, fa[nb]), __builtin_bit_cast(bf16x8, fb[mb]),
-                        acc[mb][nb], 0, 0, 0);
-        } else {
-            // lane half h holds k = 8s + 4h + q in element q: MFMA q reduces
-            // over the pair {8s + q, 8s + 4 + q}; all four cover the 8 k.
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int mb = 0; mb < Kt::MB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < Kt::NB; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            __uint_as_float(fa[nb][q]), __uint_as_float(fb[mb][q]),
-                            acc[mb][nb], 0, 0, 0);
-        }
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        __uint_as_float(fa[nb][q]), __uint_as_float(fb[mb][q]), acc[mb][nb], 0, 0,
+                        0);
     }
 }
 
