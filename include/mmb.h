@@ -102,8 +102,9 @@ int mmb_path(const void* dinp, const void* dweight, const void* dbias,
  * splits of this tile, first workspace slot of this tile}: the unit covers
  * K iterations [kt0, kt1) of its output tile.  Returns the number of units,
  * or a negative mmb_status.  Honours the MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP
- * environment overrides (one split count for every tile of that GEMM) like
- * mmb_backward.  Makes no HIP call. */
+ * environment overrides like mmb_backward: one count for every tile of that
+ * GEMM, or a comma-separated list whose entry t mod length applies to tile t
+ * (row-major tile index).  Makes no HIP call. */
 int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
                    int* splits, int* units, int max_units);
 

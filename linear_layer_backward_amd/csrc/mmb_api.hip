@@ -14,6 +14,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <string>
 #include <mutex>
 #include <queue>
 #include <tuple>
@@ -97,7 +98,7 @@ struct Plan {
     long long ws_floats = 0;
     long long ws_bias_floats = 0;
     int n_counters = 0;
-    int forced_sw = 0, forced_si = 0;
+    std::string forced;           // the split overrides the plan was made with
 };
 
 // Cost of the pieces of a unit, in microseconds, for the tile kernels as
@@ -262,8 +263,26 @@ double plan_cost(const GemmPlan g[2], const Layout& L, const DeviceInfo& dev, co
     return simulate(u, cm, dev) + 2.0 * partials * tile_bytes / cm.partial_bytes_per_us;
 }
 
+// Split overrides: empty = the planner chooses; one value = that count for
+// every tile of the GEMM; several values = tile t gets value t mod count
+// (clamped to the tile's K iterations; for tests of uneven plans).
+std::vector<int> parse_splits(const char* v) {
+    std::vector<int> out;
+    if (!v) return out;
+    const char* p = v;
+    while (*p) {
+        char* end = nullptr;
+        const long x = std::strtol(p, &end, 10);
+        if (end == p) break;   // not a number: stop
+        if (x > 0) out.push_back((int)std::min(x, 1L << 20));
+        if (*end != ',') break;
+        p = end + 1;
+    }
+    return out;
+}
+
 Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& dev,
-                int force_sw, int force_si) {
+                const std::vector<int>& force_w, const std::vector<int>& force_i) {
     const TileShape ts = tile_shape(dtype);
     GemmPlan g[2];
     // dweight[OC,C] += dout^T[OC,BT] . inp[BT,C]
@@ -281,21 +300,34 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     // one split count per GEMM (the unit encoding allows a count per tile)
     Layout best_L;
     double best = 1e300;
+    const int force_sw = force_w.size() == 1 ? force_w[0] : 0;
+    const int force_si = force_i.size() == 1 ? force_i[0] : 0;
     for (int sw = 1; sw <= max_s[0]; ++sw) {
         for (int si = 1; si <= max_s[1]; ++si) {
             if (force_sw > 0 && sw != std::min(force_sw, max_s[0])) continue;
             if (force_si > 0 && si != std::min(force_si, max_s[1])) continue;
+            if (force_w.size() > 1 && sw > 1) continue;
+            if (force_i.size() > 1 && si > 1) continue;
             Layout L;
             L.splits[UNIT_DWEIGHT].assign(ntiles[0], sw);
             L.splits[UNIT_DINP].assign(ntiles[1], si);
             const double t = plan_cost(g, L, dev, cm, tile_bytes);
-            if (trace) std::fprintf(stderr, "mmb plan: dweight splits %d dinp splits %d cost %.2f us\n", sw, si, t);
+            if (trace)
+                std::fprintf(stderr, "mmb plan: dweight splits %d dinp splits %d cost %.2f us\n", sw,
+                             si, t);
             if (t < best - 1e-9) {
                 best = t;
                 best_L = L;
             }
         }
     }
+    const std::vector<int>* lists[2] = {&force_w, &force_i};
+    for (int k = 0; k < 2; ++k) {
+        if (lists[k]->size() <= 1) continue;
+        for (int t = 0; t < ntiles[k]; ++t)
+            best_L.splits[k][t] = std::min((*lists[k])[t % lists[k]->size()], g[k].kiters);
+    }
+
     Plan p;
     std::memset(&p.proto, 0, sizeof(p.proto));
     p.units = make_units(g, best_L, dev);
@@ -332,11 +364,6 @@ std::map<int, DeviceInfo> g_dev;
 std::map<std::tuple<int, int, int, int, int, bool>, Plan> g_plans;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int env_int(const char* name) {
-    const char* v = std::getenv(name);
-    return v ? std::atoi(v) : 0;
-}
-
 int device_info(int dev, DeviceInfo* out) {
     auto it = g_dev.find(dev);
     if (it != g_dev.end()) {
@@ -358,13 +385,14 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
     // MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP force the split counts (tuning
-    // sweeps); 0 or unset lets the planner choose.
-    const int fsw = env_int("MMB_SPLITS_DWEIGHT");
-    const int fsi = env_int("MMB_SPLITS_DINP");
+    // sweeps, tests); unset lets the planner choose.
+    const char* ew = std::getenv("MMB_SPLITS_DWEIGHT");
+    const char* ei = std::getenv("MMB_SPLITS_DINP");
+    const std::string forced = std::string(ew ? ew : "") + "/" + (ei ? ei : "");
     const auto key = std::make_tuple(dev, dtype, BT, C, OC, bias);
     auto it = g_plans.find(key);
     if (it != g_plans.end()) {
-        if (it->second.forced_sw == fsw && it->second.forced_si == fsi) {
+        if (it->second.forced == forced) {
             *out = &it->second;
             return MMB_OK;
         }
@@ -377,9 +405,8 @@ int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
     int st = device_info(dev, &di);
     if (st != MMB_OK) return st;
     di.slots = tiles_resident(dtype);
-    Plan p = build_plan(dtype, BT, C, OC, bias, di, fsw, fsi);
-    p.forced_sw = fsw;
-    p.forced_si = fsi;
+    Plan p = build_plan(dtype, BT, C, OC, bias, di, parse_splits(ew), parse_splits(ei));
+    p.forced = forced;
     const size_t ub = p.units.size() * sizeof(Unit);
     if (hipMalloc(&p.d_units, ub) != hipSuccess) return MMB_ERR_NOMEM;
     if (hipMemcpy(p.d_units, p.units.data(), ub, hipMemcpyHostToDevice) != hipSuccess) {
@@ -394,20 +421,20 @@ int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
 }
 
 // Workspace: two allocations per (device, stream).  `counters` holds one
-// arrival counter per split tile and is only ever used for counters: it is
+// arrival counter per output tile and is only ever used for counters: it is
 // zeroed when allocated and every counter is reset by the last arriver of
 // its tile, so it is all zero at rest whatever plan ran before.  `partials`
 // holds [bias partials fp32][tile partials fp32] (each part 256-byte
 // aligned) and needs no initial value.
 int grow(void** buf, size_t* cap, size_t need, bool zero, hipStream_t s) {
     if (need <= *cap) return MMB_OK;
+    const size_t want = std::max(need, *cap * 2);
     if (*buf) {
         if (hipStreamSynchronize(s) != hipSuccess) return MMB_ERR_HIP;
         (void)hipFree(*buf);
         *buf = nullptr;
         *cap = 0;
     }
-    const size_t want = std::max(need, *cap * 2);
     if (hipMalloc(buf, want) != hipSuccess) {
         *buf = nullptr;
         return MMB_ERR_NOMEM;
@@ -517,8 +544,8 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
     di.xcds = num_cus >= 128 ? 8 : 1;
     di.slots = mmb::tiles_resident(dtype);
     const mmb::Plan p = mmb::build_plan(dtype, B * T, C, OC, has_bias != 0, di,
-                                        mmb::env_int("MMB_SPLITS_DWEIGHT"),
-                                        mmb::env_int("MMB_SPLITS_DINP"));
+                                        mmb::parse_splits(std::getenv("MMB_SPLITS_DWEIGHT")),
+                                        mmb::parse_splits(std::getenv("MMB_SPLITS_DINP")));
     splits[0] = p.max_splits[mmb::UNIT_DWEIGHT];
     splits[1] = p.max_splits[mmb::UNIT_DINP];
     if (units) {

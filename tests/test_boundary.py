@@ -174,6 +174,24 @@ def test_tile_shape(mmb):
         mmb.mmb_tile_shape(7)
 
 
+@pytest.mark.parametrize("lists", [("2,3,5", "1,2"), ("16,1", "8")])
+def test_plan_per_tile_split_lists(mmb, monkeypatch, lists):
+    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", lists[0])
+    monkeypatch.setenv("MMB_SPLITS_DINP", lists[1])
+    test_plan_covers_every_tile_and_split_once(mmb, (1, 700, 520, 600, 1, True), 256)
+    B, T, C, OC = 1, 700, 520, 600
+    BM, BN, BK = mmb.mmb_tile_shape(1)
+    cd = lambda a, b: -(-a // b)
+    want = {0: [int(x) for x in lists[0].split(",")], 1: [int(x) for x in lists[1].split(",")]}
+    kit = {0: cd(B * T, BK), 1: cd(OC, BK)}
+    tn = cd(C, BN)
+    _, units = mmb.mmb_plan_units(B, T, C, OC, 1, True, 256)
+    for u in units:
+        kind, m, n = u[0], u[1], u[2]
+        t = m * tn + n
+        assert u[6] == min(want[kind][t % len(want[kind])], kit[kind])
+
+
 def test_plan_split_override(mmb, monkeypatch):
     monkeypatch.setenv("MMB_SPLITS_DWEIGHT", "3")
     monkeypatch.setenv("MMB_SPLITS_DINP", "2")

@@ -199,6 +199,21 @@ def test_forced_splits(dev, monkeypatch, shape, splits):
     check_full(case, run(case, dev))
 
 
+@pytest.mark.parametrize("splits", [("2,3,5", "1,2"), ("7,1,4", "3,1,2,1,5")])
+@pytest.mark.parametrize("shape", [(3, 100, 200, 328, "f32"), (2, 150, 264, 400, "bf16"),
+                                   (1, 700, 520, 600, "bf16")], ids=["f32", "bf16", "bf16-big"])
+def test_uneven_tile_splits(dev, monkeypatch, shape, splits):
+    """Tiles of one GEMM cut into different numbers of K ranges (per-tile
+    split counts, workspace slots and arrival counts), exact and random."""
+    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", splits[0])
+    monkeypatch.setenv("MMB_SPLITS_DINP", splits[1])
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=5)
+    check_exact(case, run(case, dev))
+    case = wl.random_case(B, T, C, OC, dt, seed=6)
+    check_full(case, run(case, dev))
+
+
 def test_cfg1_tiny(dev):
     case = wl.config_cases(1)[0]
     check_full(case, run(case, dev))
