@@ -1,8 +1,9 @@
 // mmb_numeric.h -- storage types and conversions of the HIP path.
 //
 // bfloat16 is the upper half of an IEEE binary32: widening is a 16-bit shift
-// (exact); narrowing rounds to nearest, ties to even, on the bit pattern, and
-// keeps NaN a quiet NaN.
+// (exact); narrowing is gfx950's v_cvt_pk_bf16_f32, which rounds to nearest,
+// ties to even, under the default round mode of a HIP kernel, and keeps NaN
+// a NaN (branch-free: two values per instruction).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,9 +20,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

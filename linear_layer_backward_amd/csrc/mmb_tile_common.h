@@ -84,8 +84,8 @@ __device__ __forceinline__ void add_round_store(char* pos, const f32x4& v, bf16_
     o[2] += __uint_as_float(old[1] << 16);
     o[3] += __uint_as_float(old[1] & 0xffff0000u);
     u32x2 w;
-    w[0] = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-    w[1] = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+    w[0] = f32x2_to_bf16x2_bits(o[0], o[1]);
+    w[1] = f32x2_to_bf16x2_bits(o[2], o[3]);
     *(u32x2*)pos = w;
 }
 
@@ -167,32 +167,39 @@ __device__ __forceinline__ bool arrive_last(int* counter, int splits, int* s_fla
 
 // acc <- p_0 + p_1 + ... + p_{S-1}, every partial (this workgroup's own
 // included) read back with agent-coherent loads and added in split order, so
-// the bits do not depend on which split arrives last.  Up to 8 groups of 4
-// floats are fetched per batch of loads.
+// the bits do not depend on which split arrives last.  The whole of p_0 is
+// fetched at once (into the accumulators, whose values were published), then
+// each further partial in batches of up to 16 groups of 4 floats, so that one
+// partial costs about one round trip to memory.
 template <int MB, int NB, int NT>
 __device__ __forceinline__ void sum_partials(const float* w0, int splits, int tile_floats,
                                              f32x16 (&acc)[MB][NB], int tid) {
     constexpr int NG = MB * NB * 4;          // 4-float groups per thread
-    constexpr int BATCH = NG >= 32 ? 8 : NG / 2;
+    constexpr int BATCH = NG > 16 ? 16 : NG;
     static_assert(NG % BATCH == 0, "whole batches");
+    f32x4 sum[NG];
+    {
+        const auto r = make_rsrc(w0, (long long)tile_floats * 4);
 #pragma unroll
-    for (int b0 = 0; b0 < NG; b0 += BATCH) {
-        f32x4 sum[BATCH];
-        for (int sp = 0; sp < splits; ++sp) {
-            const auto r = make_rsrc(w0 + (long long)sp * tile_floats, (long long)tile_floats * 4);
+        for (int g = 0; g < NG; ++g) sum[g] = load16_agent(r, (uint32_t)((g * NT + tid) * 16));
+    }
+    for (int sp = 1; sp < splits; ++sp) {
+        const auto r = make_rsrc(w0 + (long long)sp * tile_floats, (long long)tile_floats * 4);
+#pragma unroll
+        for (int b0 = 0; b0 < NG; b0 += BATCH) {
             f32x4 v[BATCH];
 #pragma unroll
             for (int g = 0; g < BATCH; ++g)
                 v[g] = load16_agent(r, (uint32_t)(((b0 + g) * NT + tid) * 16));
 #pragma unroll
-            for (int g = 0; g < BATCH; ++g) sum[g] = sp == 0 ? v[g] : sum[g] + v[g];
+            for (int g = 0; g < BATCH; ++g) sum[b0 + g] += v[g];
         }
+    }
 #pragma unroll
-        for (int g = 0; g < BATCH; ++g) {
-            const int q = (b0 + g) & 3, blk = (b0 + g) >> 2;
+    for (int g = 0; g < NG; ++g) {
+        const int q = g & 3, blk = g >> 2;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[blk / NB][blk % NB][4 * q + e] = sum[g][e];
-        }
+        for (int e = 0; e < 4; ++e) acc[blk / NB][blk % NB][4 * q + e] = sum[g][e];
     }
 }
 
