@@ -47,7 +47,8 @@ def source_digest() -> str:
 def measured_traffic(kernel: str, cfg: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_cfg{cfg}_counters.txt")
+    from linear_layer_backward_amd import workloads as wl
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{wl.CONFIG_SLUGS[cfg]}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -77,6 +78,7 @@ def summarize_counters(cfg: int, dirs, copy_mib: int) -> str:
     """Text summary of two FETCH_SIZE / WRITE_SIZE passes over the workload and
     the same two passes over a plain copy of copy_mib MiB: the copy kernel's
     readings fix the KiB-per-counter-unit scale of each counter."""
+    from linear_layer_backward_amd import workloads as wl
     fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
     dtype = "bf16" if cfg >= 4 else "f32"
     kernel = KERNEL_NAME[dtype]
@@ -89,7 +91,7 @@ def summarize_counters(cfg: int, dirs, copy_mib: int) -> str:
     fetch_b, write_b = kf * sf * 1024, kw * sw * 1024
     lines = [
         f"kernel: {kernel}",
-        f"workload: config {cfg}",
+        f"workload: {wl.CONFIG_NAMES[cfg]}",
         f"source_digest: {source_digest()}",
         f"copy calibration: {copy_mib} MiB each way; FETCH_SIZE {cf:.1f} ({ncf} dispatches), "
         f"WRITE_SIZE {cw:.1f} ({ncw}); scale fetch {sf:.4f}, write {sw:.4f}",

@@ -165,6 +165,15 @@ CONFIG_NAMES = {
     5: "GPT-2 124M LM head backward bf16 B=8 T=1024 C=768 OC=50304, no bias",
 }
 
+# short file-name forms of the workloads (profile summaries)
+CONFIG_SLUGS = {
+    1: "tiny_f32_B2_T16_C64_OC192",
+    2: "gpt2_qkv_f32_B8_T1024_C768_OC2304",
+    3: "gpt2_mlp_pair_f32_B8_T1024",
+    4: "gpt2_fc_bf16_B16_T1024_C768_OC3072",
+    5: "gpt2_lm_head_bf16_B8_T1024_C768_OC50304",
+}
+
 
 def _case(name, cfg, dtype, B, T, C, OC, inp_std, w_std, dout_std,
           prefill_std, with_bias, inp_gelu=False, seed_add=0):
@@ -191,22 +200,22 @@ def _case(name, cfg, dtype, B, T, C, OC, inp_std, w_std, dout_std,
 def config_cases(cfg: int) -> list:
     """The calls that make up one workload (two for the MLP pair)."""
     if cfg == 1:
-        return [_case("cfg1 tiny", 1, "f32", 2, 16, 64, 192, 1.0, 0.02, 1.0, 0.1, True)]
+        return [_case("tiny fp32 B2 T16 C64 OC192", 1, "f32", 2, 16, 64, 192, 1.0, 0.02, 1.0, 0.1, True)]
     if cfg == 2:
-        return [_case("cfg2 qkv", 2, "f32", 8, 1024, 768, 2304, 1.0, 0.02, 1e-3, 0.0, True)]
+        return [_case("qkv fp32 B8 T1024 C768 OC2304", 2, "f32", 8, 1024, 768, 2304, 1.0, 0.02, 1e-3, 0.0, True)]
     if cfg == 3:
-        return [_case("cfg3 fc", 3, "f32", 8, 1024, 768, 3072, 1.0, 0.02, 1e-3, 0.0, True),
-                _case("cfg3 fc_proj", 3, "f32", 8, 1024, 3072, 768, 1.0, 0.02, 1e-3, 0.0,
+        return [_case("fc fp32 B8 T1024 C768 OC3072", 3, "f32", 8, 1024, 768, 3072, 1.0, 0.02, 1e-3, 0.0, True),
+                _case("fc_proj fp32 B8 T1024 C3072 OC768", 3, "f32", 8, 1024, 3072, 768, 1.0, 0.02, 1e-3, 0.0,
                       True, inp_gelu=True, seed_add=100)]
     if cfg == 4:
-        return [_case("cfg4 fc bf16", 4, "bf16", 16, 1024, 768, 3072, 1.0, 0.02, 1e-3, 0.0, True)]
+        return [_case("fc bf16 B16 T1024 C768 OC3072", 4, "bf16", 16, 1024, 768, 3072, 1.0, 0.02, 1e-3, 0.0, True)]
     if cfg == 5:
         B, T, C, OC = 8, 1024, 768, GPT2_VOCAB_PADDED
         s = 5000
         inp = normal(s + INP, (B * T, C), 1.0, "bf16")
         weight = normal(s + WEIGHT, (OC, C), 0.02, "bf16")
         dout = lm_head_dout(s + LOGITS, s + TARGETS, B * T, GPT2_VOCAB, OC, "bf16")
-        return [Case("cfg5 lm_head bf16", "bf16", B, T, C, OC, inp, weight, dout,
+        return [Case("lm_head bf16 B8 T1024 C768 OC50304", "bf16", B, T, C, OC, inp, weight, dout,
                      np.zeros((B * T, C), np.float32), np.zeros((OC, C), np.float32),
                      None, meta={"config": 5, "seed_base": s, "vocab": GPT2_VOCAB})]
     raise ValueError(f"no config {cfg}")

@@ -214,7 +214,7 @@ def test_uneven_tile_splits(dev, monkeypatch, shape, splits):
     check_full(case, run(case, dev))
 
 
-def test_cfg1_tiny(dev):
+def test_tiny_workload(dev):
     case = wl.config_cases(1)[0]
     check_full(case, run(case, dev))
 
