@@ -155,8 +155,9 @@ struct Layout {
 // come first; among equal ones, dweight units are ordered (split, tile_m,
 // tile_n) so that units running together share the inp rows of one K range
 // and the dout columns of one tile_m, and dinp units (tile_m, split, tile_n)
-// so that they share dout rows.  Each XCD then receives a contiguous run of
-// the GEMM with the longer units followed by a contiguous run of the other,
+// so that they share dout rows.  Every run of equal split counts, of the GEMM
+// with the longer units first, is dealt out evenly in contiguous pieces, one
+// per XCD (the remainders rotate over the XCDs), and the XCD sequences are
 // interleaved so that workgroup i lands on XCD i % xcds.
 std::vector<Unit> make_units(const GemmPlan g[2], const Layout& L, const DeviceInfo& dev) {
     std::vector<Unit> per[2];
@@ -201,28 +202,35 @@ std::vector<Unit> make_units(const GemmPlan g[2], const Layout& L, const DeviceI
     const int first = longest(UNIT_DWEIGHT) >= longest(UNIT_DINP) ? UNIT_DWEIGHT : UNIT_DINP;
     const std::vector<Unit>& a = per[first];
     const std::vector<Unit>& b = per[1 - first];
-    const int X = dev.xcds;
+    const int X = std::max(1, dev.xcds);
     const size_t n = a.size() + b.size();
     std::vector<std::vector<Unit>> seq(X);
-    size_t pa = 0, pb = 0;
-    for (int x = 0; x < X; ++x) {
-        const size_t cnt = n / X + ((size_t)x < n % X ? 1 : 0);
-        size_t ca = a.size() / X + ((size_t)x < a.size() % X ? 1 : 0);
-        ca = std::min(ca, cnt);
-        size_t cb = std::min(cnt - ca, b.size() - pb);
-        ca = cnt - cb;
-        seq[x].insert(seq[x].end(), a.begin() + pa, a.begin() + pa + ca);
-        seq[x].insert(seq[x].end(), b.begin() + pb, b.begin() + pb + cb);
-        pa += ca;
-        pb += cb;
-    }
+    int rot = 0;   // XCD that receives the next remainder unit
+    auto deal = [&](const std::vector<Unit>& list) {
+        for (size_t i = 0; i < list.size();) {
+            size_t j = i;
+            while (j < list.size() && list[j].b.z == list[i].b.z) ++j;
+            const size_t len = j - i, base = len / X, rem = len % X;
+            size_t p = i;
+            for (int x = 0; x < X; ++x) {
+                const size_t c = base + ((size_t)((x - rot + X) % X) < rem ? 1 : 0);
+                seq[x].insert(seq[x].end(), list.begin() + p, list.begin() + p + c);
+                p += c;
+            }
+            rot = (int)((rot + rem) % X);
+            i = j;
+        }
+    };
+    deal(a);
+    deal(b);
     std::vector<Unit> out;
     out.reserve(n);
-    if (pa != a.size() || pb != b.size()) {
-        out = a;
-        out.insert(out.end(), b.begin(), b.end());
-        return out;
-    }
+    for (int x = 0; x < X; ++x)
+        if (seq[x].size() != n / X + ((size_t)x < n % X ? 1 : 0)) {   // cannot happen
+            out = a;
+            out.insert(out.end(), b.begin(), b.end());
+            return out;
+        }
     for (size_t i = 0; i < n; ++i) out.push_back(seq[i % X][i / X]);
     return out;
 }
