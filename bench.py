@@ -4,11 +4,11 @@ MI355X.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
 
 A step is one whole backward pass over the workload (one mmb_backward call;
-two for the MLP pair).  Prints one JSON line: TFLOP/s over the timed steps
-(4*B*T*C*OC flops plus B*T*OC adds for the bias), the dominant kernel's
-MFMA roofline fraction from HIP events recorded around every launch on the
-stream it runs on, and the CPU oracle timed on a bounded sample of the same
-workload on the host's cores.
+two for the MLP pair).  Prints one JSON line: TFLOP/s over the timed steps,
+which run back to back (4*B*T*C*OC flops plus B*T*OC adds for the bias), the
+dominant kernel's MFMA roofline fraction from HIP events recorded around each
+launch of a second run of as many steps on the stream it runs on, and the CPU
+oracle timed on a bounded sample of the same workload on the host's cores.
 """
 from __future__ import annotations
 
@@ -212,24 +212,32 @@ def main(argv=None):
         step()
     torch.cuda.synchronize(dev)
 
+    # The K timed steps run back to back with nothing between them: an event
+    # recorded between two launches holds the second one back by several
+    # microseconds.  The kernel's own duration is then taken over K more
+    # steps, each bracketed by events on the launch stream.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step()
-        ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     ms_per_step = total_ms / K
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     flops = sum(c.flops() for c in cases)
     dtype = cases[0].dtype
