@@ -89,31 +89,56 @@ __device__ __forceinline__ void add_round_store(char* pos, const f32x4& v, bf16_
     *(u32x2*)pos = w;
 }
 
-template <typename T, int MB, int NB, int NT, int BM, int BN>
+// Global 16-byte offsets of the epilogue's row-contiguous passes: thread tid
+// moves group tid % CHUNKS of row tid / CHUNKS + ROWS_PER_PASS * i in pass i.
+// Offsets are relative to out_rsrc(); rows >= M and groups >= N are masked.
+template <typename T, int NT, int BM, int BN>
+struct OutMap {
+    static constexpr int VEC = 16 / (int)sizeof(T);   // elements per 16-byte group
+    static constexpr int CHUNKS = BN / VEC;            // 16-byte groups per row
+    static_assert(NT % CHUNKS == 0 && BM % (NT / CHUNKS) == 0, "whole rows per pass");
+    static constexpr int ROWS_PER_PASS = NT / CHUNKS;
+    static constexpr int PASSES = BM / ROWS_PER_PASS;
+};
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(T* D, long long ldd, int M, int m0, int n0) {
+    const long long base = (long long)m0 * ldd + n0;
+    return make_rsrc(D + base, ((long long)M * ldd - base) * (long long)sizeof(T));
+}
+template <typename T, int NT, int BM, int BN>
+__device__ __forceinline__ uint32_t out_off(long long ldd, int M, int N, int m0, int n0, int tid, int i) {
+    typedef OutMap<T, NT, BM, BN> OM;
+    const int ch = tid % OM::CHUNKS, row = tid / OM::CHUNKS + OM::ROWS_PER_PASS * i;
+    return (uint32_t)((row * ldd + OM::VEC * ch) * (long long)sizeof(T)) |
+           oob_if_ge(n0 + OM::VEC * ch, N) | oob_if_ge(m0 + row, M);
+}
+
+// With PRE > 0, passes 0 .. PRE-1 of the old tile were already loaded by the
+// caller (pre[i], loaded from out_rsrc() at out_off(.., i)).
+template <typename T, int MB, int NB, int NT, int BM, int BN, int PRE = 0>
 __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N, int m0, int n0,
                                                const f32x16 (&acc)[MB][NB], char* smem, int tid,
-                                               int lane, int wm0, int wn0) {
+                                               int lane, int wm0, int wn0,
+                                               const u32x4* pre = nullptr) {
+    typedef OutMap<T, NT, BM, BN> OM;
     constexpr int PITCH = out_pitch<T, BM, BN>();
-    constexpr int VEC = 16 / (int)sizeof(T);          // elements per 16-byte group
-    constexpr int CHUNKS = BN / VEC;                   // 16-byte groups per row
-    static_assert(NT % CHUNKS == 0 && BM % (NT / CHUNKS) == 0, "whole rows per pass");
-    constexpr int ROWS_PER_PASS = NT / CHUNKS;
-    constexpr int PASSES = BM / ROWS_PER_PASS;
-    const long long base = (long long)m0 * ldd + n0;
-    const auto r = make_rsrc(D + base, ((long long)M * ldd - base) * (long long)sizeof(T));
-    const int ch = tid % CHUNKS, row0 = tid / CHUNKS;
-    const uint32_t col_mask = oob_if_ge(n0 + VEC * ch, N);
-    auto goff = [&](int row) {
-        return (uint32_t)((row * ldd + VEC * ch) * (long long)sizeof(T)) | col_mask |
-               oob_if_ge(m0 + row, M);
-    };
+    constexpr int PASSES = OM::PASSES;
+    static_assert(PRE >= 0 && PRE <= PASSES, "preloaded passes");
+    const auto r = out_rsrc(D, ldd, M, m0, n0);
+    const int ch = tid % OM::CHUNKS, row0 = tid / OM::CHUNKS;
     __syncthreads();
+    // the preloaded passes go to LDS first, so that their registers are free
+    // for the loads of the others
+#pragma unroll
+    for (int i = 0; i < PRE; ++i)
+        *(u32x4*)(smem + (row0 + OM::ROWS_PER_PASS * i) * PITCH + 16 * ch) = pre[i];
     u32x4 v[PASSES];
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) v[i] = buffer_load16(r, goff(row0 + ROWS_PER_PASS * i), 0);
+    for (int i = PRE; i < PASSES; ++i)
+        v[i] = buffer_load16(r, out_off<T, NT, BM, BN>(ldd, M, N, m0, n0, tid, i), 0);
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i)
-        *(u32x4*)(smem + (row0 + ROWS_PER_PASS * i) * PITCH + 16 * ch) = v[i];
+    for (int i = PRE; i < PASSES; ++i)
+        *(u32x4*)(smem + (row0 + OM::ROWS_PER_PASS * i) * PITCH + 16 * ch) = v[i];
     __syncthreads();
     const int lr = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -130,9 +155,9 @@ __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
-        const int row = row0 + ROWS_PER_PASS * i;
+        const int row = row0 + OM::ROWS_PER_PASS * i;
         __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * PITCH + 16 * ch), r,
-                                              goff(row), 0, 0);
+                                              out_off<T, NT, BM, BN>(ldd, M, N, m0, n0, tid, i), 0, 0);
     }
 }
 

@@ -44,6 +44,8 @@
 //  * Split K (dweight's K = B*T): fp32 partial tiles in the workspace, the
 //    last arriver adds them in split order, adds the old output and rounds
 //    once to bf16.
+#include <type_traits>
+
 #include "mmb_tile_common.h"
 
 namespace mmb {
@@ -188,6 +190,15 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         const auto rb = make_rsrc(Bp + ob, live ? (b_elems - ob) * 2 : 0);
         stg_b[j] = buffer_load16(rb, b_off[j], 0);
     };
+    // Old output tile, passes 2j and 2j+1 of the epilogue, into the staging
+    // registers of pair j (an empty range for units that publish a partial).
+    const bool own_write = splits <= 1;
+    const long long out_base = (long long)m0 * ldd + n0;
+    const auto ro = make_rsrc(D + out_base, own_write ? ((long long)M * ldd - out_base) * 2 : 0);
+    auto load_out_pair = [&](int j) {
+        stg_a[j] = buffer_load16(ro, out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, 2 * j), 0);
+        stg_b[j] = buffer_load16(ro, out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, 2 * j + 1), 0);
+    };
     // Registers -> LDS buffer `stage`: load j of wave w fills 1 KB block
     // LOADS * w + j of each operand region, lane p at byte 16p.
     auto store_pair = [&](int stage, int j) {
@@ -268,7 +279,11 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         __syncthreads();
         Frag f0, f1;
         read_sub(0, 0, f0);
-        for (int it = 0; it < nk; ++it) {
+        // One iteration; in the last one there is no next stage to store,
+        // and its load slots fetch the first half of the old output tile for
+        // the epilogue instead (units that write their tile themselves).
+        auto iteration = [&](int it, auto last) {
+            constexpr bool LAST = decltype(last)::value;
             const int cur = it & 1;
             if (do_bias) bias_add(cur);
             // substeps 0..2: pair j of stage it+1 to LDS, pair j of stage it+2
@@ -276,21 +291,31 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
 #pragma unroll
             for (int j = 0; j < 3; ++j) {
                 wait_loads<2 * (LOADS - 1)>();
-                store_pair(cur ^ 1, j);
-                load_pair(kt0 + it + 2, j);
+                if constexpr (LAST) {
+                    load_out_pair(j);
+                } else {
+                    store_pair(cur ^ 1, j);
+                    load_pair(kt0 + it + 2, j);
+                }
                 read_sub(cur, j + 1, (j & 1) ? f0 : f1);
                 mma_sub((j & 1) ? f1 : f0);
                 interleave_substep<AK ? 8 : 12>();
                 __builtin_amdgcn_sched_barrier(0);
             }
             wait_loads<2 * (LOADS - 1)>();
-            store_pair(cur ^ 1, 3);
-            load_pair(kt0 + it + 2, 3);
+            if constexpr (LAST) {
+                load_out_pair(3);
+            } else {
+                store_pair(cur ^ 1, 3);
+                load_pair(kt0 + it + 2, 3);
+            }
             __syncthreads();
-            if (it + 1 < nk) read_sub(cur ^ 1, 0, f0);
+            if constexpr (!LAST) read_sub(cur ^ 1, 0, f0);
             mma_sub(f1);
             __builtin_amdgcn_sched_barrier(0);
-        }
+        };
+        for (int it = 0; it + 1 < nk; ++it) iteration(it, std::false_type());
+        iteration(nk - 1, std::true_type());
     }
     wait_loads<0>();
 
@@ -324,9 +349,19 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         sum_partials<MB, NB, NT>(w0, splits, BM * BN, acc, tid);
         if (do_bias && tid < BM) bias = sum_bias(wb, splits, BM);
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
+        write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0,
+                                                   wn0);
+    } else if (nk > 0) {
+        // the last K iteration loaded passes 0..7 of the old tile
+        static_assert(LOADS == 4, "the old tile's first 8 passes sit in the 4 staging pairs");
+        const u32x4 pre[2 * LOADS] = {stg_a[0], stg_b[0], stg_a[1], stg_b[1],
+                                      stg_a[2], stg_b[2], stg_a[3], stg_b[3]};
+        write_tile_lds<bf16_t, MB, NB, NT, BM, BN, 2 * LOADS>(D, ldd, M, N, m0, n0, acc, smem, tid,
+                                                               lane, wm0, wn0, pre);
+    } else {
+        write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0,
+                                                   wn0);
     }
-
-    write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
     if (do_bias && tid < BM && m0 + tid < M) ((bf16_t*)p.dbias)[m0 + tid] = from_f32<bf16_t>(bias);
 }
 
