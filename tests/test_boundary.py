@@ -198,3 +198,49 @@ def test_plan_split_override(mmb, monkeypatch):
     (sw, si), units = mmb.mmb_plan_units(2, 150, 264, 400, 1, True, 256)
     assert (sw, si) == (3, 2)
     assert all(u[6] == (3 if u[0] == 0 else 2) for u in units)
+
+
+def test_plan_deals_each_split_level_evenly_over_xcds(mmb, monkeypatch):
+    """Workgroup i runs on XCD i % 8; every run of equal split counts of a
+    GEMM is spread over the 8 XCDs within one unit of each other."""
+    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", "4")
+    monkeypatch.setenv("MMB_SPLITS_DINP", ",".join(["1"] * 5 + ["2", "3"]))
+    _, units = mmb.mmb_plan_units(16, 1024, 768, 3072, 1, True, 256)
+    levels = {}
+    for i, u in enumerate(units):
+        levels.setdefault((u[0], u[6]), [0] * 8)[i % 8] += 1
+    assert sorted(levels) == [(0, 4), (1, 1), (1, 2), (1, 3)]
+    for counts in levels.values():
+        assert max(counts) - min(counts) <= 1
+
+
+@pytest.mark.parametrize("shape,want", [
+    ((16, 1024, 768, 3072, 1, True), (4, 1)),     # GPT-2 fc, bf16
+    ((8, 1024, 768, 50304, 1, False), (1, 2)),    # GPT-2 LM head, bf16
+    ((8, 1024, 768, 2304, 0, True), (13, 1)),     # GPT-2 qkv, fp32
+    ((8, 1024, 768, 3072, 0, True), (2, 4)),      # GPT-2 fc, fp32
+    ((8, 1024, 3072, 768, 0, True), (2, 1)),      # GPT-2 fc_proj, fp32
+], ids=["fc_bf16", "lm_head_bf16", "qkv_f32", "fc_f32", "fc_proj_f32"])
+def test_plan_picks_the_measured_best_splits(mmb, monkeypatch, shape, want):
+    """On a 256-CU MI355X the planner's model picks the split counts that
+    timed fastest in forced-split sweeps of these shapes."""
+    monkeypatch.delenv("MMB_SPLITS_DWEIGHT", raising=False)
+    monkeypatch.delenv("MMB_SPLITS_DINP", raising=False)
+    monkeypatch.delenv("MMB_PLAN_MODEL", raising=False)
+    B, T, C, OC, dt, bias = shape
+    (sw, si), _ = mmb.mmb_plan_units(B, T, C, OC, dt, bias, 256)
+    assert (sw, si) == want
+
+
+def test_plan_model_override(mmb, monkeypatch):
+    """MMB_PLAN_MODEL replaces the cost constants; a malformed value is
+    ignored."""
+    monkeypatch.delenv("MMB_SPLITS_DWEIGHT", raising=False)
+    monkeypatch.delenv("MMB_SPLITS_DINP", raising=False)
+    shape = (16, 1024, 768, 3072, 1, True)
+    base = mmb.mmb_plan_units(*shape, 256)[0]
+    monkeypatch.setenv("MMB_PLAN_MODEL", "1,2,3")
+    assert mmb.mmb_plan_units(*shape, 256)[0] == base
+    # splitting made ruinous: every partial costs a millisecond of traffic
+    monkeypatch.setenv("MMB_PLAN_MODEL", "1.4,1.26,0.72,0.97,0.97,0.8,3.8,8.5,2.1,2.5,4.4,1e-3")
+    assert mmb.mmb_plan_units(*shape, 256)[0] == (1, 1)
