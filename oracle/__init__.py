@@ -1,4 +1,5 @@
-"""CPU oracle for the GPT-2 linear-layer backward pass (test infrastructure).
+"""CPU oracle for the GPT-2 linear-layer backward pass and its forward
+(test infrastructure).
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -11,8 +12,10 @@ marshals numpy arrays through ctypes.  Method source: the llm.c page
 cuBLAS launcher ``matmul_backward1``.
 
 Every function returns new float64 arrays and never modifies its inputs.
-The dbias output buffer is filled with NaN before the C code runs, so a
-result that added onto the buffer instead of assigning it would show.
+The dbias and forward output buffers are filled with NaN before the C code
+runs, so a result that added onto the buffer instead of assigning it would
+show.  ``forward`` is the layer's forward product (out = inp . W^T + bias),
+the step before the backward pass.
 """
 from __future__ import annotations
 
@@ -66,8 +69,9 @@ class Oracle:
         lib.mmb_oracle_dweight.argtypes = [dp, dp, dp, L, L, L, L]
         lib.mmb_oracle_dbias.argtypes = [dp, dp, L, L, L]
         lib.mmb_oracle_backward.argtypes = [dp, dp, dp, dp, dp, dp, L, L, L, L]
+        lib.mmb_oracle_forward.argtypes = [dp, dp, dp, dp, L, L, L, L]
         for f in ("mmb_oracle_dinp", "mmb_oracle_dweight", "mmb_oracle_dbias",
-                  "mmb_oracle_backward"):
+                  "mmb_oracle_backward", "mmb_oracle_forward"):
             getattr(lib, f).restype = None
         lib.mmb_oracle_threads.argtypes = []
         lib.mmb_oracle_threads.restype = ctypes.c_int
@@ -115,6 +119,16 @@ class Oracle:
                                      _ptr(d), _ptr(x), _ptr(w), B, T, C, OC)
         return gi, gw, gb
 
+    def forward(self, inp, weight, bias=None, *, B, T, C, OC):
+        """inp @ weight^T (+ bias), shape [B*T, OC]; assigned, not accumulated."""
+        x = _f64(inp, (B * T, C))
+        w = _f64(weight, (OC, C))
+        b = None if bias is None else _f64(bias, (OC,))
+        out = np.full((B * T, OC), np.nan)
+        self.lib.mmb_oracle_forward(_ptr(out), _ptr(x), _ptr(w),
+                                    None if b is None else _ptr(b), B, T, C, OC)
+        return out
+
     def threads(self) -> int:
         """OpenMP threads the parallel loops use."""
         return int(self.lib.mmb_oracle_threads())
@@ -146,6 +160,10 @@ def dbias(*a, **k):
 
 def backward(*a, **k):
     return _get().backward(*a, **k)
+
+
+def forward(*a, **k):
+    return _get().forward(*a, **k)
 
 
 def threads() -> int:

@@ -17,6 +17,10 @@
  *   dweight[o,i] <- dweight[o,i] + sum_{r<BT} dout[r,o] * inp[r,i]
  *   dbias[o]     <- sum_{r<BT} dout[r,o]          (written, not added)
  *
+ * and, for the forward whose gradients these are,
+ *
+ *   out[r,o]     <- sum_{i<C} inp[r,i] * weight[o,i] (+ bias[o])   (written)
+ *
  * with r running over the B*T rows.  All tensors are dense row-major:
  * inp [BT,C], dout [BT,OC], weight [OC,C], dinp [BT,C], dweight [OC,C],
  * dbias [OC].  The gradients of dinp and dweight add onto what the buffers
@@ -93,6 +97,28 @@ void mmb_oracle_backward(double* dinp, double* dweight, double* dbias,
     mmb_oracle_dweight(dweight, dout, inp, B, T, C, OC);
     if (dbias != NULL)
         mmb_oracle_dbias(dbias, dout, B, T, OC);
+}
+
+/* The forward of the same layer, whose gradients the functions above are:
+ * out[r,o] = sum_{i<C} inp[r,i] * weight[o,i] (+ bias[o] when bias is not
+ * NULL), one dot product of length C per output element.  The page's
+ * launcher recalls this product in its comments (one GEMM with the weight
+ * transposed, alpha = 1, beta = 0: out is assigned, never accumulated); the
+ * bias term is the b of out = inp . W^T + b whose gradient dbias is.
+ * out is [BT,OC]. */
+void mmb_oracle_forward(double* out, const double* inp, const double* weight,
+                        const double* bias, long B, long T, long C, long OC)
+{
+    const long BT = B * T;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < BT; r++) {
+        for (long o = 0; o < OC; o++) {
+            double s = 0.0;
+            for (long i = 0; i < C; i++)
+                s += inp[r * C + i] * weight[o * C + i];
+            out[r * OC + o] = bias != NULL ? s + bias[o] : s;
+        }
+    }
 }
 
 /* Number of OpenMP threads a parallel region above would use. */

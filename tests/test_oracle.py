@@ -13,6 +13,11 @@ pinned by:
     dweight of an appended ones column, the LM-head row-sum-zero property);
   * mutation tests: textual mistakes planted in a copy of the oracle's C
     source must each fail at least one pin.
+The forward product (out = inp . W^T + bias, the step before the backward
+pass) is pinned by its own hand-worked example (tests/golden/hand_forward.txt),
+by its value at inp = 0 and its exact unit-step differences (it is affine in
+every argument), and by the adjoint identity that ties it to the
+brute-force-pinned backward pass.
 """
 import os
 import re
@@ -25,6 +30,7 @@ import oracle
 from linear_layer_backward_amd import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.txt")
+GOLDEN_FWD = os.path.join(os.path.dirname(__file__), "golden", "hand_forward.txt")
 
 
 def read_golden(path=GOLDEN):
@@ -114,7 +120,67 @@ def pin_dbias_overwrites(o):
     np.testing.assert_array_equal(o.dbias(dout, B=2, T=2, OC=3), [18.0, 22.0, 26.0])
 
 
-PINS = [pin_hand_example, pin_brute_force, pin_dbias_overwrites]
+def pin_forward_hand_example(o):
+    g = read_golden(GOLDEN_FWD)
+    B, T, C, OC = (int(g[k][0, 0]) for k in ("B", "T", "C", "OC"))
+    out = o.forward(g["inp"], g["weight"], g["bias"].ravel(), B=B, T=T, C=C, OC=OC)
+    np.testing.assert_array_equal(out, g["expect_out"])
+    out = o.forward(g["inp"], g["weight"], None, B=B, T=T, C=C, OC=OC)
+    np.testing.assert_array_equal(out, g["expect_out_nobias"])
+
+
+FORWARD_SHAPES = [(1, 1, 1, 1), (1, 2, 3, 5), (2, 3, 5, 2), (1, 4, 2, 3)]
+
+
+def pin_forward_affine(o, shapes=FORWARD_SHAPES):
+    """The forward is affine in each argument with known partial derivatives,
+    so with integer inputs (exact in double) it is fixed by: its value at
+    inp = 0 (the bias on every row, or 0 without a bias), and the unit steps
+    out(inp + e[r,i]) - out = weight[:, i] on row r only,
+    out(weight + e[o,i]) - out = inp[:, i] on column o only,
+    out(bias + e[o]) - out = 1 on column o only."""
+    for n, (B, T, C, OC) in enumerate(shapes):
+        case = wl.integer_case(B, T, C, OC, seed=100 + n, lo=-3, hi=3)
+        x, w = case.inp.astype(np.float64), case.weight.astype(np.float64)
+        b = case.dinp0.ravel()[:1].repeat(OC).astype(np.float64) + np.arange(OC) - 1.0
+        BT = B * T
+        kw = dict(B=B, T=T, C=C, OC=OC)
+        np.testing.assert_array_equal(o.forward(np.zeros_like(x), w, b, **kw),
+                                      np.tile(b, (BT, 1)))
+        np.testing.assert_array_equal(o.forward(np.zeros_like(x), w, None, **kw),
+                                      np.zeros((BT, OC)))
+        base = o.forward(x, w, b, **kw)
+        for r in range(BT):
+            for i in range(C):
+                xs = x.copy(); xs[r, i] += 1.0
+                expect = np.zeros((BT, OC)); expect[r] = w[:, i]
+                np.testing.assert_array_equal(o.forward(xs, w, b, **kw) - base, expect)
+        for oc in range(OC):
+            for i in range(C):
+                ws = w.copy(); ws[oc, i] += 1.0
+                expect = np.zeros((BT, OC)); expect[:, oc] = x[:, i]
+                np.testing.assert_array_equal(o.forward(x, ws, b, **kw) - base, expect)
+            bs = b.copy(); bs[oc] += 1.0
+            expect = np.zeros((BT, OC)); expect[:, oc] = 1.0
+            np.testing.assert_array_equal(o.forward(x, w, bs, **kw) - base, expect)
+
+
+def pin_forward_adjoint(o):
+    """The backward pass is the adjoint of the forward product:
+    sum(dout * (inp @ W^T)) = sum(inp * dinp(dout)) = sum(W * dweight(dout)),
+    exact with integer inputs; the backward side is pinned by brute force."""
+    for n, (B, T, C, OC) in enumerate([(2, 3, 5, 7), (1, 6, 4, 3)]):
+        case = wl.integer_case(B, T, C, OC, seed=200 + n, lo=-3, hi=3)
+        kw = dict(B=B, T=T, C=C, OC=OC)
+        out = o.forward(case.inp, case.weight, None, **kw)
+        gi, gw, _ = o.backward(case.dout, case.inp, case.weight, None, None, False, **kw)
+        lhs = float(np.sum(case.dout * out))
+        assert lhs == float(np.sum(case.inp * gi))
+        assert lhs == float(np.sum(case.weight * gw))
+
+
+PINS = [pin_hand_example, pin_brute_force, pin_dbias_overwrites,
+        pin_forward_hand_example, pin_forward_affine, pin_forward_adjoint]
 
 
 # ---------------------------------------------------------------------------
@@ -164,6 +230,53 @@ def test_brute_force_float():
 
 def test_dbias_overwrites(o):
     pin_dbias_overwrites(o)
+
+
+def test_forward_hand_example(o):
+    pin_forward_hand_example(o)
+
+
+def test_forward_affine(o):
+    pin_forward_affine(o)
+
+
+def test_forward_adjoint(o):
+    pin_forward_adjoint(o)
+
+
+@pytest.mark.parametrize("shape", [(2, 16, 64, 192), (3, 7, 33, 65), (1, 1, 8, 1)])
+def test_forward_numpy_special_case(shape):
+    """numpy float64 matmul reproduces the forward product, with and without bias."""
+    B, T, C, OC = shape
+    case = wl.random_case(B, T, C, OC, seed=9)
+    x, w = case.inp.astype(np.float64), case.weight.astype(np.float64)
+    b = wl.normal(99, (OC,), 1.0, "f32").astype(np.float64)
+    np.testing.assert_allclose(oracle.forward(x, w, b, B=B, T=T, C=C, OC=OC), x @ w.T + b,
+                               rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.forward(x, w, None, B=B, T=T, C=C, OC=OC), x @ w.T,
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_forward_closed_form_identity_weight():
+    """weight = I (C == OC): out = inp + bias exactly."""
+    B, T, C = 2, 3, 6
+    case = wl.random_case(B, T, C, C, seed=15)
+    b = wl.normal(98, (C,), 1.0, "f32").astype(np.float64)
+    out = oracle.forward(case.inp, np.eye(C), b, B=B, T=T, C=C, OC=C)
+    np.testing.assert_array_equal(out, case.inp.astype(np.float64) + b)
+
+
+def test_forward_closed_form_one_hot_inp():
+    """inp rows one-hot at column j(r): out row r = weight[:, j(r)] + bias."""
+    B, T, C, OC = 1, 9, 4, 6
+    rng = np.random.default_rng(8)
+    hot = rng.integers(0, C, size=B * T)
+    inp = np.zeros((B * T, C)); inp[np.arange(B * T), hot] = 1.0
+    w = rng.standard_normal((OC, C))
+    b = rng.standard_normal(OC)
+    out = oracle.forward(inp, w, b, B=B, T=T, C=C, OC=OC)
+    for r in range(B * T):
+        np.testing.assert_array_equal(out[r], w[:, hot[r]] + b)
 
 
 @pytest.mark.parametrize("shape", [(2, 16, 64, 192), (3, 7, 33, 65), (1, 1, 8, 1)])
@@ -308,6 +421,19 @@ MUTATIONS = [
      "dbias[o] = s;", "dbias[o] = dbias[o] + s;"),
     ("dbias sums a row instead of a column",
      "s += dout[r * OC + o];\n        dbias", "s += dout[(o % BT) * OC + (r % OC)];\n        dbias"),
+    ("forward reads the weight transposed",
+     "s += inp[r * C + i] * weight[o * C + i];", "s += inp[r * C + i] * weight[i * OC + o];"),
+    ("forward drops the bias",
+     "bias != NULL ? s + bias[o] : s;", "bias != NULL ? s : s;"),
+    ("forward indexes the bias by row",
+     "bias != NULL ? s + bias[o] : s;", "bias != NULL ? s + bias[r % OC] : s;"),
+    ("forward drops the last term",
+     "for (long i = 0; i < C; i++)\n                s += inp",
+     "for (long i = 0; i < C - 1; i++)\n                s += inp"),
+    ("forward accumulates onto the buffer",
+     "out[r * OC + o] = bias", "out[r * OC + o] += bias"),
+    ("forward written transposed",
+     "out[r * OC + o] = bias", "out[o * BT + r] = bias"),
 ]
 
 
