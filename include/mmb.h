@@ -1,6 +1,7 @@
 /*
  * mmb.h -- C ABI of libmmb.so, the backward pass of a GPT-2 linear layer
- * (out = inp . W^T + bias) on AMD Instinct MI355X (gfx950).
+ * (out = inp . W^T + bias) on AMD Instinct MI355X (gfx950), and the forward
+ * product it is the gradient of (mmb_forward, below).
  *
  * Operation (llm.c page "dev/cuda/matmul_backward.cu": CPU reference
  * matmul_backward_cpu and the cuBLAS launcher matmul_backward1), with
@@ -112,6 +113,47 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
  * shape[1] columns (N), shape[2] the K depth of one pipeline stage.
  * Host only.  Returns MMB_OK or MMB_ERR_DTYPE / MMB_ERR_NULL. */
 int mmb_tile_shape(int dtype, int* shape);
+
+/* ---- the forward product ------------------------------------------------
+ *
+ * The forward of the same layer, whose gradients mmb_backward computes
+ * (the page's launcher recalls it in its comments: one GEMM with the weight
+ * transposed, alpha = 1, beta = 0), plus the bias:
+ *
+ *   out[r,o] = sum_{i<C} inp[r,i] * weight[o,i] + bias[o]     r<BT, o<OC
+ *
+ * out [BT,OC] is assigned (its old contents are ignored); bias [OC] may be
+ * NULL (no bias term).  inp [BT,C] and weight [OC,C] as for mmb_backward,
+ * read only; one dtype for all four tensors, with the same arithmetic: fp32
+ * throughout, or bf16 storage with fp32 accumulation and one round to
+ * nearest-even of  fp32 sum + bias.  out may not overlap inp, weight or bias
+ * (MMB_ERR_ALIAS).  16-byte aligned out, inp, weight and bias with C and OC
+ * multiples of 8 (bf16) or 4 (fp32) take the MFMA tiles, anything else the
+ * generic path.  Workspace, errors, determinism and streams as for
+ * mmb_backward (the two share the per-(device, stream) workspace). */
+int mmb_forward(void* out, const void* inp, const void* weight, const void* bias,
+                int B, int T, int C, int OC, int dtype);
+
+/* As mmb_forward, enqueued on `stream` (a hipStream_t; NULL = default). */
+int mmb_forward_stream(void* out, const void* inp, const void* weight, const void* bias,
+                       int B, int T, int C, int OC, int dtype, void* stream);
+
+/* Host-only validation of a forward argument set (no HIP call). */
+int mmb_forward_check_args(const void* out, const void* inp, const void* weight,
+                           const void* bias, int B, int T, int C, int OC, int dtype);
+
+/* Which kernel path a forward call takes: 1 = MFMA tiles, 0 = generic,
+ * or a negative mmb_status.  Host only. */
+int mmb_forward_path(const void* out, const void* inp, const void* weight,
+                     const void* bias, int B, int T, int C, int OC, int dtype);
+
+/* Host-only view of the forward work plan, as mmb_plan_units: splits[0]
+ * receives the largest split count of the forward's tiles, and each unit is
+ * {kind (always 1), tile_m, tile_n, split, kt0, kt1, splits, first slot}
+ * with tile_m over the BT rows and tile_n over the OC columns.  Honours
+ * MMB_SPLITS_FWD (one count, or a per-tile list) like mmb_forward. */
+int mmb_forward_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
+                           int* splits, int* units, int max_units);
 
 /* Synchronise every device the library has used, then free its workspaces.
  * The next call allocates again. */

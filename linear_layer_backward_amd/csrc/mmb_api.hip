@@ -59,6 +59,40 @@ int check(const void* dinp, const void* dweight, const void* dbias, const void* 
     return MMB_OK;
 }
 
+// Forward: out [BT,OC] = inp [BT,C] . weight^T + bias; out may not overlap
+// an input.
+int check_fwd(const void* out, const void* inp, const void* weight, const void* bias, int B,
+              int T, int C, int OC, int dtype) {
+    if (!out || !inp || !weight) return MMB_ERR_NULL;
+    if (B < 1 || T < 1 || C < 1 || OC < 1) return MMB_ERR_DIM;
+    if (dtype != MMB_FP32 && dtype != MMB_BF16) return MMB_ERR_DTYPE;
+    const long long BT = (long long)B * T;
+    if (BT > 0x7fffffffLL) return MMB_ERR_OVERFLOW;
+    const uintptr_t es = elem_size(dtype);
+    auto R = [&](const void* p, long long n) {
+        return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
+    };
+    const Range o = R(out, BT * OC);
+    const Range ins[3] = {R(inp, BT * C), R(weight, (long long)OC * C),
+                          bias ? R(bias, OC) : Range{0, 0}};
+    for (const Range& r : ins)
+        if (overlap(o, r)) return MMB_ERR_ALIAS;
+    return MMB_OK;
+}
+
+// 1 when the MFMA tiles can take a forward call: as for the backward pass,
+// and the bias (read as 16-byte groups in the epilogue) is aligned too.
+int choose_path_fwd(const void* out, const void* inp, const void* weight, const void* bias, int C,
+                    int OC, int dtype) {
+    const int vec = dtype == MMB_BF16 ? 8 : 4;
+    if (C % vec != 0 || OC % vec != 0) return 0;
+    if (C > (1 << 22) || OC > (1 << 22)) return 0;
+    const void* ptrs[4] = {out, inp, weight, bias};
+    for (const void* p : ptrs)
+        if ((uintptr_t)p % 16 != 0) return 0;   // NULL bias passes
+    return 1;
+}
+
 // 1 when the MFMA tiles can take the call: 16-byte vectors never straddle a
 // row end (C and OC multiples of the vector width) and every streamed buffer
 // is 16-byte aligned.  dbias is written one element at a time.
@@ -447,6 +481,61 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     return p;
 }
 
+// The forward launch: one GEMM (M = BT, N = OC, K = C) in slot UNIT_FWD, the
+// other slot empty, and one split count for all its tiles, chosen by the
+// same event model (a split forward tile sums its partials like a dinp tile;
+// only its epilogue differs, adding the bias instead of the old output).
+// MMB_SPLITS_FWD forces the count as MMB_SPLITS_DINP does for dinp.
+Plan build_plan_forward(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& dev,
+                        const std::vector<int>& force) {
+    const TileShape ts = tile_shape(dtype);
+    GemmPlan g[2];
+    g[UNIT_DWEIGHT] = GemmPlan{0, 0, 0, 0, 0, 0, 0};
+    g[UNIT_FWD] = GemmPlan{BT, OC, C, cdiv(BT, ts.BM), cdiv(OC, ts.BN), cdiv(C, ts.BK), 0};
+    const int ntiles = g[UNIT_FWD].tiles_m * g[UNIT_FWD].tiles_n;
+    const CostModel cm = cost_model(dtype);
+    const double tile_bytes = 4.0 * ts.BM * ts.BN;
+    const int max_s = std::min(8, g[UNIT_FWD].kiters);
+    const bool trace = std::getenv("MMB_PLAN_TRACE") != nullptr;
+    Layout best_L;
+    double best = 1e300;
+    for (int si = 1; si <= max_s; ++si) {
+        if (force.size() == 1 && si != std::min(force[0], max_s)) continue;
+        if (force.size() > 1 && si > 1) continue;
+        Layout L;
+        L.splits[UNIT_FWD].assign(ntiles, si);
+        const double t = plan_cost(g, L, dev, cm, tile_bytes, trace ? 1e300 : best);
+        if (trace) std::fprintf(stderr, "mmb plan: forward splits %d cost %.2f us\n", si, t);
+        if (t < best - 1e-9) {
+            best = t;
+            best_L = L;
+        }
+    }
+    if (force.size() > 1)
+        for (int t = 0; t < ntiles; ++t)
+            best_L.splits[UNIT_FWD][t] = std::min(force[t % force.size()], g[UNIT_FWD].kiters);
+
+    Plan p;
+    std::memset(&p.proto, 0, sizeof(p.proto));
+    p.units = make_units(g, best_L, dev);
+    long long slots = 0;
+    for (int s : best_L.splits[UNIT_FWD]) {
+        p.max_splits[UNIT_FWD] = std::max(p.max_splits[UNIT_FWD], s);
+        if (s > 1) slots += s;
+    }
+    (void)bias;
+    p.ws_floats = slots * ts.BM * ts.BN;
+    p.ws_bias_floats = 0;
+    p.n_counters = ntiles;
+    p.proto.BT = BT;
+    p.proto.C = C;
+    p.proto.OC = OC;
+    p.proto.g[0] = g[0];
+    p.proto.g[1] = g[1];
+    p.proto.n_units = (int)p.units.size();
+    return p;
+}
+
 // ---------------------------------------------------------------------------
 // state: plans per (device, shape) and workspaces per (device, stream)
 
@@ -459,7 +548,8 @@ struct Workspace {
 
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_dev;
-std::map<std::tuple<int, int, int, int, int, bool>, Plan> g_plans;
+// key: device, dtype, BT, C, OC, bias, forward (1) or backward (0)
+std::map<std::tuple<int, int, int, int, int, bool, int>, Plan> g_plans;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 int device_info(int dev, DeviceInfo* out) {
@@ -481,13 +571,14 @@ int device_info(int dev, DeviceInfo* out) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
-    // MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP force the split counts (tuning
-    // sweeps, tests); unset lets the planner choose.
-    const char* ew = std::getenv("MMB_SPLITS_DWEIGHT");
-    const char* ei = std::getenv("MMB_SPLITS_DINP");
+int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, bool fwd, Plan** out) {
+    // MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP (backward) and MMB_SPLITS_FWD
+    // (forward) force the split counts (tuning sweeps, tests); unset lets the
+    // planner choose.
+    const char* ew = fwd ? nullptr : std::getenv("MMB_SPLITS_DWEIGHT");
+    const char* ei = std::getenv(fwd ? "MMB_SPLITS_FWD" : "MMB_SPLITS_DINP");
     const std::string forced = std::string(ew ? ew : "") + "/" + (ei ? ei : "");
-    const auto key = std::make_tuple(dev, dtype, BT, C, OC, bias);
+    const auto key = std::make_tuple(dev, dtype, BT, C, OC, bias, fwd ? 1 : 0);
     auto it = g_plans.find(key);
     if (it != g_plans.end()) {
         if (it->second.forced == forced) {
@@ -503,7 +594,8 @@ int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, Plan** out) {
     int st = device_info(dev, &di);
     if (st != MMB_OK) return st;
     di.slots = tiles_resident(dtype);
-    Plan p = build_plan(dtype, BT, C, OC, bias, di, parse_splits(ew), parse_splits(ei));
+    Plan p = fwd ? build_plan_forward(dtype, BT, C, OC, bias, di, parse_splits(ei))
+                 : build_plan(dtype, BT, C, OC, bias, di, parse_splits(ew), parse_splits(ei));
     p.forced = forced;
     const size_t ub = p.units.size() * sizeof(Unit);
     if (hipMalloc(&p.d_units, ub) != hipSuccess) return MMB_ERR_NOMEM;
@@ -573,7 +665,7 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mu);
     Plan* plan = nullptr;
-    st = get_plan(dev, dtype, BT, C, OC, dbias != nullptr, &plan);
+    st = get_plan(dev, dtype, BT, C, OC, dbias != nullptr, false, &plan);
     if (st != MMB_OK) return st;
     TilesParams tp = plan->proto;
     st = get_workspace(dev, s, *plan, &tp);
@@ -587,10 +679,57 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     return launch_tiles(dtype, tp, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }
 
+int forward_impl(void* out, const void* inp, const void* weight, const void* bias, int B, int T,
+                 int C, int OC, int dtype, hipStream_t s) {
+    int st = check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
+    if (st != MMB_OK) return st;
+    const int BT = B * T;
+    if (!choose_path_fwd(out, inp, weight, bias, C, OC, dtype))
+        return launch_fwd_generic(dtype, out, inp, weight, bias, BT, C, OC, s) == hipSuccess
+                   ? MMB_OK
+                   : MMB_ERR_HIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    Plan* plan = nullptr;
+    st = get_plan(dev, dtype, BT, C, OC, bias != nullptr, true, &plan);
+    if (st != MMB_OK) return st;
+    TilesParams tp = plan->proto;
+    st = get_workspace(dev, s, *plan, &tp);
+    if (st != MMB_OK) return st;
+    tp.out = out;
+    tp.bias = bias;
+    tp.inp = inp;
+    tp.weight = weight;
+    return launch_fwd_tiles(dtype, tp, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace mmb
 
 extern "C" {
+
+int mmb_forward_check_args(const void* out, const void* inp, const void* weight, const void* bias,
+                           int B, int T, int C, int OC, int dtype) {
+    return mmb::check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
+}
+
+int mmb_forward_path(const void* out, const void* inp, const void* weight, const void* bias, int B,
+                     int T, int C, int OC, int dtype) {
+    const int st = mmb::check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
+    if (st != MMB_OK) return st;
+    return mmb::choose_path_fwd(out, inp, weight, bias, C, OC, dtype);
+}
+
+int mmb_forward_stream(void* out, const void* inp, const void* weight, const void* bias, int B,
+                       int T, int C, int OC, int dtype, void* stream) {
+    return mmb::forward_impl(out, inp, weight, bias, B, T, C, OC, dtype, (hipStream_t)stream);
+}
+
+int mmb_forward(void* out, const void* inp, const void* weight, const void* bias, int B, int T,
+                int C, int OC, int dtype) {
+    return mmb::forward_impl(out, inp, weight, bias, B, T, C, OC, dtype, nullptr);
+}
 
 int mmb_check_args(const void* dinp, const void* dweight, const void* dbias, const void* dout,
                    const void* inp, const void* weight, int B, int T, int C, int OC, int dtype) {
@@ -646,6 +785,30 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
                                         mmb::parse_splits(std::getenv("MMB_SPLITS_DINP")));
     splits[0] = p.max_splits[mmb::UNIT_DWEIGHT];
     splits[1] = p.max_splits[mmb::UNIT_DINP];
+    if (units) {
+        const int n = std::min<int>(max_units, (int)p.units.size());
+        for (int i = 0; i < n; ++i) {
+            const int4 a = p.units[i].a, b = p.units[i].b;
+            const int v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            for (int j = 0; j < 8; ++j) units[8 * i + j] = v[j];
+        }
+    }
+    return (int)p.units.size();
+}
+
+int mmb_forward_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
+                           int* splits, int* units, int max_units) {
+    if (B < 1 || T < 1 || C < 1 || OC < 1 || num_cus < 1) return MMB_ERR_DIM;
+    if (dtype != MMB_FP32 && dtype != MMB_BF16) return MMB_ERR_DTYPE;
+    if ((long long)B * T > 0x7fffffffLL) return MMB_ERR_OVERFLOW;
+    if (!splits) return MMB_ERR_NULL;
+    mmb::DeviceInfo di;
+    di.cus = num_cus;
+    mmb::set_topology(&di);
+    di.slots = mmb::tiles_resident(dtype);
+    const mmb::Plan p = mmb::build_plan_forward(dtype, B * T, C, OC, has_bias != 0, di,
+                                                mmb::parse_splits(std::getenv("MMB_SPLITS_FWD")));
+    splits[0] = p.max_splits[mmb::UNIT_FWD];
     if (units) {
         const int n = std::min<int>(max_units, (int)p.units.size());
         for (int i = 0; i < n; ++i) {

@@ -5,7 +5,8 @@
 //
 // Operation: llm.c page "dev/cuda/matmul_backward.cu" -- the dinp and
 // dweight GEMMs of matmul_backward1 (beta = 1) and the one-thread-per-channel
-// bias kernel matmul_backward_bias_kernel_naive (assigning dbias).
+// bias kernel matmul_backward_bias_kernel_naive (assigning dbias); and the
+// forward product out = inp . W^T + bias that the launcher's comments recall.
 #include "mmb_internal.h"
 #include "mmb_numeric.h"
 
@@ -61,6 +62,39 @@ __global__ __launch_bounds__(kBlock) void generic_dbias(T* __restrict__ dbias,
     dbias[o] = from_f32<T>(acc);
 }
 
+// Forward: out[r,o] = sum_i inp[r,i] * weight[o,i] (+ bias[o]), assigned;
+// block = one row r and 256 consecutive o (inp[r,i] is a broadcast).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void generic_forward(T* __restrict__ out,
+                                                          const T* __restrict__ inp,
+                                                          const T* __restrict__ weight,
+                                                          const T* __restrict__ bias,
+                                                          int C, int OC) {
+    const long long r = blockIdx.y;
+    const int o = blockIdx.x * kBlock + threadIdx.x;
+    if (o >= OC) return;
+    const T* x = inp + r * C;
+    const T* w = weight + (long long)o * C;
+    float acc = 0.f;
+    for (int i = 0; i < C; ++i) acc = fmaf(to_f32(x[i]), to_f32(w[i]), acc);
+    if (bias != nullptr) acc += to_f32(bias[o]);
+    out[r * OC + o] = from_f32<T>(acc);
+}
+
+template <typename T>
+hipError_t launch_forward(void* out, const void* inp, const void* weight, const void* bias,
+                          int BT, int C, int OC, hipStream_t s) {
+    const unsigned gx = (unsigned)((OC + kBlock - 1) / kBlock);
+    const int kRowsPerLaunch = 65535;   // grid.y limit
+    for (int r0 = 0; r0 < BT; r0 += kRowsPerLaunch) {
+        const int rows = BT - r0 < kRowsPerLaunch ? BT - r0 : kRowsPerLaunch;
+        hipLaunchKernelGGL(generic_forward<T>, dim3(gx, rows), dim3(kBlock), 0, s,
+                           (T*)out + (long long)r0 * OC, (const T*)inp + (long long)r0 * C,
+                           (const T*)weight, (const T*)bias, C, OC);
+    }
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch(void* dinp, void* dweight, void* dbias, const void* dout,
                   const void* inp, const void* weight, int BT, int C, int OC,
@@ -94,6 +128,12 @@ hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
                           int BT, int C, int OC, hipStream_t s) {
     if (dtype == 0) return launch<float>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s);
     return launch<bf16_t>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s);
+}
+
+hipError_t launch_fwd_generic(int dtype, void* out, const void* inp, const void* weight,
+                              const void* bias, int BT, int C, int OC, hipStream_t s) {
+    if (dtype == 0) return launch_forward<float>(out, inp, weight, bias, BT, C, OC, s);
+    return launch_forward<bf16_t>(out, inp, weight, bias, BT, C, OC, s);
 }
 
 }  // namespace mmb

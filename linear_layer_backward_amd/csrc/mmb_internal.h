@@ -14,6 +14,10 @@ namespace mmb {
 // (slot counts whole tiles) and the last to arrive finishes the tile.
 // Encoded as two int4: {kind, tile_m, tile_n, split}, {kt0, kt1, splits, slot}.
 enum UnitKind : int { UNIT_DWEIGHT = 0, UNIT_DINP = 1 };
+// The forward launch (out = inp . W^T + bias) runs one GEMM; it sits in slot
+// UNIT_DINP of the plan (its A operand, inp, is K-contiguous like dout in
+// the dinp GEMM) and slot UNIT_DWEIGHT is empty.
+constexpr int UNIT_FWD = UNIT_DINP;
 
 struct GemmPlan {
     int M, N, K;          // D[M,N] += A[M,K] . B[K,N]
@@ -22,7 +26,8 @@ struct GemmPlan {
     int tile_base;        // index of tile (0,0) in the counter array
 };
 
-// Everything the tiled kernel needs, passed by value.
+// Everything the tiled kernels need, passed by value (the backward launch
+// uses dinp .. weight, the forward launch out, bias, inp and weight).
 struct TilesParams {
     void* dinp;
     void* dweight;
@@ -37,6 +42,8 @@ struct TilesParams {
     float* ws;            // split-K partial tiles (fp32), one tile per slot
     float* ws_bias;       // split-K partial dbias rows (fp32), BM floats per slot
     int* counters;        // one arrival counter per tile, zero at rest
+    void* out;            // forward launch: out [BT,OC]
+    const void* bias;     // forward launch: bias [OC], may be NULL
 };
 
 // Tile shapes of the MFMA kernels (rows x cols of the output tile, K depth of
@@ -53,6 +60,12 @@ int tiles_bf16_bn();   // output columns of one bf16 tile
 // (LDS and register limits of the kernel as built).
 int tiles_resident(int dtype);
 int tiles_bf16_resident();
+// The forward product out = inp . W^T + bias with the same tiles (one GEMM,
+// M = BT, N = OC, K = C, in plan slot UNIT_FWD).
+hipError_t launch_fwd_tiles(int dtype, const TilesParams& p, hipStream_t s);
+hipError_t launch_fwd_tiles_bf16(const TilesParams& p, hipStream_t s);
+hipError_t launch_fwd_generic(int dtype, void* out, const void* inp, const void* weight,
+                              const void* bias, int BT, int C, int OC, hipStream_t s);
 hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
                           const void* dout, const void* inp, const void* weight,
                           int BT, int C, int OC, hipStream_t s);

@@ -113,8 +113,42 @@ __device__ __forceinline__ uint32_t out_off(long long ldd, int M, int N, int m0,
            oob_if_ge(n0 + OM::VEC * ch, N) | oob_if_ge(m0 + row, M);
 }
 
-// With PRE > 0, passes 0 .. PRE-1 of the old tile were already loaded by the
-// caller (pre[i], loaded from out_rsrc() at out_off(.., i)).
+// Second half of the epilogue, once LDS holds the base tile (the old output,
+// or the bias rows) and a barrier has published it: every lane adds its
+// accumulators at its fragment positions and rounds once in place, then the
+// tile goes out row-contiguously.
+template <typename T, int MB, int NB, int NT, int BM, int BN>
+__device__ __forceinline__ void add_round_write(T* D, long long ldd, int M, int N, int m0, int n0,
+                                                const f32x16 (&acc)[MB][NB], char* smem, int tid,
+                                                int lane, int wm0, int wn0) {
+    typedef OutMap<T, NT, BM, BN> OM;
+    constexpr int PITCH = out_pitch<T, BM, BN>();
+    const auto r = out_rsrc(D, ldd, M, m0, n0);
+    const int ch = tid % OM::CHUNKS, row0 = tid / OM::CHUNKS;
+    const int lr = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = wm0 + mb * 32 + lr, col = wn0 + nb * 32 + 8 * q + 4 * half;
+                const f32x4 a = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
+                                 acc[mb][nb][4 * q + 3]};
+                add_round_store(smem + row * PITCH + (int)sizeof(T) * col, a, T{});
+            }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < OM::PASSES; ++i) {
+        const int row = row0 + OM::ROWS_PER_PASS * i;
+        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * PITCH + 16 * ch), r,
+                                              out_off<T, NT, BM, BN>(ldd, M, N, m0, n0, tid, i), 0, 0);
+    }
+}
+
+// beta = 1: D = old + acc.  With PRE > 0, passes 0 .. PRE-1 of the old tile
+// were already loaded by the caller (pre[i], loaded from out_rsrc() at
+// out_off(.., i)).
 template <typename T, int MB, int NB, int NT, int BM, int BN, int PRE = 0>
 __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N, int m0, int n0,
                                                const f32x16 (&acc)[MB][NB], char* smem, int tid,
@@ -140,25 +174,30 @@ __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N
     for (int i = PRE; i < PASSES; ++i)
         *(u32x4*)(smem + (row0 + OM::ROWS_PER_PASS * i) * PITCH + 16 * ch) = v[i];
     __syncthreads();
-    const int lr = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = wm0 + mb * 32 + lr, col = wn0 + nb * 32 + 8 * q + 4 * half;
-                const f32x4 a = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
-                                 acc[mb][nb][4 * q + 3]};
-                add_round_store(smem + row * PITCH + (int)sizeof(T) * col, a, T{});
-            }
+    add_round_write<T, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
+}
+
+// beta = 0 with a bias row (the forward product): D[m, n] = acc + bias[n],
+// rounded once; bias == nullptr adds nothing.  Every LDS row of the tile
+// starts as the bias slice [n0, n0 + BN), so the add/round pass is the one of
+// the beta = 1 epilogue.  bias is 16-byte aligned and N a multiple of the
+// 16-byte group, as on the rest of this path.
+template <typename T, int MB, int NB, int NT, int BM, int BN>
+__device__ __forceinline__ void write_tile_bias(T* D, long long ldd, int M, int N, int m0, int n0,
+                                                const f32x16 (&acc)[MB][NB], char* smem, int tid,
+                                                int lane, int wm0, int wn0, const T* bias) {
+    typedef OutMap<T, NT, BM, BN> OM;
+    constexpr int PITCH = out_pitch<T, BM, BN>();
+    const int ch = tid % OM::CHUNKS, row0 = tid / OM::CHUNKS;
+    const auto rb = make_rsrc(bias + (bias ? n0 : 0),
+                              bias ? (long long)(N - n0) * (long long)sizeof(T) : 0);
+    const u32x4 b = buffer_load16(rb, (uint32_t)(16 * ch) | oob_if_ge(n0 + OM::VEC * ch, N), 0);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-        const int row = row0 + OM::ROWS_PER_PASS * i;
-        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * PITCH + 16 * ch), r,
-                                              out_off<T, NT, BM, BN>(ldd, M, N, m0, n0, tid, i), 0, 0);
-    }
+    for (int i = 0; i < OM::PASSES; ++i)
+        *(u32x4*)(smem + (row0 + OM::ROWS_PER_PASS * i) * PITCH + 16 * ch) = b;
+    __syncthreads();
+    add_round_write<T, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
 }
 
 // ---- split-K ---------------------------------------------------------------

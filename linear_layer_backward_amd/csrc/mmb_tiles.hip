@@ -1,6 +1,8 @@
 // mmb_tiles.hip -- fp32 MFMA tiles of the linear-layer backward pass: both
 // GEMMs and the bias reduction in one launch of output-tile work units (the
-// bf16 tiles live in mmb_tiles_bf16.hip).
+// bf16 tiles live in mmb_tiles_bf16.hip); and of the forward product
+// out = inp . W^T + bias (both operands K-contiguous, beta = 0, the bias
+// added in the epilogue), a launch of its own.
 //
 // Operation (llm.c page "dev/cuda/matmul_backward.cu", launcher
 // matmul_backward1 and bias kernels):
@@ -115,13 +117,19 @@ __device__ __forceinline__ void mma_stage(const char* sa, const char* sb, int wm
 }
 
 // ---- one work unit ---------------------------------------------------------
-// AK: the A operand (M side) is K-contiguous in memory (dinp: A = dout rows);
-// otherwise it is M-contiguous (dweight: A = dout^T).  B is always
-// N-contiguous (weight for dinp, inp for dweight).
-template <typename T, bool AK>
+// The three GEMMs, with the orientation of their operands in memory:
+//   DINP     dinp [BT,C]   += dout [BT,OC] . weight [OC,C]  A K-contiguous, B N-contiguous
+//   DWEIGHT  dweight [OC,C] += dout^T . inp [BT,C]          A M-contiguous, B N-contiguous
+//   FWD      out [BT,OC]    = inp [BT,C] . weight^T + bias  A K-contiguous, B K-contiguous
+// (FWD: out = inp . W^T, the forward product whose gradients the other two are.)
+enum class Op { DINP, DWEIGHT, FWD };
+
+template <typename T, Op OP>
 __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u, int4 v,
                                          char* smem, int* s_flag) {
     using Kt = K<T>;
+    constexpr bool AK = OP != Op::DWEIGHT;   // A rows K-contiguous (dout rows, inp rows)
+    constexpr bool BKC = OP == Op::FWD;      // B rows K-contiguous (weight rows)
     constexpr int BM = Kt::BM, BN = Kt::BN, BK = Kt::BK, E = Kt::E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tile_m = u.y, tile_n = u.z, split = u.w;
@@ -131,15 +139,15 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     // partial sums (if any) start at workspace slot `slot`
     const int kt0 = v.x, kt1 = v.y, splits = v.z, slot = v.w;
 
-    const T* A = (const T*)p.dout;                       // ld = OC either way
-    const T* Bop = (const T*)(AK ? p.weight : p.inp);    // ld = C
-    T* D = (T*)(AK ? p.dinp : p.dweight);                // ld = C
-    const long long lda = p.OC, ldb = p.C, ldd = p.C;
-    const bool do_bias = !AK && p.dbias != nullptr && tile_n == 0;
+    const T* A = (const T*)(OP == Op::FWD ? p.inp : p.dout);
+    const T* Bop = (const T*)(OP == Op::DWEIGHT ? p.inp : p.weight);   // ld = C
+    T* D = (T*)(OP == Op::DINP ? p.dinp : OP == Op::DWEIGHT ? p.dweight : p.out);
+    const long long lda = OP == Op::FWD ? p.C : p.OC, ldb = p.C, ldd = OP == Op::FWD ? p.OC : p.C;
+    const bool do_bias = OP == Op::DWEIGHT && p.dbias != nullptr && tile_n == 0;
 
     // staging thread roles
     const int kg = tid & 7, xg = tid >> 3;       // E x E block: K-group, column group
-    const bool b_active = xg < BN / E;
+    const bool b_active = BKC || xg < BN / E;
     const bool a_active = AK || xg < BM / E;
 
     constexpr int APER = AK ? Kt::A_KC_PER : E;
@@ -148,10 +156,20 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
 #pragma unroll
     for (int x = 0; x < E; ++x) bsum[x] = 0.f;
 
+    static_assert(Kt::BN * 8 / kThreads == E, "K-contiguous B: E vectors per thread");
     auto load = [&](int kt) {
         const int k0 = kt * BK;
-        // B: rows k (K-strided), E columns starting at n0 + xg*E
-        {
+        if constexpr (BKC) {
+            // B: rows n, 16-byte vectors along K
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const int n = n0 + (tid >> 3) + 32 * j;
+                const int k = k0 + (tid & 7) * E;
+                rb[j] = (n < N && k < Kd) ? *(const u32x4*)(Bop + (long long)n * ldb + k)
+                                          : u32x4{0, 0, 0, 0};
+            }
+        } else {
+            // B: rows k (K-strided), E columns starting at n0 + xg*E
             const int n = n0 + xg * E;
             const bool colok = b_active && n < N;
 #pragma unroll
@@ -185,7 +203,10 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     auto store = [&](int stage) {
         char* sa = smem + stage * Kt::STAGE_BYTES;
         char* sb = sa + BM * kRowBytes;
-        if (b_active) {
+        if constexpr (BKC) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) *(u32x4*)(sb + swz((tid >> 3) + 32 * j, tid & 7)) = rb[j];
+        } else if (b_active) {
             u32x4 t[E];
             transpose_block(rb, t, T{});
 #pragma unroll
@@ -260,8 +281,12 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
     }
 
-    write_tile_lds<T, Kt::MB, Kt::NB, kThreads, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
-                                                       wm0, wn0);
+    if constexpr (OP == Op::FWD)
+        write_tile_bias<T, Kt::MB, Kt::NB, kThreads, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid,
+                                                            lane, wm0, wn0, (const T*)p.bias);
+    else
+        write_tile_lds<T, Kt::MB, Kt::NB, kThreads, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid,
+                                                           lane, wm0, wn0);
     if (bias_owner) {
         T* db = (T*)p.dbias;
 #pragma unroll
@@ -278,9 +303,19 @@ __global__ __launch_bounds__(kThreads) void mmb_tiles_kernel(TilesParams p) {
     __shared__ int s_flag;
     const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
     if (u.x == UNIT_DINP)
-        run_unit<T, true>(p, p.g[UNIT_DINP], u, v, smem, &s_flag);
+        run_unit<T, Op::DINP>(p, p.g[UNIT_DINP], u, v, smem, &s_flag);
     else
-        run_unit<T, false>(p, p.g[UNIT_DWEIGHT], u, v, smem, &s_flag);
+        run_unit<T, Op::DWEIGHT>(p, p.g[UNIT_DWEIGHT], u, v, smem, &s_flag);
+}
+
+// The forward product out = inp . W^T + bias over the same tiles (plan slot
+// UNIT_FWD).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void mmb_fwd_kernel(TilesParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[K<T>::LDS_BYTES];
+    __shared__ int s_flag;
+    const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
+    run_unit<T, Op::FWD>(p, p.g[UNIT_FWD], u, v, smem, &s_flag);
 }
 
 }  // namespace
@@ -301,6 +336,13 @@ hipError_t launch_tiles(int dtype, const TilesParams& p, hipStream_t s) {
     if (dtype == 1) return launch_tiles_bf16(p, s);
     if (p.n_units <= 0) return hipSuccess;
     hipLaunchKernelGGL(mmb_tiles_kernel<float>, dim3(p.n_units), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_tiles(int dtype, const TilesParams& p, hipStream_t s) {
+    if (dtype == 1) return launch_fwd_tiles_bf16(p, s);
+    if (p.n_units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mmb_fwd_kernel<float>, dim3(p.n_units), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

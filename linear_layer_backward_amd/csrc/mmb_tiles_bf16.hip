@@ -1,6 +1,8 @@
 // mmb_tiles_bf16.hip -- bf16-storage / fp32-accumulate MFMA tiles of the
 // linear-layer backward pass (dinp and dweight GEMMs with beta = 1, dbias
-// fused into the dweight units of output column tile 0), one launch.
+// fused into the dweight units of output column tile 0), one launch; and of
+// the forward product out = inp . W^T + bias (both operands K-contiguous,
+// beta = 0, the bias added in the epilogue), a launch of its own.
 //
 // Operation: llm.c page "dev/cuda/matmul_backward.cu", launcher
 // matmul_backward1 (the two GEMMs) and the bias kernels (column sums of dout).
@@ -123,13 +125,20 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* region, int xb, int s, int
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// AK: A (M side) is K-contiguous in memory (dinp: dout rows); otherwise it
-// is M-contiguous (dweight: dout^T).  B (N side) is always N-contiguous
-// (weight for dinp, inp for dweight).  Leading dimensions: dout OC, weight
-// and inp C, output C.
-template <bool AK>
+// The three GEMMs these tiles run, with the orientation of their operands in
+// memory (leading dimensions: dout OC, weight and inp C):
+//   DINP     D = dinp [BT,C]  += dout [BT,OC] . weight [OC,C]   A K-contiguous, B N-contiguous
+//   DWEIGHT  D = dweight[OC,C] += dout^T . inp [BT,C]           A M-contiguous, B N-contiguous
+//   FWD      D = out [BT,OC]   = inp [BT,C] . weight^T + bias   A K-contiguous, B K-contiguous
+// (FWD: out = inp . W^T, the forward product whose gradients the other two are.)
+enum class Op { DINP, DWEIGHT, FWD };
+
+template <Op OP>
 __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u, int4 v,
                                          char* smem, int* s_flag) {
+    constexpr bool AK = OP != Op::DWEIGHT;   // A rows K-contiguous (dout rows, inp rows)
+    constexpr bool BKC = OP == Op::FWD;      // B rows K-contiguous (weight rows)
+    constexpr bool BETA1 = OP != Op::FWD;    // gradients accumulate; the forward assigns
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int tile_m = u.y, tile_n = u.z, split = u.w;
@@ -140,21 +149,21 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const int kt0 = v.x, kt1 = v.y, splits = v.z, slot = v.w;
     const int nk = kt1 - kt0;
 
-    const bf16_t* A = (const bf16_t*)p.dout;
-    const bf16_t* Bp = (const bf16_t*)(AK ? p.weight : p.inp);
-    bf16_t* D = (bf16_t*)(AK ? p.dinp : p.dweight);
-    const long long lda = p.OC, ldb = p.C, ldd = p.C;
-    const long long a_elems = (long long)p.BT * p.OC;
-    const long long b_elems = AK ? (long long)p.OC * p.C : (long long)p.BT * p.C;
-    const bool do_bias = !AK && p.dbias != nullptr && tile_n == 0;
+    const bf16_t* A = (const bf16_t*)(OP == Op::FWD ? p.inp : p.dout);
+    const bf16_t* Bp = (const bf16_t*)(OP == Op::DWEIGHT ? p.inp : p.weight);
+    bf16_t* D = (bf16_t*)(OP == Op::DINP ? p.dinp : OP == Op::DWEIGHT ? p.dweight : p.out);
+    const long long lda = OP == Op::FWD ? p.C : p.OC, ldb = p.C, ldd = OP == Op::FWD ? p.OC : p.C;
+    const long long a_elems = (long long)p.BT * lda;
+    const long long b_elems = OP == Op::DWEIGHT ? (long long)p.BT * p.C : (long long)p.OC * p.C;
+    const bool do_bias = OP == Op::DWEIGHT && p.dbias != nullptr && tile_n == 0;
 
     // Load geometry.  Wave w's i-th load of a region fills 1 KB block
     // LOADS * w + i; lane p lands at byte 16p of the block, so the lane
     // fetches the global vector that belongs there under the swizzle.
-    //   K-contiguous A: block rows 8 * block + p/8, physical chunk p%8
+    //   K-contiguous: block rows 8 * block + p/8, physical chunk p%8
     //   M/N-contiguous: block rows 2 * block + p/32, physical chunk p%32
     uint32_t a_off[LOADS], b_off[LOADS];
-    int a_kc[LOADS];   // K-contiguous A: K offset of the lane's vector in load i
+    int a_kc[LOADS], b_kc[LOADS];   // K-contiguous: K offset of the lane's vector in load i
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int blk = LOADS * wave + i;
@@ -168,11 +177,20 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             const int col = m0 + 8 * ((lane & 31) ^ sw_mn(row));
             a_off[i] = col < M ? (uint32_t)((row * lda + col) * 2) : kOOB;
         }
-        const int col = n0 + 8 * ((lane & 31) ^ sw_mn(row));
-        b_off[i] = col < N ? (uint32_t)((row * ldb + col) * 2) : kOOB;
+        if constexpr (BKC) {
+            const int krow = 8 * blk + (lane >> 3);
+            const int c = (lane & 7) ^ sw_kc(krow);
+            b_kc[i] = 8 * c;
+            b_off[i] = (uint32_t)(krow * ldb * 2 + c * 16);
+        } else {
+            const int col = n0 + 8 * ((lane & 31) ^ sw_mn(row));
+            b_kc[i] = 0;
+            b_off[i] = col < N ? (uint32_t)((row * ldb + col) * 2) : kOOB;
+        }
     }
 
     auto a_origin = [&](int kt) { return AK ? (long long)m0 * lda + kt * BK : (long long)kt * BK * lda; };
+    auto b_origin = [&](int kt) { return BKC ? (long long)n0 * ldb + kt * BK : (long long)(kt * BK) * ldb; };
     // Global -> register staging of stage kt, chunk pair j (load j of each
     // operand).  A stage past the end (kt >= kt1) still issues its loads, over
     // an empty range (they return zeros), so that every wave's count of
@@ -186,13 +204,15 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         // K tail inside a K-contiguous row: vectors at or past K read zeros
         const uint32_t kmask = AK ? oob_if_ge(k0 + a_kc[j], Kd) : 0u;
         stg_a[j] = buffer_load16(ra, a_off[j] | kmask, 0);
-        const long long ob = (long long)k0 * ldb;
+        const long long ob = b_origin(kt);
         const auto rb = make_rsrc(Bp + ob, live ? (b_elems - ob) * 2 : 0);
-        stg_b[j] = buffer_load16(rb, b_off[j], 0);
+        const uint32_t kmask_b = BKC ? oob_if_ge(k0 + b_kc[j], Kd) : 0u;
+        stg_b[j] = buffer_load16(rb, b_off[j] | kmask_b, 0);
     };
     // Old output tile, passes 2j and 2j+1 of the epilogue, into the staging
-    // registers of pair j (an empty range for units that publish a partial).
-    const bool own_write = splits <= 1;
+    // registers of pair j (an empty range for units that publish a partial;
+    // the forward has no old tile).
+    const bool own_write = BETA1 && splits <= 1;
     const long long out_base = (long long)m0 * ldd + n0;
     const auto ro = make_rsrc(D + out_base, own_write ? ((long long)M * ldd - out_base) * 2 : 0);
     auto load_out_pair = [&](int j) {
@@ -233,7 +253,8 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         const char* sa = smem + stage * STAGE;
         const char* sb = sa + REGION;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) f.a[nb] = frag_mn(sb, wn0 + nb * 32, k, lane);
+        for (int nb = 0; nb < NB; ++nb)
+            f.a[nb] = BKC ? frag_kc(sb, wn0 + nb * 32, k, lane) : frag_mn(sb, wn0 + nb * 32, k, lane);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             f.b[mb] = AK ? frag_kc(sa, wm0 + mb * 32, k, lane) : frag_mn(sa, wm0 + mb * 32, k, lane);
@@ -292,19 +313,19 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             for (int j = 0; j < 3; ++j) {
                 wait_loads<2 * (LOADS - 1)>();
                 if constexpr (LAST) {
-                    load_out_pair(j);
+                    if constexpr (BETA1) load_out_pair(j);
                 } else {
                     store_pair(cur ^ 1, j);
                     load_pair(kt0 + it + 2, j);
                 }
                 read_sub(cur, j + 1, (j & 1) ? f0 : f1);
                 mma_sub((j & 1) ? f1 : f0);
-                interleave_substep<AK ? 8 : 12>();
+                interleave_substep<(AK ? MB : 2 * MB) + (BKC ? NB : 2 * NB)>();
                 __builtin_amdgcn_sched_barrier(0);
             }
             wait_loads<2 * (LOADS - 1)>();
             if constexpr (LAST) {
-                load_out_pair(3);
+                if constexpr (BETA1) load_out_pair(3);
             } else {
                 store_pair(cur ^ 1, 3);
                 load_pair(kt0 + it + 2, 3);
@@ -349,8 +370,15 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         sum_partials<MB, NB, NT>(w0, splits, BM * BN, acc, tid);
         if (do_bias && tid < BM) bias = sum_bias(wb, splits, BM);
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
-        write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0,
-                                                   wn0);
+        if constexpr (BETA1)
+            write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
+                                                       wm0, wn0);
+        else
+            write_tile_bias<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
+                                                        wm0, wn0, (const bf16_t*)p.bias);
+    } else if (!BETA1) {
+        write_tile_bias<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0,
+                                                    wn0, (const bf16_t*)p.bias);
     } else if (nk > 0) {
         // the last K iteration loaded passes 0..7 of the old tile
         static_assert(LOADS == 4, "the old tile's first 8 passes sit in the 4 staging pairs");
@@ -372,9 +400,18 @@ __global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
     int* s_flag = (int*)(smem + 8192);
     const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
     if (u.x == UNIT_DINP)
-        run_unit<true>(p, p.g[UNIT_DINP], u, v, smem, s_flag);
+        run_unit<Op::DINP>(p, p.g[UNIT_DINP], u, v, smem, s_flag);
     else
-        run_unit<false>(p, p.g[UNIT_DWEIGHT], u, v, smem, s_flag);
+        run_unit<Op::DWEIGHT>(p, p.g[UNIT_DWEIGHT], u, v, smem, s_flag);
+}
+
+// The forward product out = inp . W^T + bias over the same tiles (plan slot
+// UNIT_FWD).
+__global__ __launch_bounds__(NT, 1) void mmb_fwd_bf16_kernel(TilesParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+    int* s_flag = (int*)(smem + 8192);
+    const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
+    run_unit<Op::FWD>(p, p.g[UNIT_FWD], u, v, smem, s_flag);
 }
 
 }  // namespace
@@ -387,6 +424,12 @@ int tiles_bf16_resident() { return (160 * 1024) / LDS_BYTES; }
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s) {
     if (p.n_units <= 0) return hipSuccess;
     hipLaunchKernelGGL(mmb_tiles_bf16_kernel, dim3(p.n_units), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_tiles_bf16(const TilesParams& p, hipStream_t s) {
+    if (p.n_units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mmb_fwd_bf16_kernel, dim3(p.n_units), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

@@ -1,16 +1,19 @@
 """Python binding of libmmb.so (C ABI in include/mmb.h).
 
-Argument marshalling only: every step of the backward pass runs in the HIP
-kernels of the library.  Importing this module loads ``libmmb.so`` from this
-package directory and raises ImportError if it has not been built
+Argument marshalling only: every step of the backward pass (and of the
+forward product) runs in the HIP kernels of the library.  Importing this
+module loads ``libmmb.so`` from this package directory and raises
+ImportError if it has not been built
 (``python -m linear_layer_backward_amd.build``); there is no fallback.
 
 The functions named like the C entry points take raw device addresses
 (ints) or torch tensors (their ``data_ptr()`` is passed) and raise
 ``MmbError`` on a non-zero status, except ``mmb_check_args`` and
-``mmb_path``, which return the status like their C counterparts.
-``backward`` is the tensor-level convenience: it infers B, T, C, OC and the
-dtype from the tensors and enqueues on torch's current stream.
+``mmb_path`` (and their forward twins), which return the status like their
+C counterparts.
+``backward`` and ``forward`` are the tensor-level conveniences: they infer
+B, T, C, OC and the dtype from the tensors and enqueue on torch's current
+stream.
 """
 from __future__ import annotations
 
@@ -51,6 +54,14 @@ _lib.mmb_tile_shape.argtypes = [_i, ctypes.POINTER(_i)]
 _lib.mmb_tile_shape.restype = _i
 _lib.mmb_release.argtypes = []
 _lib.mmb_release.restype = _i
+_FWD_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i]
+for _f in ("mmb_forward", "mmb_forward_check_args", "mmb_forward_path"):
+    getattr(_lib, _f).argtypes = _FWD_ARGS
+    getattr(_lib, _f).restype = _i
+_lib.mmb_forward_stream.argtypes = _FWD_ARGS + [_vp]
+_lib.mmb_forward_stream.restype = _i
+_lib.mmb_forward_plan_units.argtypes = [_i] * 7 + [ctypes.POINTER(_i), ctypes.POINTER(_i), _i]
+_lib.mmb_forward_plan_units.restype = _i
 
 
 class MmbError(RuntimeError):
@@ -97,6 +108,45 @@ def mmb_backward_stream(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dt
                                          B, T, C, OC, dtype), s or None)
     if st != 0:
         raise MmbError(st)
+
+
+def _fwd_args(out, inp, weight, bias, B, T, C, OC, dtype):
+    return (_addr(out), _addr(inp), _addr(weight), _addr(bias), int(B), int(T), int(C),
+            int(OC), int(dtype))
+
+
+def mmb_forward_check_args(out, inp, weight, bias, B, T, C, OC, dtype) -> int:
+    return _lib.mmb_forward_check_args(*_fwd_args(out, inp, weight, bias, B, T, C, OC, dtype))
+
+
+def mmb_forward_path(out, inp, weight, bias, B, T, C, OC, dtype) -> int:
+    return _lib.mmb_forward_path(*_fwd_args(out, inp, weight, bias, B, T, C, OC, dtype))
+
+
+def mmb_forward(out, inp, weight, bias, B, T, C, OC, dtype) -> None:
+    st = _lib.mmb_forward(*_fwd_args(out, inp, weight, bias, B, T, C, OC, dtype))
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_forward_stream(out, inp, weight, bias, B, T, C, OC, dtype, stream) -> None:
+    s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
+    st = _lib.mmb_forward_stream(*_fwd_args(out, inp, weight, bias, B, T, C, OC, dtype),
+                                 s or None)
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_forward_plan_units(B, T, C, OC, dtype, has_bias, num_cus):
+    """(largest split count, list of units) of the forward plan, as
+    mmb_plan_units.  Host only."""
+    sp = (_i * 1)()
+    n = _lib.mmb_forward_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, None, 0)
+    if n < 0:
+        raise MmbError(n)
+    buf = (_i * (8 * n))()
+    _lib.mmb_forward_plan_units(B, T, C, OC, dtype, int(has_bias), num_cus, sp, buf, n)
+    return sp[0], [tuple(buf[8 * k:8 * k + 8]) for k in range(n)]
 
 
 def mmb_release() -> None:
@@ -166,3 +216,33 @@ def backward(dinp, dweight, dbias, dout, inp, weight, B=None, T=None, stream=Non
     with torch.cuda.device(dout.device):
         mmb_backward_stream(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC,
                             torch_dtype_code(dt), stream)
+
+
+def forward(out, inp, weight, bias=None, B=None, T=None, stream=None) -> None:
+    """out = inp . weight^T + bias (assigned).
+
+    Tensors: contiguous, on one GPU, all float32 or all bfloat16.  inp is
+    [B, T, C] (or [B*T, C] with B and T given), weight [OC, C], out B*T*OC
+    elements, bias OC or None.  Enqueued on `stream` (default: torch's
+    current stream of inp's device)."""
+    import torch
+    ts = [out, inp, weight] + ([bias] if bias is not None else [])
+    dt = inp.dtype
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.device != inp.device:
+            raise ValueError("tensors must be contiguous, on one GPU, and share one dtype")
+    if weight.dim() != 2:
+        raise ValueError("weight must be [OC, C]")
+    OC, C = weight.shape
+    if B is None or T is None:
+        if inp.dim() != 3:
+            raise ValueError("give B and T for a 2-D inp")
+        B, T = inp.shape[0], inp.shape[1]
+    if inp.numel() != B * T * C or out.numel() != B * T * OC:
+        raise ValueError("inconsistent shapes")
+    if bias is not None and bias.numel() != OC:
+        raise ValueError("bias must hold OC elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(inp.device)
+    with torch.cuda.device(inp.device):
+        mmb_forward_stream(out, inp, weight, bias, B, T, C, OC, torch_dtype_code(dt), stream)

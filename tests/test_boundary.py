@@ -244,3 +244,110 @@ def test_plan_model_override(mmb, monkeypatch):
     # splitting made ruinous: every partial costs a millisecond of traffic
     monkeypatch.setenv("MMB_PLAN_MODEL", "1.4,1.26,0.72,0.97,0.97,0.8,3.8,8.5,2.1,2.5,4.4,1e-3")
     assert mmb.mmb_plan_units(*shape, 256)[0] == (1, 1)
+
+
+# ---------------------------------------------------------------------------
+# the forward product: out = inp . W^T + bias
+
+def fargs(dtype=1, B=16, T=1024, C=768, OC=3072, bias=True):
+    out, inp, weight, b = addrs(4)
+    return [out, inp, weight, b if bias else None, B, T, C, OC, dtype]
+
+
+def test_header_declares_the_forward_entry_points():
+    names = declared_functions()
+    for f in ("mmb_forward", "mmb_forward_stream", "mmb_forward_check_args", "mmb_forward_path",
+              "mmb_forward_plan_units"):
+        assert f in names
+
+
+def test_forward_valid_arguments(mmb):
+    assert mmb.mmb_forward_check_args(*fargs()) == 0
+    assert mmb.mmb_forward_check_args(*fargs(bias=False)) == 0
+    assert mmb.mmb_forward_check_args(*fargs(dtype=0, B=1, T=1, C=1, OC=1)) == 0
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_forward_null_pointers(mmb, idx):
+    a = fargs()
+    a[idx] = None
+    assert mmb.mmb_forward_check_args(*a) == -1
+
+
+@pytest.mark.parametrize("idx", [4, 5, 6, 7])
+@pytest.mark.parametrize("val", [0, -3])
+def test_forward_bad_dims(mmb, idx, val):
+    a = fargs()
+    a[idx] = val
+    assert mmb.mmb_forward_check_args(*a) == -2
+
+
+def test_forward_bad_dtype_and_overflow(mmb):
+    assert mmb.mmb_forward_check_args(*fargs(dtype=2)) == -3
+    assert mmb.mmb_forward_check_args(*fargs(B=65536, T=32768, C=8, OC=8)) == -4
+    assert mmb.mmb_forward_check_args(*fargs(B=65535, T=32768, C=8, OC=8)) == 0
+
+
+def test_forward_alias(mmb):
+    a = fargs(dtype=0, B=2, T=4, C=8, OC=8)   # fp32: out holds 64 floats = 256 B
+    a[1] = a[0] + 252                          # inp starts inside out
+    assert mmb.mmb_forward_check_args(*a) == -5
+    a[1] = a[0] + 256                          # adjacent
+    assert mmb.mmb_forward_check_args(*a) == 0
+    b = fargs(dtype=1)
+    b[3] = b[0] + 2                            # bias inside out
+    assert mmb.mmb_forward_check_args(*b) == -5
+    c = fargs(dtype=1)
+    c[2] = c[1]                                # inputs may share memory
+    assert mmb.mmb_forward_check_args(*c) == 0
+
+
+def test_forward_path_choice(mmb):
+    assert mmb.mmb_forward_path(*fargs(dtype=1)) == 1
+    assert mmb.mmb_forward_path(*fargs(dtype=1, bias=False)) == 1
+    assert mmb.mmb_forward_path(*fargs(dtype=1, C=764)) == 0
+    assert mmb.mmb_forward_path(*fargs(dtype=0, C=764)) == 1
+    assert mmb.mmb_forward_path(*fargs(dtype=0, OC=3070)) == 0
+    a = fargs(dtype=1)
+    a[3] += 2                                  # the bias is read as 16-byte groups
+    assert mmb.mmb_forward_path(*a) == 0
+    b = fargs(dtype=1)
+    b[0] += 8
+    assert mmb.mmb_forward_path(*b) == 0
+    assert mmb.mmb_forward_path(*fargs(dtype=4)) == -3
+
+
+@pytest.mark.parametrize("shape", [
+    (16, 1024, 768, 3072, 1), (8, 1024, 768, 50304, 1), (16, 1024, 3072, 768, 1),
+    (8, 1024, 768, 2304, 0), (8, 1024, 3072, 768, 0), (2, 16, 64, 192, 0), (1, 1, 8, 8, 1)])
+@pytest.mark.parametrize("cus", [256, 32])
+def test_forward_plan_covers_every_tile_once(mmb, shape, cus):
+    """M = B*T rows, N = OC columns, K = C; every output tile appears with K
+    ranges that partition [0, kiters) in split order."""
+    B, T, C, OC, dt = shape
+    smax, units = mmb.mmb_forward_plan_units(B, T, C, OC, dt, True, cus)
+    BM, BN, BK = mmb.mmb_tile_shape(dt)
+    cd = lambda a, b: -(-a // b)
+    tm, tn, kiters = cd(B * T, BM), cd(OC, BN), cd(C, BK)
+    by_tile = {}
+    for u in units:
+        kind, m, n, s, kt0, kt1, S, slot = u
+        assert kind == 1 and 0 <= m < tm and 0 <= n < tn
+        by_tile.setdefault((m, n), []).append(u)
+    assert len(by_tile) == tm * tn
+    for us in by_tile.values():
+        S = us[0][6]
+        rng = sorted((u[3], u[4], u[5]) for u in us)
+        assert [r[0] for r in rng] == list(range(S))
+        assert rng[0][1] == 0 and rng[-1][2] == kiters
+        assert all(a[2] == b[1] for a, b in zip(rng, rng[1:]))
+    assert smax == max(u[6] for u in units)
+
+
+def test_forward_plan_split_override(mmb, monkeypatch):
+    monkeypatch.setenv("MMB_SPLITS_FWD", "3")
+    smax, units = mmb.mmb_forward_plan_units(2, 150, 264, 400, 1, True, 256)
+    assert smax == 3 and all(u[6] == 3 for u in units)
+    monkeypatch.setenv("MMB_SPLITS_FWD", "2,1,3")
+    smax, units = mmb.mmb_forward_plan_units(2, 150, 264, 400, 1, True, 256)
+    assert smax == 3 and {u[6] for u in units} == {1, 2, 3}

@@ -1,0 +1,226 @@
+"""GPU parity of the forward product out = inp . W^T + bias (the step before
+the backward pass) through the C ABI, against the CPU oracle's forward.
+
+Same bar as the backward pass: max|gpu - oracle| / max|oracle| <= 1e-4 for
+fp32 and <= 2e-2 for bf16; with integer inputs fp32 results equal the oracle
+bit for bit and bf16 results equal the oracle's exact value rounded once to
+nearest-even bf16.  out is filled with NaN before each call: the forward
+assigns it, so no NaN may survive.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from linear_layer_backward_amd import workloads as wl
+from test_parity import TOL, assert_close, from_dev, round_bf16, sample, tile_edges, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from linear_layer_backward_amd import mmb  # noqa: F401  (fails loudly if unbuilt)
+    return torch.device("cuda:0")
+
+
+def make_bias(OC, seed, integer=False):
+    if integer:
+        return np.random.default_rng(seed).integers(-2, 3, size=OC).astype(np.float32)
+    return wl.normal(seed, (OC,), 0.02, "f32")
+
+
+def run_fwd(case, bias, dev, guard=0, stream=None):
+    """out for a workloads.Case's inp and weight (and bias or None); returns
+    [BT, OC] float64 and, with guard > 0, the guarded buffer."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    dt = case.dtype
+    _, x = to_dev(case.inp, dt, dev)
+    _, w = to_dev(case.weight, dt, dev)
+    _, b = (None, None) if bias is None else to_dev(bias, dt, dev)
+    full, out = to_dev(np.full(case.BT * case.OC, np.nan, np.float32), dt, dev, guard)
+    mmb.mmb_forward_stream(out, x, w, b, case.B, case.T, case.C, case.OC,
+                           mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32,
+                           stream if stream is not None else torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    got = from_dev(out, dt).reshape(case.BT, case.OC)
+    return (got, full) if guard else got
+
+
+def oracle_fwd(case, bias, rows=None):
+    x = case.inp if rows is None else case.inp[rows]
+    n = case.BT if rows is None else len(rows)
+    return oracle.forward(x, case.weight, bias, B=1, T=n, C=case.C, OC=case.OC)
+
+
+def check(case, bias, got, exact=False, rows=None):
+    ref = oracle_fwd(case, bias, rows)
+    g = got if rows is None else got[rows]
+    assert not np.any(np.isnan(got)), "out not fully written"
+    if exact:
+        np.testing.assert_array_equal(g, round_bf16(ref) if case.dtype == "bf16" else ref)
+    else:
+        assert_close(g, ref, case.dtype, "out")
+
+
+SMALL = [
+    (2, 16, 64, 192, "f32"), (3, 100, 200, 328, "f32"), (1, 300, 132, 260, "f32"),
+    (2, 150, 264, 400, "bf16"), (1, 513, 200, 136, "bf16"), (1, 1, 8, 8, "bf16"),
+    (1, 1, 4, 4, "f32"),
+    # generic path: C or OC not a multiple of the vector width
+    (2, 7, 65, 129, "f32"), (3, 5, 33, 17, "bf16"), (1, 3, 12, 10, "bf16"),
+]
+
+
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_forward_small_random(dev, shape, bias):
+    B, T, C, OC, dt = shape
+    case = wl.random_case(B, T, C, OC, dt, seed=C + OC)
+    b = make_bias(OC, 7) if bias else None
+    if b is not None:
+        b = wl.from_storage(wl.storage(b, dt), dt)
+    check(case, b, run_fwd(case, b, dev))
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_forward_small_integer_exact(dev, shape):
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=3 + C)
+    b = make_bias(OC, 11, integer=True)
+    check(case, b, run_fwd(case, b, dev), exact=True)
+
+
+@pytest.mark.parametrize("splits", ["2", "3", "5", "2,1,3", "4,2"])
+@pytest.mark.parametrize("shape", [(3, 100, 200, 328, "f32"), (2, 150, 264, 400, "bf16"),
+                                   (1, 300, 520, 264, "bf16")], ids=lambda s: "x".join(map(str, s)))
+def test_forward_forced_splits(dev, monkeypatch, shape, splits):
+    """Split-K forward tiles: partials summed by the last arriver, then the
+    bias epilogue; exact with integer inputs."""
+    monkeypatch.setenv("MMB_SPLITS_FWD", splits)
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=17)
+    b = make_bias(OC, 5, integer=True)
+    check(case, b, run_fwd(case, b, dev), exact=True)
+    check(case, None, run_fwd(case, None, dev), exact=True)
+
+
+@pytest.mark.parametrize("shape", [(2, 150, 264, 400, "bf16"), (3, 100, 200, 328, "f32"),
+                                   (3, 5, 33, 17, "bf16")], ids=lambda s: "x".join(map(str, s)))
+def test_forward_guard_bands(dev, shape):
+    """Nothing outside out is written (canaries on both sides)."""
+    B, T, C, OC, dt = shape
+    case = wl.random_case(B, T, C, OC, dt, seed=2)
+    g = 4096
+    got, full = run_fwd(case, None, dev, guard=g)
+    check(case, None, got)
+    host = from_dev(full, dt)
+    assert np.all(host[:g] == 12288.0) and np.all(host[-g:] == 12288.0)
+
+
+def test_forward_deterministic(dev, monkeypatch):
+    monkeypatch.setenv("MMB_SPLITS_FWD", "3")
+    case = wl.random_case(2, 150, 264, 400, "bf16", seed=4)
+    b = make_bias(400, 3)
+    a = run_fwd(case, b, dev)
+    c = run_fwd(case, b, dev)
+    assert a.tobytes() == c.tobytes()
+
+
+FULL = [  # (B, T, C, OC, dtype, bias): GPT-2 124M layer shapes
+    (16, 1024, 768, 3072, "bf16", True),    # MLP fc
+    (16, 1024, 3072, 768, "bf16", True),    # MLP fc_proj (few tiles: split K)
+    (8, 1024, 768, 50304, "bf16", False),   # LM head
+    (8, 1024, 768, 2304, "f32", True),      # qkv
+    (8, 1024, 3072, 768, "f32", True),      # fc_proj
+]
+
+
+@pytest.mark.parametrize("shape", FULL, ids=lambda s: "x".join(map(str, s[:5])))
+def test_forward_full_shapes_sampled(dev, shape):
+    """Full layer shapes, inputs drawn like the backward workloads
+    (inp N(0,1), weight N(0,0.02), bias N(0,0.02)); sampled rows (tile
+    edges and random ones) against the oracle row by row."""
+    B, T, C, OC, dt, bias = shape
+    BT = B * T
+    inp = wl.normal(500 + C, (BT, C), 1.0, dt)
+    weight = wl.normal(501 + OC, (OC, C), 0.02, dt)
+    b = wl.normal(502, (OC,), 0.02, dt) if bias else None
+    case = wl.Case(name=f"forward {B}x{T}x{C}x{OC} {dt}", B=B, T=T, C=C, OC=OC, dtype=dt,
+                   inp=inp, weight=weight, dout=None, dinp0=None, dweight0=None,
+                   dbias0=None)
+    print(f"[parity] {case.name}", flush=True)
+    got = run_fwd(case, b, dev)
+    rows = sample(BT, tile_edges(BT, 256), 48, seed=OC)
+    check(case, b, got, rows=rows)
+
+
+@pytest.mark.parametrize("shape", [(16, 1024, 768, 3072, "bf16"), (8, 1024, 3072, 768, "f32"),
+                                   (8, 1024, 768, 50304, "bf16")], ids=["fc", "fc_proj", "lm_head"])
+def test_forward_full_shapes_integer_exact(dev, shape):
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=C, prefill=False)
+    b = make_bias(OC, 9, integer=True)
+    print(f"[parity] forward integer {case.name}", flush=True)
+    got = run_fwd(case, b, dev)
+    rows = sample(case.BT, tile_edges(case.BT, 256), 32, seed=1)
+    check(case, b, got, exact=True, rows=rows)
+
+
+def test_forward_backward_adjoint(dev):
+    """The backward pass is the adjoint of the forward product: with integer
+    inputs (fp32, every sum exact) sum(dout * inp.W^T) == sum(inp * ddinp)
+    == sum(W * ddweight), each side computed by the GPU."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    B, T, C, OC = 2, 300, 264, 392
+    case = wl.integer_case(B, T, C, OC, "f32", seed=77, prefill=False)
+    out = run_fwd(case, None, dev)
+    _, dout = to_dev(case.dout, "f32", dev)
+    _, x = to_dev(case.inp, "f32", dev)
+    _, w = to_dev(case.weight, "f32", dev)
+    gi = torch.zeros(case.BT * C, device=dev)
+    gw = torch.zeros(OC * C, device=dev)
+    mmb.mmb_backward_stream(gi, gw, None, dout, x, w, B, T, C, OC, mmb.MMB_FP32,
+                            torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    lhs = int(np.sum(case.dout.astype(np.int64) * out.astype(np.int64)))
+    assert lhs == int(np.sum(case.inp.astype(np.int64).ravel() * gi.cpu().numpy().astype(np.int64)))
+    assert lhs == int(np.sum(case.weight.astype(np.int64).ravel() *
+                             gw.cpu().numpy().astype(np.int64)))
+
+
+def test_forward_tensor_binding(dev):
+    import torch
+    from linear_layer_backward_amd import mmb
+    B, T, C, OC = 2, 64, 128, 256
+    case = wl.random_case(B, T, C, OC, "bf16", seed=6)
+    x = torch.from_numpy(case.inp.reshape(B, T, C)).to(dev).to(torch.bfloat16)
+    w = torch.from_numpy(case.weight).to(dev).to(torch.bfloat16)
+    b = torch.linspace(-1, 1, OC, device=dev).to(torch.bfloat16)
+    out = torch.full((B, T, OC), float("nan"), device=dev, dtype=torch.bfloat16)
+    mmb.forward(out, x, w, b)
+    torch.cuda.synchronize(dev)
+    ref = oracle.forward(x.float().cpu().numpy().reshape(B * T, C), w.float().cpu().numpy(),
+                         b.float().cpu().numpy(), B=B, T=T, C=C, OC=OC)
+    assert_close(out.float().cpu().numpy().reshape(B * T, OC).astype(np.float64), ref, "bf16",
+                 "out")
+    with pytest.raises(ValueError):
+        mmb.forward(out, x, w.float(), b)
+
+
+def test_forward_and_backward_share_the_workspace(dev, monkeypatch):
+    """Split forward and split backward calls alternate on one stream: the
+    shared tile counters and partial buffers stay consistent."""
+    from test_parity import check_exact, run
+    for n in range(3):
+        monkeypatch.setenv("MMB_SPLITS_FWD", str(2 + n))
+        monkeypatch.setenv("MMB_SPLITS_DWEIGHT", str(3 + n))
+        case = wl.integer_case(2, 150, 264, 400, "bf16", seed=90 + n)
+        b = make_bias(400, n, integer=True)
+        check(case, b, run_fwd(case, b, dev), exact=True)
+        check_exact(case, run(case, dev))
+    assert TOL["f32"] == 1e-4
