@@ -1,7 +1,8 @@
 """Benchmark of the linear-layer backward pass (dinp + dweight + dbias) on one
-MI355X.
+MI355X, and (--op forward) of the forward product out = inp.W^T + bias at the
+same layer shapes.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--op backward]
 
 A step is one whole backward pass over the workload (one mmb_backward call;
 two for the MLP pair).  Prints one JSON line: TFLOP/s over the timed steps,
@@ -28,11 +29,29 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "matmul-backward TFLOP/s (dinp+dweight+dbias) at GPT-2 fc shape; % MFMA peak"
+METRIC_FORWARD = "matmul-forward TFLOP/s (inp.W^T + bias) at GPT-2 layer shape; % MFMA peak"
 # MI355X dense peaks (AMD published): bf16 MFMA 2.5 PFLOP/s (256 CUs x 2.4 GHz
 # x 4096 flop/clk/CU = 2516.6 TFLOP/s), fp32 MFMA 157.3 TFLOP/s
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
-# the one kernel a step launches, per compute type
+# the one kernel a step launches, per operation and compute type
 KERNEL_NAME = {"bf16": "mmb_tiles_bf16_kernel", "f32": "mmb_tiles_kernel"}
+KERNEL_NAME_FORWARD = {"bf16": "mmb_fwd_bf16_kernel", "f32": "mmb_fwd_kernel"}
+
+
+def kernel_name(op: str, dtype: str) -> str:
+    return (KERNEL_NAME_FORWARD if op == "forward" else KERNEL_NAME)[dtype]
+
+
+def forward_bias(case):
+    """The forward's bias for a workload case: N(0, 0.02) in the case's dtype
+    (seeded), or None where the layer has no bias (the LM head)."""
+    from linear_layer_backward_amd import workloads as wl
+    return wl.normal(7000 + case.OC, (case.OC,), 0.02, case.dtype) if case.with_bias else None
+
+
+def forward_flops(case) -> int:
+    """2*B*T*C*OC for the product, plus one add per output for the bias."""
+    return 2 * case.BT * case.C * case.OC + (case.BT * case.OC if case.with_bias else 0)
 
 
 def source_digest() -> str:
@@ -74,14 +93,14 @@ def _counter_mean(run_dir: str, counter: str, kernel: str):
     return float(np.mean(vals)), len(vals)
 
 
-def summarize_counters(cfg: int, dirs, copy_mib: int) -> str:
+def summarize_counters(cfg: int, dirs, copy_mib: int, op: str = "backward") -> str:
     """Text summary of two FETCH_SIZE / WRITE_SIZE passes over the workload and
     the same two passes over a plain copy of copy_mib MiB: the copy kernel's
     readings fix the KiB-per-counter-unit scale of each counter."""
     from linear_layer_backward_amd import workloads as wl
     fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
     dtype = "bf16" if cfg >= 4 else "f32"
-    kernel = KERNEL_NAME[dtype]
+    kernel = kernel_name(op, dtype)
     copy_kib = copy_mib * 1024.0
     cf, ncf = _counter_mean(cal_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
     cw, ncw = _counter_mean(cal_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
@@ -91,7 +110,7 @@ def summarize_counters(cfg: int, dirs, copy_mib: int) -> str:
     fetch_b, write_b = kf * sf * 1024, kw * sw * 1024
     lines = [
         f"kernel: {kernel}",
-        f"workload: {wl.CONFIG_NAMES[cfg]}",
+        f"workload: {wl.CONFIG_NAMES[cfg]}" + (" (forward product)" if op == "forward" else ""),
         f"source_digest: {source_digest()}",
         f"copy calibration: {copy_mib} MiB each way; FETCH_SIZE {cf:.1f} ({ncf} dispatches), "
         f"WRITE_SIZE {cw:.1f} ({ncw}); scale fetch {sf:.4f}, write {sw:.4f}",
@@ -115,6 +134,31 @@ def upload(case, dev):
     return dict(dinp=up(case.dinp0), dweight=up(case.dweight0),
                 dbias=up(case.dbias0) if case.with_bias else None,
                 dout=up(case.dout), inp=up(case.inp), weight=up(case.weight))
+
+
+def cpu_baseline_forward(case, bias, target_s: float = 12.0):
+    """The oracle's forward (unchanged) on the first `rows` rows of out,
+    sized from a probe to about target_s seconds."""
+    import oracle
+    x64 = case.inp.astype(np.float64)
+    w64 = case.weight.astype(np.float64)
+    b64 = None if bias is None else bias.astype(np.float64)
+
+    def run(rows):
+        xr = np.ascontiguousarray(x64[:rows])
+        t0 = time.perf_counter()
+        oracle.forward(xr, w64, b64, B=1, T=rows, C=case.C, OC=case.OC)
+        dt = time.perf_counter() - t0
+        return dt, 2 * rows * case.C * case.OC + (rows * case.OC if bias is not None else 0)
+
+    threads = oracle.threads()
+    r0 = max(threads, 16)
+    t, _ = run(r0)
+    rows = int(min(case.BT, r0 * max(1.0, target_s / max(t, 1e-3))))
+    dt, flops = run(rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{case.name}, forward: out rows 0..{rows - 1} of {case.BT}; "
+                      f"fp64 OpenMP, {dt:.1f} s for {flops:.3e} flops"}
 
 
 def cpu_baseline(case, target_s: float = 12.0):
@@ -161,6 +205,8 @@ def main(argv=None):
     # steady clocks: fewer warm-up steps measure the ramp, not the kernel
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--op", default="backward", choices=["backward", "forward"],
+                    help="backward (the metric) or the forward product at the same shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -172,7 +218,7 @@ def main(argv=None):
 
     if args.summarize_counters:
         print(summarize_counters(args.config, args.summarize_counters,
-                                 args.copy_calibration or 256), end="")
+                                 args.copy_calibration or 256, args.op), end="")
         return 0
 
     if args.gpus != 1:
@@ -197,16 +243,29 @@ def main(argv=None):
     from linear_layer_backward_amd import mmb
     from linear_layer_backward_amd import workloads as wl
 
+    fwd = args.op == "forward"
     cases = wl.config_cases(args.config)
-    print(f"[bench] workload: {wl.CONFIG_NAMES[args.config]}", file=sys.stderr, flush=True)
+    print(f"[bench] workload: {wl.CONFIG_NAMES[args.config]}"
+          + (" (forward product)" if fwd else ""), file=sys.stderr, flush=True)
     bufs = [upload(c, dev) for c in cases]
     stream = torch.cuda.current_stream(dev)
     codes = [mmb.MMB_BF16 if c.dtype == "bf16" else mmb.MMB_FP32 for c in cases]
+    biases = [forward_bias(c) for c in cases]
+    if fwd:
+        tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+        for c, b, bias in zip(cases, bufs, biases):
+            b["out"] = torch.empty(c.BT * c.OC, dtype=tdt[c.dtype], device=dev)
+            b["bias"] = (None if bias is None else
+                         torch.from_numpy(np.asarray(bias, np.float32)).to(dev).to(tdt[c.dtype]))
 
     def step():
         for c, b, code in zip(cases, bufs, codes):
-            mmb.mmb_backward_stream(b["dinp"], b["dweight"], b["dbias"], b["dout"], b["inp"],
-                                    b["weight"], c.B, c.T, c.C, c.OC, code, stream)
+            if fwd:
+                mmb.mmb_forward_stream(b["out"], b["inp"], b["weight"], b["bias"], c.B, c.T,
+                                       c.C, c.OC, code, stream)
+            else:
+                mmb.mmb_backward_stream(b["dinp"], b["dweight"], b["dbias"], b["dout"], b["inp"],
+                                        b["weight"], c.B, c.T, c.C, c.OC, code, stream)
 
     for _ in range(args.warmup):
         step()
@@ -239,16 +298,16 @@ def main(argv=None):
     torch.cuda.synchronize(dev)
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    flops = sum(c.flops() for c in cases)
+    flops = sum(forward_flops(c) if fwd else c.flops() for c in cases)
     dtype = cases[0].dtype
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    kernel = KERNEL_NAME[dtype]
+    kernel = kernel_name(args.op, dtype)
     traffic = measured_traffic(kernel, args.config)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FORWARD if fwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -260,7 +319,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl.CONFIG_NAMES[args.config],
+        "config": {"workload": wl.CONFIG_NAMES[args.config] + (" (forward product)" if fwd else ""),
                    "calls": [{"B": c.B, "T": c.T, "C": c.C, "OC": c.OC, "bias": c.with_bias}
                              for c in cases],
                    "flops_per_step": flops},
@@ -272,7 +331,8 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cases[0])
+        out["cpu_baseline"] = (cpu_baseline_forward(cases[0], biases[0]) if fwd
+                               else cpu_baseline(cases[0]))
     print(json.dumps(out), flush=True)
     return 0
 
