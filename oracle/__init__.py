@@ -15,7 +15,9 @@ Every function returns new float64 arrays and never modifies its inputs.
 The dbias and forward output buffers are filled with NaN before the C code
 runs, so a result that added onto the buffer instead of assigning it would
 show.  ``forward`` is the layer's forward product (out = inp . W^T + bias),
-the step before the backward pass.
+the step before the backward pass.  ``backward_sr`` rounds the bf16
+parameter gradients stochastically (Philox-4x64-10 random bits, see
+mmb_oracle.c).
 """
 from __future__ import annotations
 
@@ -73,6 +75,16 @@ class Oracle:
         for f in ("mmb_oracle_dinp", "mmb_oracle_dweight", "mmb_oracle_dbias",
                   "mmb_oracle_backward", "mmb_oracle_forward"):
             getattr(lib, f).restype = None
+        u64 = ctypes.c_uint64
+        lib.mmb_oracle_philox4x64_10.argtypes = [ctypes.POINTER(u64), ctypes.POINTER(u64),
+                                                 ctypes.POINTER(u64)]
+        lib.mmb_oracle_philox4x64_10.restype = None
+        lib.mmb_oracle_sr_bits.argtypes = [u64, u64, u64, u64]
+        lib.mmb_oracle_sr_bits.restype = ctypes.c_uint32
+        lib.mmb_oracle_sr_bf16.argtypes = [ctypes.c_float, ctypes.c_uint32]
+        lib.mmb_oracle_sr_bf16.restype = ctypes.c_uint16
+        lib.mmb_oracle_round_sr.argtypes = [ctypes.POINTER(ctypes.c_uint16), dp, L, L, u64, u64]
+        lib.mmb_oracle_round_sr.restype = None
         lib.mmb_oracle_threads.argtypes = []
         lib.mmb_oracle_threads.restype = ctypes.c_int
         self.lib = lib
@@ -129,6 +141,42 @@ class Oracle:
                                     None if b is None else _ptr(b), B, T, C, OC)
         return out
 
+    def philox(self, ctr, key):
+        """Philox-4x64-10 of a 4-word counter and a 2-word key (ints)."""
+        u64 = ctypes.c_uint64
+        c, k, o = (u64 * 4)(*ctr), (u64 * 2)(*key), (u64 * 4)()
+        self.lib.mmb_oracle_philox4x64_10(c, k, o)
+        return [int(v) for v in o]
+
+    def sr_bits(self, seed, tag, row, col) -> int:
+        """The 16 random bits of element (row, col) of gradient `tag`."""
+        return int(self.lib.mmb_oracle_sr_bits(seed, tag, row, col))
+
+    def sr_bf16(self, x, r16) -> int:
+        """bf16 bits of the float x rounded with random bits r16."""
+        return int(self.lib.mmb_oracle_sr_bf16(float(x), int(r16)))
+
+    def round_sr(self, exact, seed, tag):
+        """Stochastic bf16 rounding (uint16 bits) of a 2-D array of exact
+        values, element (r, c) with its own random bits."""
+        e = np.ascontiguousarray(np.asarray(exact, dtype=np.float64))
+        if e.ndim == 1:
+            e = e.reshape(1, -1)
+        out = np.zeros(e.shape, np.uint16)
+        self.lib.mmb_oracle_round_sr(out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                     _ptr(e), e.shape[0], e.shape[1], seed, tag)
+        return out
+
+    def backward_sr(self, dout, inp, weight, dinp_prefill=None, dweight_prefill=None,
+                    with_bias=True, *, seed, B, T, C, OC):
+        """The bf16 backward pass with stochastic rounding of the parameter
+        gradients: (dinp exact, dweight bf16 bits, dbias bf16 bits or None).
+        dinp is returned exact (it is rounded to nearest on the GPU side)."""
+        gi, gw, gb = self.backward(dout, inp, weight, dinp_prefill, dweight_prefill, with_bias,
+                                   B=B, T=T, C=C, OC=OC)
+        return (gi, self.round_sr(gw, seed, 1),
+                self.round_sr(gb, seed, 2).ravel() if with_bias else None)
+
     def threads(self) -> int:
         """OpenMP threads the parallel loops use."""
         return int(self.lib.mmb_oracle_threads())
@@ -164,6 +212,26 @@ def backward(*a, **k):
 
 def forward(*a, **k):
     return _get().forward(*a, **k)
+
+
+def philox(*a, **k):
+    return _get().philox(*a, **k)
+
+
+def sr_bits(*a, **k):
+    return _get().sr_bits(*a, **k)
+
+
+def sr_bf16(*a, **k):
+    return _get().sr_bf16(*a, **k)
+
+
+def round_sr(*a, **k):
+    return _get().round_sr(*a, **k)
+
+
+def backward_sr(*a, **k):
+    return _get().backward_sr(*a, **k)
 
 
 def threads() -> int:

@@ -21,6 +21,8 @@
  *
  *   out[r,o]     <- sum_{i<C} inp[r,i] * weight[o,i] (+ bias[o])   (written)
  *
+ * plus the stochastic rounding of bf16 gradients described further down.
+ *
  * with r running over the B*T rows.  All tensors are dense row-major:
  * inp [BT,C], dout [BT,OC], weight [OC,C], dinp [BT,C], dweight [OC,C],
  * dbias [OC].  The gradients of dinp and dweight add onto what the buffers
@@ -33,6 +35,8 @@
  * the result does not depend on the thread count.
  */
 #include <stddef.h>
+#include <stdint.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -119,6 +123,84 @@ void mmb_oracle_forward(double* out, const double* inp, const double* weight,
             out[r * OC + o] = bias != NULL ? s + bias[o] : s;
         }
     }
+}
+
+/* ---- stochastic rounding of bf16 gradients ------------------------------
+ *
+ * The llm.c encoder page writes bf16 parameter gradients with stochastic
+ * rounding: the fp32 value  accumulated sum + old value  is rounded up or
+ * down to a neighbouring bf16 at random, with a deterministic seed per
+ * element, so that the rounding is unbiased and runs repeat bit for bit.
+ * The page does not show its hash.  Here the random bits come from
+ * Philox-4x64 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011), keyed by (seed, tag),
+ * tag 1 for dweight and 2 for dbias.  Element (row, col) of a row-major
+ * gradient takes the call with counter (row, 2*(col/32) + (col/4)%2, 0, 0)
+ * and uses bits 16*(col%4) .. 16*(col%4)+15 of output word (col%32)/8: one
+ * call covers 16 elements of a row.  The fp32 value x (the exact result
+ * rounded to nearest fp32) becomes the upper half of  bits(x) + r16:  it
+ * rounds away from zero exactly when the 16 discarded bits plus r16 carry,
+ * i.e. with probability (discarded bits)/65536.  Non-finite values round to
+ * nearest. */
+
+/* Philox-4x64-10: ten rounds of two 64x64->128-bit products with the
+ * published multipliers, the key bumped by the published Weyl constants
+ * between rounds. */
+void mmb_oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; round++) {
+        const unsigned __int128 p0 = (unsigned __int128)M0 * c0;
+        const unsigned __int128 p1 = (unsigned __int128)M1 * c2;
+        const uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        const uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* The 16 random bits of element (row, col) of the gradient `tag`. */
+uint32_t mmb_oracle_sr_bits(uint64_t seed, uint64_t tag, uint64_t row, uint64_t col)
+{
+    const uint64_t ctr[4] = {row, 2 * (col / 32) + (col / 4) % 2, 0, 0};
+    const uint64_t key[2] = {seed, tag};
+    uint64_t w[4];
+    mmb_oracle_philox4x64_10(ctr, key, w);
+    return (uint32_t)((w[(col % 32) / 8] >> (16 * (col % 4))) & 0xFFFF);
+}
+
+/* bf16 bits of x rounded with the random bits r16 (0 <= r16 < 65536). */
+uint16_t mmb_oracle_sr_bf16(float x, uint32_t r16)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u)
+        return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x0040u : 0u));
+    return (uint16_t)((u + r16) >> 16);
+}
+
+/* out[r*cols + c] = stochastic bf16 rounding of exact[r*cols + c] (each value
+ * first rounded to nearest fp32), with the bits of element (r, c) of `tag`. */
+void mmb_oracle_round_sr(uint16_t* out, const double* exact, long rows, long cols,
+                         uint64_t seed, uint64_t tag)
+{
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; r++)
+        for (long c = 0; c < cols; c++)
+            out[r * cols + c] = mmb_oracle_sr_bf16((float)exact[r * cols + c],
+                                                   mmb_oracle_sr_bits(seed, tag, (uint64_t)r,
+                                                                      (uint64_t)c));
 }
 
 /* Number of OpenMP threads a parallel region above would use. */

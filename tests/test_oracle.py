@@ -18,6 +18,10 @@ pass) is pinned by its own hand-worked example (tests/golden/hand_forward.txt),
 by its value at inp = 0 and its exact unit-step differences (it is affine in
 every argument), and by the adjoint identity that ties it to the
 brute-force-pinned backward pass.
+The stochastic rounding of bf16 gradients is pinned by numpy's own
+Philox-4x64-10, an exhaustive count of round-ups over all 65536 random
+values, the element-to-counter mapping checked against numpy, and an
+unbiasedness check.
 """
 import os
 import re
@@ -179,8 +183,85 @@ def pin_forward_adjoint(o):
         assert lhs == float(np.sum(case.weight * gw))
 
 
+def _numpy_philox(ctr, key):
+    """numpy's Philox bit generator is Philox-4x64-10; it advances its
+    counter by one before producing a block, so start one below."""
+    c = list(ctr)
+    assert c[0] >= 1
+    c[0] -= 1
+    bg = np.random.Philox(counter=np.array(c, dtype=np.uint64),
+                          key=np.array(list(key), dtype=np.uint64))
+    return [int(v) for v in bg.random_raw(4)]
+
+
+PHILOX_CASES = [([1, 0, 0, 0], [0, 0]), ([6, 6, 7, 8], [11, 12]),
+                ([2 ** 64 - 1, 2 ** 64 - 1, 2 ** 64 - 1, 2 ** 64 - 1], [2 ** 64 - 1, 2 ** 64 - 1]),
+                ([0x243F6A8885A308D3, 0x13198A2E03707344, 0xA4093822299F31D0, 0x082EFA98EC4E6C89],
+                 [0x452821E638D01377, 0xBE5466CF34E90C6C]),
+                ([12345, 77, 0, 0], [2024, 1]), ([3, 0, 0, 0], [0, 2])]
+
+
+def pin_philox_numpy(o):
+    """The oracle's Philox-4x64-10 equals numpy's implementation of the
+    published generator on counters and keys that exercise every word."""
+    for ctr, key in PHILOX_CASES:
+        assert o.philox(ctr, key) == _numpy_philox(ctr, key), (ctr, key)
+
+
+def pin_sr_mapping(o):
+    """Element (row, col) of gradient `tag` takes bits 16*(col%4).. of word
+    (col%32)//8 of the block with counter (row, 2*(col//32) + (col//4)%2),
+    key (seed, tag); checked against numpy's generator."""
+    rng = np.random.default_rng(5)
+    for _ in range(24):
+        seed, tag = int(rng.integers(0, 2 ** 63)), int(rng.integers(1, 3))
+        row, col = int(rng.integers(1, 5000)), int(rng.integers(0, 4000))
+        w = _numpy_philox([row, 2 * (col // 32) + (col // 4) % 2, 0, 0], [seed, tag])
+        assert o.sr_bits(seed, tag, row, col) == (w[(col % 32) // 8] >> (16 * (col % 4))) & 0xFFFF
+
+
+def _f32_bits(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+def pin_sr_closed_form(o):
+    """Rounding with r16 over all 65536 values: a value that bf16 holds
+    exactly never moves; otherwise the result is the lower neighbour (the
+    truncation) or the upper one, the upper exactly d times where d is the
+    value of the 16 discarded bits; the sign never changes the magnitude."""
+    for x in (1.0, -3.5, 2.0 ** -20, 0.0):
+        b = _f32_bits(x) >> 16
+        assert all(o.sr_bf16(x, r) == b for r in (0, 1, 0x7FFF, 0x8000, 0xFFFF))
+    for x in (1.0 + 2.0 ** -9, -(1.0 + 3 * 2.0 ** -12), 257.0, 3.0e-5, -1234.567):
+        u = _f32_bits(x)
+        lo, d = u >> 16, u & 0xFFFF
+        got = [o.sr_bf16(x, r) for r in range(0, 65536, 1)]
+        assert set(got) <= {lo, lo + 1}
+        assert got.count(lo + 1) == d
+        assert o.sr_bf16(-x, 0x9000) == o.sr_bf16(x, 0x9000) ^ 0x8000
+
+
+def pin_sr_round_array(o):
+    """round_sr rounds each exact value to nearest fp32 first, then with the
+    element's own bits; a constant array between two bf16 neighbours is
+    rounded without bias (mean within 4 standard deviations)."""
+    exact = np.array([[1.0 + 2.0 ** -9 + 2.0 ** -40, -257.0, 5.0]])
+    bits = o.round_sr(exact, 99, 1)
+    for c in range(3):
+        assert bits[0, c] == o.sr_bf16(np.float32(exact[0, c]), o.sr_bits(99, 1, 0, c))
+    x = 1.0 + 2.0 ** -9           # a quarter of the way from 1 to 1 + 2^-7
+    rows, cols = 64, 512
+    b = o.round_sr(np.full((rows, cols), x), 7, 1).astype(np.uint32) << 16
+    vals = b.view(np.float32).astype(np.float64)
+    assert set(np.unique(vals)) <= {1.0, 1.0 + 2.0 ** -7}
+    p_up = np.mean(vals > 1.0)
+    sd = np.sqrt(0.25 * 0.75 / vals.size)
+    assert abs(p_up - 0.25) < 4 * sd, p_up
+
+
 PINS = [pin_hand_example, pin_brute_force, pin_dbias_overwrites,
-        pin_forward_hand_example, pin_forward_affine, pin_forward_adjoint]
+        pin_forward_hand_example, pin_forward_affine, pin_forward_adjoint,
+        pin_philox_numpy, pin_sr_mapping, pin_sr_closed_form, pin_sr_round_array]
 
 
 # ---------------------------------------------------------------------------
@@ -242,6 +323,43 @@ def test_forward_affine(o):
 
 def test_forward_adjoint(o):
     pin_forward_adjoint(o)
+
+
+def test_philox_matches_numpy(o):
+    pin_philox_numpy(o)
+
+
+def test_sr_bits_mapping(o):
+    pin_sr_mapping(o)
+
+
+def test_sr_closed_form(o):
+    pin_sr_closed_form(o)
+
+
+def test_sr_round_array(o):
+    pin_sr_round_array(o)
+
+
+def test_backward_sr_integer(o):
+    """Integer inputs: dinp exact as in backward(); dweight and dbias bits
+    are the stochastic rounding of the exact sums (which exceed bf16's 8-bit
+    mantissa), each one of the two bf16 neighbours of the exact value."""
+    B, T, C, OC = 2, 400, 24, 16
+    c = wl.integer_case(B, T, C, OC, seed=61, lo=-5, hi=5)
+    kw = dict(B=B, T=T, C=C, OC=OC)
+    ri, rw, rb = o.backward(c.dout, c.inp, c.weight, c.dinp0, c.dweight0, True, **kw)
+    gi, gw, gb = o.backward_sr(c.dout, c.inp, c.weight, c.dinp0, c.dweight0, True, seed=5, **kw)
+    np.testing.assert_array_equal(gi, ri)
+    for bits, exact in ((gw, rw), (gb, rb)):
+        v = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        lo = ((exact.astype(np.float32).view(np.uint32) >> 16) << 16).view(np.float32)
+        hi_mag = ((exact.astype(np.float32).view(np.uint32) >> 16) + 1) << 16
+        hi = hi_mag.astype(np.uint32).view(np.float32)
+        assert np.all((v == lo) | (v == hi))
+    assert np.mean(np.abs(rw) > 256) > 0.3     # most sums need rounding
+    assert np.any(gw != o.backward_sr(c.dout, c.inp, c.weight, c.dinp0, c.dweight0, True,
+                                      seed=6, **kw)[1])
 
 
 @pytest.mark.parametrize("shape", [(2, 16, 64, 192), (3, 7, 33, 65), (1, 1, 8, 1)])
@@ -434,6 +552,15 @@ MUTATIONS = [
      "out[r * OC + o] = bias", "out[r * OC + o] += bias"),
     ("forward written transposed",
      "out[r * OC + o] = bias", "out[o * BT + r] = bias"),
+    ("philox wrong multiplier", "0xCA5A826395121157ULL", "0xCA5A826395121155ULL"),
+    ("philox wrong Weyl constant", "W1 = 0xBB67AE8584CAA73BULL", "W1 = 0xBB67AE8584CAA73AULL"),
+    ("philox nine rounds", "round < 10", "round < 9"),
+    ("philox mixes the wrong word", "c0 = hi1 ^ c1 ^ k0;", "c0 = hi1 ^ c3 ^ k0;"),
+    ("sr bits from the wrong word", "w[(col % 32) / 8]", "w[(col % 16) / 4]"),
+    ("sr counter ignores the half", "2 * (col / 32) + (col / 4) % 2", "2 * (col / 32)"),
+    ("sr truncates", "return (uint16_t)((u + r16) >> 16);", "return (uint16_t)(u >> 16);"),
+    ("sr rounds on the wrong bits", "return (uint16_t)((u + r16) >> 16);",
+     "return (uint16_t)((u + (r16 >> 1)) >> 16);"),
 ]
 
 
