@@ -30,16 +30,20 @@ if ROOT not in sys.path:
 
 METRIC = "matmul-backward TFLOP/s (dinp+dweight+dbias) at GPT-2 fc shape; % MFMA peak"
 METRIC_FORWARD = "matmul-forward TFLOP/s (inp.W^T + bias) at GPT-2 layer shape; % MFMA peak"
+METRIC_SR = ("matmul-backward TFLOP/s (dinp+dweight+dbias, bf16 dweight/dbias stochastically "
+             "rounded) at GPT-2 layer shape; % MFMA peak")
 # MI355X dense peaks (AMD published): bf16 MFMA 2.5 PFLOP/s (256 CUs x 2.4 GHz
 # x 4096 flop/clk/CU = 2516.6 TFLOP/s), fp32 MFMA 157.3 TFLOP/s
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 # the one kernel a step launches, per operation and compute type
 KERNEL_NAME = {"bf16": "mmb_tiles_bf16_kernel", "f32": "mmb_tiles_kernel"}
 KERNEL_NAME_FORWARD = {"bf16": "mmb_fwd_bf16_kernel", "f32": "mmb_fwd_kernel"}
+KERNEL_NAME_SR = {"bf16": "mmb_tiles_bf16_sr_kernel"}
 
 
 def kernel_name(op: str, dtype: str) -> str:
-    return (KERNEL_NAME_FORWARD if op == "forward" else KERNEL_NAME)[dtype]
+    table = {"forward": KERNEL_NAME_FORWARD, "backward_sr": KERNEL_NAME_SR}.get(op, KERNEL_NAME)
+    return table[dtype]
 
 
 def forward_bias(case):
@@ -205,8 +209,9 @@ def main(argv=None):
     # steady clocks: fewer warm-up steps measure the ramp, not the kernel
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--op", default="backward", choices=["backward", "forward"],
-                    help="backward (the metric) or the forward product at the same shapes")
+    ap.add_argument("--op", default="backward", choices=["backward", "forward", "backward_sr"],
+                    help="backward (the metric), the forward product at the same shapes, or the "
+                         "bf16 backward with stochastically rounded dweight/dbias")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -244,7 +249,11 @@ def main(argv=None):
     from linear_layer_backward_amd import workloads as wl
 
     fwd = args.op == "forward"
+    sr = args.op == "backward_sr"
     cases = wl.config_cases(args.config)
+    if sr and cases[0].dtype != "bf16":
+        print("--op backward_sr needs a bf16 workload (--config 4 or 5)", file=sys.stderr)
+        return 2
     print(f"[bench] workload: {wl.CONFIG_NAMES[args.config]}"
           + (" (forward product)" if fwd else ""), file=sys.stderr, flush=True)
     bufs = [upload(c, dev) for c in cases]
@@ -263,6 +272,9 @@ def main(argv=None):
             if fwd:
                 mmb.mmb_forward_stream(b["out"], b["inp"], b["weight"], b["bias"], c.B, c.T,
                                        c.C, c.OC, code, stream)
+            elif sr:
+                mmb.mmb_backward_sr(b["dinp"], b["dweight"], b["dbias"], b["dout"], b["inp"],
+                                    b["weight"], c.B, c.T, c.C, c.OC, 1234, stream)
             else:
                 mmb.mmb_backward_stream(b["dinp"], b["dweight"], b["dbias"], b["dout"], b["inp"],
                                         b["weight"], c.B, c.T, c.C, c.OC, code, stream)
@@ -307,7 +319,7 @@ def main(argv=None):
     traffic = measured_traffic(kernel, args.config)
 
     out = {
-        "metric": METRIC_FORWARD if fwd else METRIC,
+        "metric": METRIC_FORWARD if fwd else (METRIC_SR if sr else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -319,7 +331,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl.CONFIG_NAMES[args.config] + (" (forward product)" if fwd else ""),
+        "config": {"workload": wl.CONFIG_NAMES[args.config] + (" (forward product)" if fwd else "")
+                   + (" (stochastic rounding)" if sr else ""),
                    "calls": [{"B": c.B, "T": c.T, "C": c.C, "OC": c.OC, "bias": c.with_bias}
                              for c in cases],
                    "flops_per_step": flops},

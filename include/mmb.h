@@ -80,6 +80,25 @@ int mmb_backward_stream(void* dinp, void* dweight, void* dbias,
                         const void* dout, const void* inp, const void* weight,
                         int B, int T, int C, int OC, int dtype, void* stream);
 
+/* The bf16 backward pass with stochastic rounding of the parameter
+ * gradients (the llm.c encoder page writes its bf16 gradients this way, with
+ * a deterministic seed per element).  Tensors, layout, ownership, errors and
+ * streams as mmb_backward_stream with dtype MMB_BF16 (there is no dtype
+ * argument: fp32 needs no rounding).  dinp is rounded to nearest as in
+ * mmb_backward.  dweight[o,i] and dbias[o] take the fp32 value (old + sum for
+ * dweight, the sum for dbias) to one of its two bf16 neighbours: with d the
+ * 16 bits below the bf16 mantissa and r16 the element's random bits, the
+ * result is the upper half of bits(value) + r16, so it moves away from zero
+ * with probability d/65536 (unbiased).  r16 comes from Philox-4x64-10
+ * (Salmon et al., SC 2011) keyed by (seed, tag), tag 1 for dweight and 2 for
+ * dbias: element (row, col) (dbias: row 0, col o) uses bits 16*(col%4) ..
+ * 16*(col%4)+15 of word (col%32)/8 of the block with counter
+ * (row, 2*(col/32) + (col/4)%2, 0, 0).  The same seed gives the same bits on
+ * every run and every split plan; non-finite values round to nearest. */
+int mmb_backward_sr(void* dinp, void* dweight, void* dbias,
+                    const void* dout, const void* inp, const void* weight,
+                    int B, int T, int C, int OC, unsigned long long seed, void* stream);
+
 /* Host-only validation of an argument set, exactly the checks that
  * mmb_backward performs before touching the GPU.  Makes no HIP call. */
 int mmb_check_args(const void* dinp, const void* dweight, const void* dbias,

@@ -650,14 +650,16 @@ int get_workspace(int dev, hipStream_t s, const Plan& p, TilesParams* tp) {
     return MMB_OK;
 }
 
+// sr: bf16 only; dweight and dbias rounded stochastically under `seed`.
 int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
-                  const void* weight, int B, int T, int C, int OC, int dtype, hipStream_t s) {
+                  const void* weight, int B, int T, int C, int OC, int dtype, hipStream_t s,
+                  bool sr = false, unsigned long long seed = 0) {
     int st = check(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
     const int BT = B * T;
     if (!choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype)) {
-        return launch_generic(dtype, dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s) ==
-                       hipSuccess
+        return launch_generic(dtype, dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s, sr,
+                              seed) == hipSuccess
                    ? MMB_OK
                    : MMB_ERR_HIP;
     }
@@ -676,7 +678,9 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     tp.dout = dout;
     tp.inp = inp;
     tp.weight = weight;
-    return launch_tiles(dtype, tp, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+    tp.seed = seed;
+    const hipError_t e = sr ? launch_tiles_bf16_sr(tp, s) : launch_tiles(dtype, tp, s);
+    return e == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }
 
 int forward_impl(void* out, const void* inp, const void* weight, const void* bias, int B, int T,
@@ -748,6 +752,13 @@ int mmb_backward_stream(void* dinp, void* dweight, void* dbias, const void* dout
                         int dtype, void* stream) {
     return mmb::backward_impl(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype,
                               (hipStream_t)stream);
+}
+
+int mmb_backward_sr(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
+                    const void* weight, int B, int T, int C, int OC, unsigned long long seed,
+                    void* stream) {
+    return mmb::backward_impl(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, MMB_BF16,
+                              (hipStream_t)stream, true, seed);
 }
 
 int mmb_backward(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,

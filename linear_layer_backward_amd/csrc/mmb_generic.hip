@@ -34,12 +34,13 @@ __global__ __launch_bounds__(kBlock) void generic_dinp(T* __restrict__ dinp,
 }
 
 // dweight[o,i] = old + sum_r dout[r,o] * inp[r,i]; block = one channel o and
-// 256 consecutive i.
-template <typename T>
+// 256 consecutive i.  SR: bf16 stochastic rounding (element (o0 + o, i), tag 1).
+template <typename T, bool SR = false>
 __global__ __launch_bounds__(kBlock) void generic_dweight(T* __restrict__ dweight,
                                                           const T* __restrict__ dout,
                                                           const T* __restrict__ inp,
-                                                          int BT, int C, int OC) {
+                                                          int BT, int C, int OC, long long o0 = 0,
+                                                          unsigned long long seed = 0) {
     const long long o = blockIdx.y;
     const int i = blockIdx.x * kBlock + threadIdx.x;
     if (i >= C) return;
@@ -47,19 +48,26 @@ __global__ __launch_bounds__(kBlock) void generic_dweight(T* __restrict__ dweigh
     for (long long r = 0; r < BT; ++r)
         acc = fmaf(to_f32(dout[r * OC + o]), to_f32(inp[r * C + i]), acc);
     T* out = dweight + o * C + i;
-    *out = from_f32<T>(to_f32(*out) + acc);
+    if constexpr (SR)
+        *out = T{(uint16_t)sr_bf16_element(to_f32(*out) + acc, seed, 1, (uint64_t)(o0 + o),
+                                           (uint64_t)i)};
+    else
+        *out = from_f32<T>(to_f32(*out) + acc);
 }
 
 // dbias[o] = sum_r dout[r,o]: one thread per channel, reads coalesce along o.
-template <typename T>
+template <typename T, bool SR = false>
 __global__ __launch_bounds__(kBlock) void generic_dbias(T* __restrict__ dbias,
                                                         const T* __restrict__ dout,
-                                                        int BT, int OC) {
+                                                        int BT, int OC, unsigned long long seed = 0) {
     const int o = blockIdx.x * kBlock + threadIdx.x;
     if (o >= OC) return;
     float acc = 0.f;
     for (long long r = 0; r < BT; ++r) acc += to_f32(dout[r * OC + o]);
-    dbias[o] = from_f32<T>(acc);
+    if constexpr (SR)
+        dbias[o] = T{(uint16_t)sr_bf16_element(acc, seed, 2, 0, (uint64_t)o)};
+    else
+        dbias[o] = from_f32<T>(acc);
 }
 
 // Forward: out[r,o] = sum_i inp[r,i] * weight[o,i] (+ bias[o]), assigned;
@@ -95,10 +103,10 @@ hipError_t launch_forward(void* out, const void* inp, const void* weight, const 
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SR = false>
 hipError_t launch(void* dinp, void* dweight, void* dbias, const void* dout,
                   const void* inp, const void* weight, int BT, int C, int OC,
-                  hipStream_t s) {
+                  hipStream_t s, unsigned long long seed = 0) {
     const dim3 block(kBlock);
     const unsigned gx = (unsigned)((C + kBlock - 1) / kBlock);
     // grid.y is limited to 65535 by the hardware dispatcher: chunk the rows
@@ -111,13 +119,13 @@ hipError_t launch(void* dinp, void* dweight, void* dbias, const void* dout,
     }
     for (int o0 = 0; o0 < OC; o0 += kRowsPerLaunch) {
         const int rows = OC - o0 < kRowsPerLaunch ? OC - o0 : kRowsPerLaunch;
-        hipLaunchKernelGGL(generic_dweight<T>, dim3(gx, rows), block, 0, s,
+        hipLaunchKernelGGL((generic_dweight<T, SR>), dim3(gx, rows), block, 0, s,
                            (T*)dweight + (long long)o0 * C, (const T*)dout + o0,
-                           (const T*)inp, BT, C, OC);
+                           (const T*)inp, BT, C, OC, (long long)o0, seed);
     }
     if (dbias != nullptr)
-        hipLaunchKernelGGL(generic_dbias<T>, dim3((OC + kBlock - 1) / kBlock), block, 0, s,
-                           (T*)dbias, (const T*)dout, BT, OC);
+        hipLaunchKernelGGL((generic_dbias<T, SR>), dim3((OC + kBlock - 1) / kBlock), block, 0, s,
+                           (T*)dbias, (const T*)dout, BT, OC, seed);
     return hipGetLastError();
 }
 
@@ -125,8 +133,11 @@ hipError_t launch(void* dinp, void* dweight, void* dbias, const void* dout,
 
 hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
                           const void* dout, const void* inp, const void* weight,
-                          int BT, int C, int OC, hipStream_t s) {
+                          int BT, int C, int OC, hipStream_t s, bool sr,
+                          unsigned long long seed) {
     if (dtype == 0) return launch<float>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s);
+    if (sr)
+        return launch<bf16_t, true>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s, seed);
     return launch<bf16_t>(dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s);
 }
 

@@ -44,6 +44,7 @@ struct TilesParams {
     int* counters;        // one arrival counter per tile, zero at rest
     void* out;            // forward launch: out [BT,OC]
     const void* bias;     // forward launch: bias [OC], may be NULL
+    unsigned long long seed;  // stochastic-rounding launch: Philox key word 0
 };
 
 // Tile shapes of the MFMA kernels (rows x cols of the output tile, K depth of
@@ -54,6 +55,8 @@ TileShape tile_shape(int dtype);
 // Launchers (return hipError_t of the launch).
 hipError_t launch_tiles(int dtype, const TilesParams& p, hipStream_t s);
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s);
+// bf16 backward with stochastically rounded dweight and dbias (seed in p)
+hipError_t launch_tiles_bf16_sr(const TilesParams& p, hipStream_t s);
 int tiles_bf16_bk();   // K depth of one stage of the bf16 tiles
 int tiles_bf16_bn();   // output columns of one bf16 tile
 // Workgroups of the MFMA tile kernel for `dtype` that fit on one CU at once
@@ -66,8 +69,10 @@ hipError_t launch_fwd_tiles(int dtype, const TilesParams& p, hipStream_t s);
 hipError_t launch_fwd_tiles_bf16(const TilesParams& p, hipStream_t s);
 hipError_t launch_fwd_generic(int dtype, void* out, const void* inp, const void* weight,
                               const void* bias, int BT, int C, int OC, hipStream_t s);
+// sr: bf16 only, dweight and dbias stochastically rounded under `seed`
 hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
                           const void* dout, const void* inp, const void* weight,
-                          int BT, int C, int OC, hipStream_t s);
+                          int BT, int C, int OC, hipStream_t s, bool sr = false,
+                          unsigned long long seed = 0);
 
 }  // namespace mmb

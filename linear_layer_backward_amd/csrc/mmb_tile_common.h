@@ -89,6 +89,23 @@ __device__ __forceinline__ void add_round_store(char* pos, const f32x4& v, bf16_
     *(u32x2*)pos = w;
 }
 
+// bf16 with stochastic rounding: the 4 values take bits 0..15, 16..31, ...
+// of `bits` (one word of the element block, see sr_block).
+__device__ __forceinline__ void add_round_store_sr(char* pos, const f32x4& v, uint64_t bits) {
+    const u32x2 old = *(const u32x2*)pos;
+    f32x4 o = v;
+    o[0] += __uint_as_float(old[0] << 16);
+    o[1] += __uint_as_float(old[0] & 0xffff0000u);
+    o[2] += __uint_as_float(old[1] << 16);
+    o[3] += __uint_as_float(old[1] & 0xffff0000u);
+    u32x2 w;
+    w[0] = sr_bf16_bits(o[0], (uint32_t)bits & 0xFFFFu) |
+           (sr_bf16_bits(o[1], (uint32_t)(bits >> 16) & 0xFFFFu) << 16);
+    w[1] = sr_bf16_bits(o[2], (uint32_t)(bits >> 32) & 0xFFFFu) |
+           (sr_bf16_bits(o[3], (uint32_t)(bits >> 48) & 0xFFFFu) << 16);
+    *(u32x2*)pos = w;
+}
+
 // Global 16-byte offsets of the epilogue's row-contiguous passes: thread tid
 // moves group tid % CHUNKS of row tid / CHUNKS + ROWS_PER_PASS * i in pass i.
 // Offsets are relative to out_rsrc(); rows >= M and groups >= N are masked.
@@ -116,11 +133,14 @@ __device__ __forceinline__ uint32_t out_off(long long ldd, int M, int N, int m0,
 // Second half of the epilogue, once LDS holds the base tile (the old output,
 // or the bias rows) and a barrier has published it: every lane adds its
 // accumulators at its fragment positions and rounds once in place, then the
-// tile goes out row-contiguously.
-template <typename T, int MB, int NB, int NT, int BM, int BN>
+// tile goes out row-contiguously.  SR: stochastic rounding to bf16 with the
+// elements' Philox bits under (seed, tag) instead of round to nearest.
+template <typename T, int MB, int NB, int NT, int BM, int BN, bool SR = false>
 __device__ __forceinline__ void add_round_write(T* D, long long ldd, int M, int N, int m0, int n0,
                                                 const f32x16 (&acc)[MB][NB], char* smem, int tid,
-                                                int lane, int wm0, int wn0) {
+                                                int lane, int wm0, int wn0, uint64_t seed = 0,
+                                                uint64_t tag = 0) {
+    static_assert(!SR || sizeof(T) == 2, "stochastic rounding is for bf16 outputs");
     typedef OutMap<T, NT, BM, BN> OM;
     constexpr int PITCH = out_pitch<T, BM, BN>();
     const auto r = out_rsrc(D, ldd, M, m0, n0);
@@ -129,14 +149,22 @@ __device__ __forceinline__ void add_round_write(T* D, long long ldd, int M, int 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb) {
+            uint64_t bits[4] = {0, 0, 0, 0};
+            if constexpr (SR)
+                sr_block(seed, tag, (uint64_t)(m0 + wm0 + mb * 32 + lr),
+                         (uint64_t)(n0 + wn0 + nb * 32 + 4 * half), bits);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = wm0 + mb * 32 + lr, col = wn0 + nb * 32 + 8 * q + 4 * half;
                 const f32x4 a = {acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2],
                                  acc[mb][nb][4 * q + 3]};
-                add_round_store(smem + row * PITCH + (int)sizeof(T) * col, a, T{});
+                if constexpr (SR)
+                    add_round_store_sr(smem + row * PITCH + (int)sizeof(T) * col, a, bits[q]);
+                else
+                    add_round_store(smem + row * PITCH + (int)sizeof(T) * col, a, T{});
             }
+        }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < OM::PASSES; ++i) {
@@ -149,11 +177,12 @@ __device__ __forceinline__ void add_round_write(T* D, long long ldd, int M, int 
 // beta = 1: D = old + acc.  With PRE > 0, passes 0 .. PRE-1 of the old tile
 // were already loaded by the caller (pre[i], loaded from out_rsrc() at
 // out_off(.., i)).
-template <typename T, int MB, int NB, int NT, int BM, int BN, int PRE = 0>
+template <typename T, int MB, int NB, int NT, int BM, int BN, int PRE = 0, bool SR = false>
 __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N, int m0, int n0,
                                                const f32x16 (&acc)[MB][NB], char* smem, int tid,
                                                int lane, int wm0, int wn0,
-                                               const u32x4* pre = nullptr) {
+                                               const u32x4* pre = nullptr, uint64_t seed = 0,
+                                               uint64_t tag = 0) {
     typedef OutMap<T, NT, BM, BN> OM;
     constexpr int PITCH = out_pitch<T, BM, BN>();
     constexpr int PASSES = OM::PASSES;
@@ -174,7 +203,8 @@ __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N
     for (int i = PRE; i < PASSES; ++i)
         *(u32x4*)(smem + (row0 + OM::ROWS_PER_PASS * i) * PITCH + 16 * ch) = v[i];
     __syncthreads();
-    add_round_write<T, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
+    add_round_write<T, MB, NB, NT, BM, BN, SR>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0,
+                                               seed, tag);
 }
 
 // beta = 0 with a bias row (the forward product): D[m, n] = acc + bias[n],

@@ -133,9 +133,12 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* region, int xb, int s, int
 // (FWD: out = inp . W^T, the forward product whose gradients the other two are.)
 enum class Op { DINP, DWEIGHT, FWD };
 
-template <Op OP>
+// SR: the output (dweight) and dbias are rounded stochastically (Philox bits
+// under p.seed, tags 1 and 2) instead of to nearest.
+template <Op OP, bool SR = false>
 __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g, int4 u, int4 v,
                                          char* smem, int* s_flag) {
+    static_assert(!SR || OP == Op::DWEIGHT, "stochastic rounding is for the parameter gradients");
     constexpr bool AK = OP != Op::DWEIGHT;   // A rows K-contiguous (dout rows, inp rows)
     constexpr bool BKC = OP == Op::FWD;      // B rows K-contiguous (weight rows)
     constexpr bool BETA1 = OP != Op::FWD;    // gradients accumulate; the forward assigns
@@ -371,8 +374,8 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         if (do_bias && tid < BM) bias = sum_bias(wb, splits, BM);
         if (tid == 0) p.counters[g.tile_base + tile] = 0;
         if constexpr (BETA1)
-            write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
-                                                       wm0, wn0);
+            write_tile_lds<bf16_t, MB, NB, NT, BM, BN, 0, SR>(D, ldd, M, N, m0, n0, acc, smem, tid,
+                                                              lane, wm0, wn0, nullptr, p.seed, 1);
         else
             write_tile_bias<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
                                                         wm0, wn0, (const bf16_t*)p.bias);
@@ -384,13 +387,19 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         static_assert(LOADS == 4, "the old tile's first 8 passes sit in the 4 staging pairs");
         const u32x4 pre[2 * LOADS] = {stg_a[0], stg_b[0], stg_a[1], stg_b[1],
                                       stg_a[2], stg_b[2], stg_a[3], stg_b[3]};
-        write_tile_lds<bf16_t, MB, NB, NT, BM, BN, 2 * LOADS>(D, ldd, M, N, m0, n0, acc, smem, tid,
-                                                               lane, wm0, wn0, pre);
+        write_tile_lds<bf16_t, MB, NB, NT, BM, BN, 2 * LOADS, SR>(D, ldd, M, N, m0, n0, acc, smem,
+                                                                   tid, lane, wm0, wn0, pre, p.seed, 1);
     } else {
-        write_tile_lds<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0,
-                                                   wn0);
+        write_tile_lds<bf16_t, MB, NB, NT, BM, BN, 0, SR>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
+                                                          wm0, wn0, nullptr, p.seed, 1);
     }
-    if (do_bias && tid < BM && m0 + tid < M) ((bf16_t*)p.dbias)[m0 + tid] = from_f32<bf16_t>(bias);
+    if (do_bias && tid < BM && m0 + tid < M) {
+        if constexpr (SR)
+            ((bf16_t*)p.dbias)[m0 + tid] =
+                bf16_t{(uint16_t)sr_bf16_element(bias, p.seed, 2, 0, (uint64_t)(m0 + tid))};
+        else
+            ((bf16_t*)p.dbias)[m0 + tid] = from_f32<bf16_t>(bias);
+    }
 }
 
 __global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
@@ -403,6 +412,18 @@ __global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_kernel(TilesParams p) {
         run_unit<Op::DINP>(p, p.g[UNIT_DINP], u, v, smem, s_flag);
     else
         run_unit<Op::DWEIGHT>(p, p.g[UNIT_DWEIGHT], u, v, smem, s_flag);
+}
+
+// The same launch with stochastically rounded dweight and dbias (dinp is
+// still rounded to nearest).
+__global__ __launch_bounds__(NT, 1) void mmb_tiles_bf16_sr_kernel(TilesParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+    int* s_flag = (int*)(smem + 8192);
+    const int4 u = p.units[2 * blockIdx.x], v = p.units[2 * blockIdx.x + 1];
+    if (u.x == UNIT_DINP)
+        run_unit<Op::DINP>(p, p.g[UNIT_DINP], u, v, smem, s_flag);
+    else
+        run_unit<Op::DWEIGHT, true>(p, p.g[UNIT_DWEIGHT], u, v, smem, s_flag);
 }
 
 // The forward product out = inp . W^T + bias over the same tiles (plan slot
@@ -424,6 +445,12 @@ int tiles_bf16_resident() { return (160 * 1024) / LDS_BYTES; }
 hipError_t launch_tiles_bf16(const TilesParams& p, hipStream_t s) {
     if (p.n_units <= 0) return hipSuccess;
     hipLaunchKernelGGL(mmb_tiles_bf16_kernel, dim3(p.n_units), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiles_bf16_sr(const TilesParams& p, hipStream_t s) {
+    if (p.n_units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mmb_tiles_bf16_sr_kernel, dim3(p.n_units), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@ _lib.mmb_tile_shape.argtypes = [_i, ctypes.POINTER(_i)]
 _lib.mmb_tile_shape.restype = _i
 _lib.mmb_release.argtypes = []
 _lib.mmb_release.restype = _i
+_lib.mmb_backward_sr.argtypes = [_vp] * 6 + [_i] * 4 + [ctypes.c_ulonglong, _vp]
+_lib.mmb_backward_sr.restype = _i
 _FWD_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i]
 for _f in ("mmb_forward", "mmb_forward_check_args", "mmb_forward_path"):
     getattr(_lib, _f).argtypes = _FWD_ARGS
@@ -106,6 +108,16 @@ def mmb_backward_stream(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dt
     s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
     st = _lib.mmb_backward_stream(*_args(dinp, dweight, dbias, dout, inp, weight,
                                          B, T, C, OC, dtype), s or None)
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_backward_sr(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, seed,
+                    stream) -> None:
+    """bf16 backward with stochastically rounded dweight and dbias."""
+    s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
+    a = _args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, MMB_BF16)[:10]
+    st = _lib.mmb_backward_sr(*a, int(seed) & ((1 << 64) - 1), s or None)
     if st != 0:
         raise MmbError(st)
 
