@@ -250,3 +250,65 @@ def integer_case(B, T, C, OC, dtype="f32", seed=0, with_bias=True, prefill=True,
     dbias0 = np.zeros(OC, np.float32) if with_bias else None
     return Case(f"integer B={B} T={T} C={C} OC={OC} {dtype}", dtype, B, T, C, OC,
                 inp, weight, dout, dinp0, dweight0, dbias0, meta={"integer": True})
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm backward inputs (the adjacent op of the same model; page
+# "dev/cuda/layernorm_backward.cu", whose benchmark runs B=8, T=1024, C=1600
+# with every input from make_random_float, read here as uniform on [-1, 1))
+
+@dataclass
+class LNCase:
+    """One LayerNorm-backward call: inputs and initial output contents."""
+    name: str
+    dtype: str
+    B: int
+    T: int
+    C: int
+    dout: np.ndarray      # [BT, C]
+    inp: np.ndarray       # [BT, C]
+    weight: np.ndarray    # [C]
+    mean: np.ndarray      # [BT], the forward's saved row means
+    rstd: np.ndarray      # [BT], the forward's saved 1/sqrt(var + eps)
+    dinp0: np.ndarray     # [BT, C]
+    dweight0: np.ndarray  # [C]
+    dbias0: np.ndarray    # [C]
+
+    @property
+    def BT(self) -> int:
+        return self.B * self.T
+
+
+LN_EPS = 1e-5
+
+
+def layernorm_stats(inp: np.ndarray, eps: float = LN_EPS):
+    """Row statistics the LayerNorm forward saves for its backward (input
+    preparation only): mean and 1/sqrt(biased variance + eps), in fp64."""
+    x = np.asarray(inp, np.float64)
+    m = x.mean(axis=1)
+    v = ((x - m[:, None]) ** 2).mean(axis=1)
+    return m, 1.0 / np.sqrt(v + eps)
+
+
+def layernorm_case(B, T, C, dtype="bf16", seed=0, prefill=False) -> LNCase:
+    """inp, weight and dout uniform on [-1, 1) (seeded, rounded to dtype);
+    mean and rstd from the rounded inp, rounded to dtype as the forward
+    stores them; outputs zero or, with prefill, uniform on [-0.1, 0.1)."""
+    g = _rng(30_000_000 + seed)
+    BT = B * T
+
+    def uni(shape, scale=1.0):
+        return to_dtype_values(g.uniform(-scale, scale, size=shape), dtype)
+
+    inp, weight, dout = uni((BT, C)), uni((C,)), uni((BT, C))
+    m, r = layernorm_stats(inp)
+    mean, rstd = to_dtype_values(m, dtype), to_dtype_values(r, dtype)
+    if prefill:
+        dinp0, dweight0, dbias0 = uni((BT, C), 0.1), uni((C,), 0.1), uni((C,), 0.1)
+    else:
+        dinp0 = np.zeros((BT, C), np.float32)
+        dweight0, dbias0 = np.zeros(C, np.float32), np.zeros(C, np.float32)
+    return LNCase(name=f"layernorm backward {dtype} B{B} T{T} C{C}", dtype=dtype, B=B, T=T, C=C,
+                  dout=dout, inp=inp, weight=weight, mean=mean, rstd=rstd, dinp0=dinp0,
+                  dweight0=dweight0, dbias0=dbias0)

@@ -17,7 +17,8 @@ runs, so a result that added onto the buffer instead of assigning it would
 show.  ``forward`` is the layer's forward product (out = inp . W^T + bias),
 the step before the backward pass.  ``backward_sr`` rounds the bf16
 parameter gradients stochastically (Philox-4x64-10 random bits, see
-mmb_oracle.c).
+mmb_oracle.c).  ``layernorm_backward`` is the adjacent LayerNorm backward
+of the same model (its own page, dev/cuda/layernorm_backward.cu).
 """
 from __future__ import annotations
 
@@ -75,6 +76,8 @@ class Oracle:
         for f in ("mmb_oracle_dinp", "mmb_oracle_dweight", "mmb_oracle_dbias",
                   "mmb_oracle_backward", "mmb_oracle_forward"):
             getattr(lib, f).restype = None
+        lib.mmb_oracle_layernorm_backward.argtypes = [dp] * 8 + [L, L, L]
+        lib.mmb_oracle_layernorm_backward.restype = None
         u64 = ctypes.c_uint64
         lib.mmb_oracle_philox4x64_10.argtypes = [ctypes.POINTER(u64), ctypes.POINTER(u64),
                                                  ctypes.POINTER(u64)]
@@ -177,6 +180,20 @@ class Oracle:
         return (gi, self.round_sr(gw, seed, 1),
                 self.round_sr(gb, seed, 2).ravel() if with_bias else None)
 
+    def layernorm_backward(self, dout, inp, weight, mean, rstd, dinp_prefill=None,
+                           dweight_prefill=None, dbias_prefill=None, *, B, T, C):
+        """LayerNorm backward: (dinp [BT,C], dweight [C], dbias [C]), each
+        added onto its prefill (zeros when None)."""
+        BT = B * T
+        d, x = _f64(dout, (BT, C)), _f64(inp, (BT, C))
+        w, m, s = _f64(weight, (C,)), _f64(mean, (BT,)), _f64(rstd, (BT,))
+        gi = np.zeros((BT, C)) if dinp_prefill is None else _f64(dinp_prefill, (BT, C)).copy()
+        gw = np.zeros(C) if dweight_prefill is None else _f64(dweight_prefill, (C,)).copy()
+        gb = np.zeros(C) if dbias_prefill is None else _f64(dbias_prefill, (C,)).copy()
+        self.lib.mmb_oracle_layernorm_backward(_ptr(gi), _ptr(gw), _ptr(gb), _ptr(d), _ptr(x),
+                                               _ptr(w), _ptr(m), _ptr(s), B, T, C)
+        return gi, gw, gb
+
     def threads(self) -> int:
         """OpenMP threads the parallel loops use."""
         return int(self.lib.mmb_oracle_threads())
@@ -232,6 +249,10 @@ def round_sr(*a, **k):
 
 def backward_sr(*a, **k):
     return _get().backward_sr(*a, **k)
+
+
+def layernorm_backward(*a, **k):
+    return _get().layernorm_backward(*a, **k)
 
 
 def threads() -> int:

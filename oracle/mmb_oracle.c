@@ -21,7 +21,8 @@
  *
  *   out[r,o]     <- sum_{i<C} inp[r,i] * weight[o,i] (+ bias[o])   (written)
  *
- * plus the stochastic rounding of bf16 gradients described further down.
+ * plus the stochastic rounding of bf16 gradients and the LayerNorm backward
+ * (the adjacent op of the same model) described further down.
  *
  * with r running over the B*T rows.  All tensors are dense row-major:
  * inp [BT,C], dout [BT,OC], weight [OC,C], dinp [BT,C], dweight [OC,C],
@@ -122,6 +123,59 @@ void mmb_oracle_forward(double* out, const double* inp, const double* weight,
                 s += inp[r * C + i] * weight[o * C + i];
             out[r * OC + o] = bias != NULL ? s + bias[o] : s;
         }
+    }
+}
+
+/* ---- LayerNorm backward ---------------------------------------------------
+ *
+ * The llm.c page "dev/cuda/layernorm_backward.cu", CPU reference
+ * layernorm_backward_cpu: for every row r of B*T rows of C channels, with
+ * the forward's saved mean[r] and rstd[r],
+ *   norm_i  = (inp[r,i] - mean[r]) * rstd[r]
+ *   dnorm_i = weight[i] * dout[r,i]
+ *   a = (1/C) sum_i dnorm_i,   b = (1/C) sum_i dnorm_i * norm_i
+ *   dbias[i]   += dout[r,i]
+ *   dweight[i] += norm_i * dout[r,i]
+ *   dinp[r,i]  += (dnorm_i - a - norm_i * b) * rstd[r]
+ * All three outputs accumulate onto their buffers, as on the page.  Rows are
+ * independent for dinp (OpenMP over rows); dweight and dbias sum over rows,
+ * so they are computed column by column (OpenMP over channels), each one
+ * sequential double sum in row order. */
+void mmb_oracle_layernorm_backward(double* dinp, double* dweight, double* dbias,
+                                   const double* dout, const double* inp, const double* weight,
+                                   const double* mean, const double* rstd,
+                                   long B, long T, long C)
+{
+    const long BT = B * T;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < BT; r++) {
+        const double* d = dout + r * C;
+        const double* x = inp + r * C;
+        double a = 0.0, b = 0.0;
+        for (long i = 0; i < C; i++) {
+            const double norm = (x[i] - mean[r]) * rstd[r];
+            const double dnorm = weight[i] * d[i];
+            a += dnorm;
+            b += dnorm * norm;
+        }
+        a /= (double)C;
+        b /= (double)C;
+        for (long i = 0; i < C; i++) {
+            const double norm = (x[i] - mean[r]) * rstd[r];
+            const double dnorm = weight[i] * d[i];
+            dinp[r * C + i] += (dnorm - a - norm * b) * rstd[r];
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < C; i++) {
+        double sw = 0.0, sb = 0.0;
+        for (long r = 0; r < BT; r++) {
+            const double norm = (inp[r * C + i] - mean[r]) * rstd[r];
+            sb += dout[r * C + i];
+            sw += norm * dout[r * C + i];
+        }
+        dbias[i] += sb;
+        dweight[i] += sw;
     }
 }
 

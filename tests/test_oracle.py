@@ -259,9 +259,58 @@ def pin_sr_round_array(o):
     assert abs(p_up - 0.25) < 4 * sd, p_up
 
 
+def _ln_forward_loss(x, w, b, dout, eps=1e-5):
+    """L = sum(dout * LayerNorm(x; w, b)), the forward of the LayerNorm page
+    (row mean, biased variance, 1/sqrt(var + eps), scale and shift), fp64."""
+    m = x.mean(axis=1, keepdims=True)
+    v = ((x - m) ** 2).mean(axis=1, keepdims=True)
+    return float(np.sum(dout * ((x - m) / np.sqrt(v + eps) * w + b)))
+
+
+def pin_layernorm_finite_differences(o):
+    """Gradients of the forward loss by central differences: dinp (the
+    forward is smooth in x; h = 1e-5 leaves an O(h^2) error far below the
+    tolerance) and dweight, dbias (the loss is affine in them)."""
+    rng = np.random.default_rng(12)
+    for B, T, C in ((1, 3, 7), (2, 2, 16)):
+        BT = B * T
+        x = rng.uniform(-1, 1, (BT, C))
+        w = rng.uniform(-1, 1, C)
+        b = rng.uniform(-1, 1, C)
+        d = rng.uniform(-1, 1, (BT, C))
+        mean, rstd = wl.layernorm_stats(x)
+        gi, gw, gb = o.layernorm_backward(d, x, w, mean, rstd, B=B, T=T, C=C)
+        h = 1e-5
+        fi = np.zeros_like(x)
+        for r in range(BT):
+            for i in range(C):
+                xp = x.copy(); xp[r, i] += h
+                xm = x.copy(); xm[r, i] -= h
+                fi[r, i] = (_ln_forward_loss(xp, w, b, d) - _ln_forward_loss(xm, w, b, d)) / (2 * h)
+        np.testing.assert_allclose(gi, fi, rtol=0, atol=1e-7 * np.abs(fi).max())
+        for i in range(C):
+            e = np.zeros(C); e[i] = 1.0
+            fw = (_ln_forward_loss(x, w + e, b, d) - _ln_forward_loss(x, w - e, b, d)) / 2
+            fb = (_ln_forward_loss(x, w, b + e, d) - _ln_forward_loss(x, w, b - e, d)) / 2
+            assert abs(gw[i] - fw) <= 1e-10 * (1 + abs(fw)), (i, gw[i], fw)
+            assert abs(gb[i] - fb) <= 1e-10 * (1 + abs(fb)), (i, gb[i], fb)
+
+
+def pin_layernorm_accumulates(o):
+    """All three outputs add onto their buffers: out(P) - P == out(0)."""
+    c = wl.layernorm_case(1, 5, 12, "f32", seed=3, prefill=True)
+    kw = dict(B=c.B, T=c.T, C=c.C)
+    a = o.layernorm_backward(c.dout, c.inp, c.weight, c.mean, c.rstd, c.dinp0, c.dweight0,
+                             c.dbias0, **kw)
+    z = o.layernorm_backward(c.dout, c.inp, c.weight, c.mean, c.rstd, **kw)
+    for got, zero, pre in zip(a, z, (c.dinp0, c.dweight0, c.dbias0)):
+        np.testing.assert_allclose(got - pre, zero, rtol=0, atol=1e-15)
+
+
 PINS = [pin_hand_example, pin_brute_force, pin_dbias_overwrites,
         pin_forward_hand_example, pin_forward_affine, pin_forward_adjoint,
-        pin_philox_numpy, pin_sr_mapping, pin_sr_closed_form, pin_sr_round_array]
+        pin_philox_numpy, pin_sr_mapping, pin_sr_closed_form, pin_sr_round_array,
+        pin_layernorm_finite_differences, pin_layernorm_accumulates]
 
 
 # ---------------------------------------------------------------------------
@@ -323,6 +372,34 @@ def test_forward_affine(o):
 
 def test_forward_adjoint(o):
     pin_forward_adjoint(o)
+
+
+def test_layernorm_finite_differences(o):
+    pin_layernorm_finite_differences(o)
+
+
+def test_layernorm_accumulates(o):
+    pin_layernorm_accumulates(o)
+
+
+def test_layernorm_invariants(o):
+    """With the row's true statistics: each row of the dinp increment sums to
+    zero (sum of norm is zero); dbias is the column sum of dout; dweight the
+    column sum of norm * dout; dout = 1/weight makes dnorm = 1 and the dinp
+    increment vanish."""
+    c = wl.layernorm_case(2, 8, 24, "f32", seed=4)
+    x = c.inp.astype(np.float64)
+    mean, rstd = wl.layernorm_stats(x)
+    kw = dict(B=c.B, T=c.T, C=c.C)
+    gi, gw, gb = o.layernorm_backward(c.dout, x, c.weight, mean, rstd, **kw)
+    assert np.all(np.abs(gi.sum(axis=1)) <= 1e-12 * np.abs(gi).sum(axis=1))
+    np.testing.assert_allclose(gb, c.dout.astype(np.float64).sum(axis=0), rtol=1e-14, atol=1e-14)
+    norm = (x - mean[:, None]) * rstd[:, None]
+    np.testing.assert_allclose(gw, (norm * c.dout).sum(axis=0), rtol=1e-12, atol=1e-12)
+    w = np.where(np.abs(c.weight) < 0.05, 0.5, c.weight).astype(np.float64)
+    d = np.tile(1.0 / w, (c.BT, 1))
+    gi2, _, _ = o.layernorm_backward(d, x, w, mean, rstd, **kw)
+    assert np.abs(gi2).max() <= 1e-12 * np.abs(rstd).max() * c.C
 
 
 def test_philox_matches_numpy(o):
@@ -561,6 +638,18 @@ MUTATIONS = [
     ("sr truncates", "return (uint16_t)((u + r16) >> 16);", "return (uint16_t)(u >> 16);"),
     ("sr rounds on the wrong bits", "return (uint16_t)((u + r16) >> 16);",
      "return (uint16_t)((u + (r16 >> 1)) >> 16);"),
+    ("layernorm drops the mean term", "dinp[r * C + i] += (dnorm - a - norm * b) * rstd[r];",
+     "dinp[r * C + i] += (dnorm - norm * b) * rstd[r];"),
+    ("layernorm halves the norm term", "dinp[r * C + i] += (dnorm - a - norm * b) * rstd[r];",
+     "dinp[r * C + i] += (dnorm - a - 0.5 * norm * b) * rstd[r];"),
+    ("layernorm misses the final scale", "dinp[r * C + i] += (dnorm - a - norm * b) * rstd[r];",
+     "dinp[r * C + i] += (dnorm - a - norm * b);"),
+    ("layernorm sums instead of averaging", "        a /= (double)C;\n", "\n"),
+    ("layernorm dweight from dnorm", "sw += norm * dout[r * C + i];",
+     "sw += norm * dout[r * C + i] * weight[i];"),
+    ("layernorm dbias assigned", "dbias[i] += sb;", "dbias[i] = sb;"),
+    ("layernorm norm without rstd", "const double norm = (x[i] - mean[r]) * rstd[r];\n            const double dnorm = weight[i] * d[i];\n            a += dnorm;",
+     "const double norm = (x[i] - mean[r]);\n            const double dnorm = weight[i] * d[i];\n            a += dnorm;"),
 ]
 
 
