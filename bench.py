@@ -39,6 +39,93 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 KERNEL_NAME = {"bf16": "mmb_tiles_bf16_kernel", "f32": "mmb_tiles_kernel"}
 KERNEL_NAME_FORWARD = {"bf16": "mmb_fwd_bf16_kernel", "f32": "mmb_fwd_kernel"}
 KERNEL_NAME_SR = {"bf16": "mmb_tiles_bf16_sr_kernel"}
+METRIC_LN = "layernorm-backward GB/s (dinp+dweight+dbias) at the page's B=8 T=1024 C=1600; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def layernorm_bytes(c) -> int:
+    """Algorithmic HBM bytes of one LayerNorm backward: read dout, inp and
+    the old dinp and write dinp (BT*C each), read weight, mean and rstd, read
+    and write dweight and dbias."""
+    es = 2 if c.dtype == "bf16" else 4
+    return es * (4 * c.BT * c.C + c.C + 2 * c.BT + 4 * c.C)
+
+
+def bench_layernorm(args):
+    """--op layernorm: the LayerNorm backward at the page's benchmark shape
+    (B=8, T=1024, C=1600, bf16 as the page's build), HBM-bound."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    from linear_layer_backward_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    c = wl.layernorm_case(8, 1024, 1600, "bf16", seed=1)
+    print(f"[bench] workload: {c.name}", file=sys.stderr, flush=True)
+
+    def up(a):
+        raw = wl.storage(np.asarray(a, np.float32).ravel(), c.dtype)
+        return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+    b = [up(a) for a in (c.dinp0, c.dweight0, c.dbias0, c.dout, c.inp, c.weight, c.mean, c.rstd)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mmb.mmb_layernorm_backward(*b, c.B, c.T, c.C, mmb.MMB_BF16, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(K):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for a, z in ev:
+        a.record(stream)
+        step()
+        z.record(stream)
+    torch.cuda.synchronize(dev)
+    launch_ms = float(np.mean([a.elapsed_time(z) for a, z in ev]))
+    nbytes = layernorm_bytes(c)
+    out = {
+        "metric": METRIC_LN, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "B": c.B, "T": c.T, "C": c.C, "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (launch_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("ln_bwd_rows", 0, LN_SLUG),
+                     "kernel": "ln_bwd_rows + ln_bwd_reduce (one call)",
+                     "launch_ms": round(launch_ms, 5)},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        # the whole workload, repeated for at least 2 s (one pass is short)
+        reps, t = 0, time.perf_counter()
+        while True:
+            oracle.layernorm_backward(c.dout, c.inp, c.weight, c.mean, c.rstd, B=c.B, T=c.T,
+                                      C=c.C)
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= 2.0:
+                break
+        sb = reps * nbytes
+        out["cpu_baseline"] = {"value": sb / dt / 1e9, "unit": "GB/s", "cores": oracle.threads(),
+                               "kind": "oracle",
+                               "sample": f"{c.name}: the whole call {reps} times; fp64 OpenMP, "
+                                         f"{dt:.2f} s for {sb:.3e} bf16-equivalent bytes"}
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def kernel_name(op: str, dtype: str) -> str:
@@ -67,11 +154,15 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, cfg: int):
+LN_SLUG = "layernorm_bf16_B8_T1024_C1600"
+
+
+def measured_traffic(kernel: str, cfg: int, slug: str = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, if it was taken on the current kernel sources."""
     from linear_layer_backward_amd import workloads as wl
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{wl.CONFIG_SLUGS[cfg]}_counters.txt")
+    slug = slug or wl.CONFIG_SLUGS[cfg]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{slug}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -209,7 +300,8 @@ def main(argv=None):
     # steady clocks: fewer warm-up steps measure the ramp, not the kernel
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--op", default="backward", choices=["backward", "forward", "backward_sr"],
+    ap.add_argument("--op", default="backward",
+                    choices=["backward", "forward", "backward_sr", "layernorm"],
                     help="backward (the metric), the forward product at the same shapes, or the "
                          "bf16 backward with stochastically rounded dweight/dbias")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -244,6 +336,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
         return 0
+
+    if args.op == "layernorm":
+        return bench_layernorm(args)
 
     from linear_layer_backward_amd import mmb
     from linear_layer_backward_amd import workloads as wl

@@ -174,6 +174,48 @@ int mmb_forward_path(const void* out, const void* inp, const void* weight,
 int mmb_forward_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num_cus,
                            int* splits, int* units, int max_units);
 
+/* ---- LayerNorm backward -----------------------------------------------------
+ *
+ * The op next to the linear layer in a GPT-2 block (llm.c page
+ * "dev/cuda/layernorm_backward.cu", CPU reference layernorm_backward_cpu).
+ * For every row r < BT = B*T of C channels, with the forward's saved mean[r]
+ * and rstd[r] (1/sqrt(biased variance + eps)):
+ *
+ *   norm_i = (inp[r,i] - mean[r]) * rstd[r],   dnorm_i = weight[i] * dout[r,i]
+ *   a = (1/C) sum_i dnorm_i,   b = (1/C) sum_i dnorm_i * norm_i
+ *   dinp[r,i]  += (dnorm_i - a - norm_i * b) * rstd[r]
+ *   dweight[i] += sum_r norm_i * dout[r,i]
+ *   dbias[i]   += sum_r dout[r,i]
+ *
+ * All three outputs accumulate, as on the page.  Layout: dout, inp, dinp
+ * [BT,C] row-major; weight, dweight, dbias [C]; mean, rstd [BT].  One dtype
+ * for all eight tensors: MMB_FP32, or MMB_BF16 storage with fp32 arithmetic
+ * and one round to nearest-even per output.  Device pointers owned by the
+ * caller, all required; outputs may not overlap each other or an input
+ * (MMB_ERR_ALIAS).  16-byte aligned dinp, dout, inp and weight with C a
+ * multiple of 8 (bf16) / 4 (fp32) and C <= 2048 (bf16) / 1024 (fp32) take the
+ * row kernel (two launches: rows, then a fixed-order column reduction of the
+ * per-workgroup fp32 partials, which live in the library's per-(device,
+ * stream) workspace); anything else takes the generic kernels.  Results are
+ * deterministic.  Errors as for mmb_backward. */
+int mmb_layernorm_backward(void* dinp, void* dweight, void* dbias,
+                           const void* dout, const void* inp, const void* weight,
+                           const void* mean, const void* rstd,
+                           int B, int T, int C, int dtype, void* stream);
+
+/* Host-only validation of a LayerNorm-backward argument set (no HIP call). */
+int mmb_layernorm_check_args(const void* dinp, const void* dweight, const void* dbias,
+                             const void* dout, const void* inp, const void* weight,
+                             const void* mean, const void* rstd,
+                             int B, int T, int C, int dtype);
+
+/* Which path a LayerNorm-backward call takes: 1 = row kernel, 0 = generic,
+ * or a negative mmb_status.  Host only. */
+int mmb_layernorm_path(const void* dinp, const void* dweight, const void* dbias,
+                       const void* dout, const void* inp, const void* weight,
+                       const void* mean, const void* rstd,
+                       int B, int T, int C, int dtype);
+
 /* Synchronise every device the library has used, then free its workspaces.
  * The next call allocates again. */
 int mmb_release(void);

@@ -683,6 +683,80 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     return e == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }
 
+// LayerNorm backward: every pointer required; the three outputs may not
+// overlap each other or any input.
+int check_ln(const void* dinp, const void* dweight, const void* dbias, const void* dout,
+             const void* inp, const void* weight, const void* mean, const void* rstd, int B, int T,
+             int C, int dtype) {
+    if (!dinp || !dweight || !dbias || !dout || !inp || !weight || !mean || !rstd)
+        return MMB_ERR_NULL;
+    if (B < 1 || T < 1 || C < 1) return MMB_ERR_DIM;
+    if (dtype != MMB_FP32 && dtype != MMB_BF16) return MMB_ERR_DTYPE;
+    const long long BT = (long long)B * T;
+    if (BT > 0x7fffffffLL) return MMB_ERR_OVERFLOW;
+    const uintptr_t es = elem_size(dtype);
+    auto R = [&](const void* p, long long n) {
+        return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
+    };
+    const Range outs[3] = {R(dinp, BT * C), R(dweight, C), R(dbias, C)};
+    const Range ins[5] = {R(dout, BT * C), R(inp, BT * C), R(weight, C), R(mean, BT), R(rstd, BT)};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = a + 1; b < 3; ++b)
+            if (overlap(outs[a], outs[b])) return MMB_ERR_ALIAS;
+        for (const Range& r : ins)
+            if (overlap(outs[a], r)) return MMB_ERR_ALIAS;
+    }
+    return MMB_OK;
+}
+
+// Vectors per lane of the LayerNorm row kernel, or 0 for the generic kernels
+// (also when a row-streamed buffer is not 16-byte aligned).
+int ln_path(const void* dinp, const void* dout, const void* inp, const void* weight, int C,
+            int dtype) {
+    const void* ptrs[4] = {dinp, dout, inp, weight};
+    for (const void* p : ptrs)
+        if ((uintptr_t)p % 16 != 0) return 0;
+    return ln_vectors_per_lane(dtype, C);
+}
+
+int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
+                   const void* weight, const void* mean, const void* rstd, int B, int T, int C,
+                   int dtype, hipStream_t s) {
+    int st = check_ln(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C, dtype);
+    if (st != MMB_OK) return st;
+    LNParams p;
+    p.dinp = dinp;
+    p.dweight = dweight;
+    p.dbias = dbias;
+    p.dout = dout;
+    p.inp = inp;
+    p.weight = weight;
+    p.mean = mean;
+    p.rstd = rstd;
+    p.BT = (long long)B * T;
+    p.C = C;
+    p.partial = nullptr;
+    const int nj = ln_path(dinp, dout, inp, weight, C, dtype);
+    int G = 0;
+    // held through the launch: another call may not regrow the partials first
+    std::unique_lock<std::mutex> lock(g_mu, std::defer_lock);
+    if (nj > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
+        lock.lock();
+        DeviceInfo di;
+        st = device_info(dev, &di);
+        if (st != MMB_OK) return st;
+        // one workgroup of 8 row-waves per CU (fewer for few rows)
+        G = (int)std::max(1LL, std::min<long long>(di.cus, (p.BT + 7) / 8));
+        Workspace& w = g_ws[{dev, s}];
+        st = grow(&w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
+        if (st != MMB_OK) return st;
+        p.partial = (float*)w.partials;
+    }
+    return launch_layernorm_backward(dtype, p, G, nj, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+}
+
 int forward_impl(void* out, const void* inp, const void* weight, const void* bias, int B, int T,
                  int C, int OC, int dtype, hipStream_t s) {
     int st = check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
@@ -712,6 +786,28 @@ int forward_impl(void* out, const void* inp, const void* weight, const void* bia
 }  // namespace mmb
 
 extern "C" {
+
+int mmb_layernorm_backward(void* dinp, void* dweight, void* dbias, const void* dout,
+                           const void* inp, const void* weight, const void* mean,
+                           const void* rstd, int B, int T, int C, int dtype, void* stream) {
+    return mmb::layernorm_impl(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C, dtype,
+                               (hipStream_t)stream);
+}
+
+int mmb_layernorm_check_args(const void* dinp, const void* dweight, const void* dbias,
+                             const void* dout, const void* inp, const void* weight,
+                             const void* mean, const void* rstd, int B, int T, int C, int dtype) {
+    return mmb::check_ln(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C, dtype);
+}
+
+int mmb_layernorm_path(const void* dinp, const void* dweight, const void* dbias, const void* dout,
+                       const void* inp, const void* weight, const void* mean, const void* rstd,
+                       int B, int T, int C, int dtype) {
+    const int st = mmb::check_ln(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C,
+                                 dtype);
+    if (st != MMB_OK) return st;
+    return mmb::ln_path(dinp, dout, inp, weight, C, dtype) > 0 ? 1 : 0;
+}
 
 int mmb_forward_check_args(const void* out, const void* inp, const void* weight, const void* bias,
                            int B, int T, int C, int OC, int dtype) {

@@ -69,6 +69,27 @@ hipError_t launch_fwd_tiles(int dtype, const TilesParams& p, hipStream_t s);
 hipError_t launch_fwd_tiles_bf16(const TilesParams& p, hipStream_t s);
 hipError_t launch_fwd_generic(int dtype, void* out, const void* inp, const void* weight,
                               const void* bias, int BT, int C, int OC, hipStream_t s);
+// LayerNorm backward (one dtype for all tensors; every output accumulates).
+struct LNParams {
+    void* dinp;            // [BT, C]
+    void* dweight;         // [C]
+    void* dbias;           // [C]
+    const void* dout;      // [BT, C]
+    const void* inp;       // [BT, C]
+    const void* weight;    // [C]
+    const void* mean;      // [BT]
+    const void* rstd;      // [BT]
+    long long BT;
+    int C;
+    float* partial;        // [G, 2C] fp32 column sums per workgroup
+};
+// 16-byte vectors per lane of the row kernel for C (1, 2 or 4), or 0 for
+// the generic kernels (C not a multiple of the vector width, or too wide).
+int ln_vectors_per_lane(int dtype, int C);
+// G workgroups for the row kernel (partial holds G * 2C floats); nj from
+// ln_vectors_per_lane.  Two launches on `s` (rows, then the column reduce).
+hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, int nj, hipStream_t s);
+
 // sr: bf16 only, dweight and dbias stochastically rounded under `seed`
 hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,
                           const void* dout, const void* inp, const void* weight,

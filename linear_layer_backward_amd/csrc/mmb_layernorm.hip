@@ -1,0 +1,278 @@
+// mmb_layernorm.hip -- LayerNorm backward, the op next to the linear layer in
+// a GPT-2 block (llm.c page "dev/cuda/layernorm_backward.cu", CPU reference
+// layernorm_backward_cpu).  For every row r of B*T rows of C channels, with
+// the forward's saved mean[r] and rstd[r]:
+//   norm_i = (inp[r,i] - mean[r]) * rstd[r],   dnorm_i = weight[i] * dout[r,i]
+//   a = mean_i dnorm_i,   b = mean_i dnorm_i * norm_i
+//   dinp[r,i] += (dnorm_i - a - norm_i * b) * rstd[r]
+//   dweight[i] += sum_r norm_i * dout[r,i],   dbias[i] += sum_r dout[r,i]
+//
+// The op is bound by HBM: per row it reads dout, inp and the old dinp and
+// writes dinp; the flops are a few per element.  gfx950 design:
+//  * One wave64 per row, 8 waves per workgroup, one workgroup per CU, rows
+//    dealt out wave by wave.  Lane l owns the 16-byte column vectors
+//    l, l + 64, ... (NJ <= 4 of them: C <= 2048 in bf16, 1024 in fp32; wider
+//    rows take the generic kernels below), so each row
+//    is read with fully coalesced 16-byte loads and the lane's weight slice
+//    and its dweight / dbias sums stay in registers for all its rows.
+//  * The next row's dout and inp are loaded before the current row's
+//    reductions, so every wave keeps two rows in flight.
+//  * The two row means are wave reductions (xor shuffles, fixed order).
+//  * dweight / dbias: each workgroup adds its 8 waves' sums in LDS in wave
+//    order and writes one fp32 partial row of 2C values; a second launch sums
+//    the partials of all workgroups in workgroup order (16 interleaved groups
+//    per column, then the groups in order), adds the old values and rounds
+//    once.  No atomics: results repeat bit for bit.
+//  * bf16 storage: values widen exactly to fp32, all arithmetic is fp32, each
+//    output is rounded once to nearest-even.
+#include "mmb_tile_common.h"
+
+namespace mmb {
+namespace {
+
+constexpr int LN_NT = 512, LN_NW = LN_NT / 64;
+
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int N = 4; };
+template <> struct Vec<bf16_t> { static constexpr int N = 8; };
+
+// element e of a 16-byte vector, widened to fp32
+template <typename T>
+__device__ __forceinline__ float elem(const u32x4& v, int e) {
+    if constexpr (sizeof(T) == 4) return __uint_as_float(v[e]);
+    else return __uint_as_float(e & 1 ? (v[e >> 1] & 0xffff0000u) : (v[e >> 1] << 16));
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack(const float (&f)[Vec<T>::N]) {
+    u32x4 o;
+    if constexpr (sizeof(T) == 4) {
+        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(f[e]);
+    } else {
+        for (int e = 0; e < 4; ++e) o[e] = f32x2_to_bf16x2_bits(f[2 * e], f[2 * e + 1]);
+    }
+    return o;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+template <typename T, int NJ>
+__global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
+    constexpr int V = Vec<T>::N;
+    __shared__ float red[2 * 64 * NJ * V];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int C = p.C;
+    const long long rowbytes = (long long)C * (long long)sizeof(T);
+    // lane's vector j covers columns V * (lane + 64 j) .. + V - 1
+    uint32_t off[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int col = V * (lane + 64 * j);
+        off[j] = (uint32_t)(col * (int)sizeof(T)) | oob_if_ge(col, C);
+    }
+    u32x4 w[NJ];
+    {
+        const auto rw = make_rsrc(p.weight, rowbytes);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) w[j] = buffer_load16(rw, off[j], 0);
+    }
+    float aw[NJ][V], ab[NJ][V];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < V; ++e) aw[j][e] = ab[j][e] = 0.f;
+
+    const long long nwaves = (long long)gridDim.x * LN_NW;
+    long long r = (long long)blockIdx.x * LN_NW + wave;
+    const T* dout = (const T*)p.dout;
+    const T* inp = (const T*)p.inp;
+    T* dinp = (T*)p.dinp;
+    u32x4 d[NJ], x[NJ];
+    auto load_row = [&](long long row) {
+        const bool live = row < p.BT;
+        const auto rd = make_rsrc(dout + (live ? row : 0) * C, live ? rowbytes : 0);
+        const auto rx = make_rsrc(inp + (live ? row : 0) * C, live ? rowbytes : 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            d[j] = buffer_load16(rd, off[j], 0);
+            x[j] = buffer_load16(rx, off[j], 0);
+        }
+    };
+    load_row(r);
+    const float invC = 1.0f / (float)C;
+    for (; r < p.BT; r += nwaves) {
+        const float m = to_f32(((const T*)p.mean)[r]);
+        const float s = to_f32(((const T*)p.rstd)[r]);
+        float nrm[NJ][V], dn[NJ][V];
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float dv = elem<T>(d[j], e);
+                nrm[j][e] = (elem<T>(x[j], e) - m) * s;
+                dn[j][e] = elem<T>(w[j], e) * dv;
+                sa += dn[j][e];
+                sb += dn[j][e] * nrm[j][e];
+                ab[j][e] += dv;
+                aw[j][e] += nrm[j][e] * dv;
+            }
+        // the next row's loads fly during the reductions and the update
+        load_row(r + nwaves);
+        const float a = wave_sum(sa) * invC, b = wave_sum(sb) * invC;
+        const auto rg = make_rsrc(dinp + r * C, rowbytes);
+        u32x4 g[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) g[j] = buffer_load16(rg, off[j], 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            float o[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                o[e] = elem<T>(g[j], e) + (dn[j][e] - a - nrm[j][e] * b) * s;
+            __builtin_amdgcn_raw_buffer_store_b128(pack<T>(o), rg, off[j], 0, 0);
+        }
+    }
+    // the 8 waves' column sums, added in wave order: [dweight | dbias]
+    for (int wv = 0; wv < LN_NW; ++wv) {
+        if (wave == wv) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const int i = V * (lane + 64 * j) + e;
+                    red[i] = wv == 0 ? aw[j][e] : red[i] + aw[j][e];
+                    red[64 * NJ * V + i] = wv == 0 ? ab[j][e] : red[64 * NJ * V + i] + ab[j][e];
+                }
+        }
+        __syncthreads();
+    }
+    float* part = p.partial + (long long)blockIdx.x * 2 * C;
+    for (int i = tid; i < C; i += LN_NT) {
+        part[i] = red[i];
+        part[C + i] = red[64 * NJ * V + i];
+    }
+}
+
+// dweight[i] += sum_g partial[g][i], dbias[i] += sum_g partial[g][C + i]:
+// 64 columns per workgroup, 16 groups of workgroup partials g = q, q + 16, ...
+// summed in order, then the 16 group sums in order.
+constexpr int RED_COLS = 64, RED_GROUPS = 16;
+
+template <typename T>
+__global__ __launch_bounds__(RED_COLS * RED_GROUPS) void ln_bwd_reduce(LNParams p, int G) {
+    __shared__ float s[RED_GROUPS][RED_COLS];
+    const int c = threadIdx.x % RED_COLS, q = threadIdx.x / RED_COLS;
+    const int col = blockIdx.x * RED_COLS + c;   // over 2C: dweight then dbias
+    const int C2 = 2 * p.C;
+    float acc = 0.f;
+    if (col < C2) {
+        int g = q;
+        for (; g + 3 * RED_GROUPS < G; g += 4 * RED_GROUPS) {
+            const float v0 = p.partial[(long long)g * C2 + col];
+            const float v1 = p.partial[(long long)(g + RED_GROUPS) * C2 + col];
+            const float v2 = p.partial[(long long)(g + 2 * RED_GROUPS) * C2 + col];
+            const float v3 = p.partial[(long long)(g + 3 * RED_GROUPS) * C2 + col];
+            acc = (((acc + v0) + v1) + v2) + v3;
+        }
+        for (; g < G; g += RED_GROUPS) acc += p.partial[(long long)g * C2 + col];
+    }
+    s[q][c] = acc;
+    __syncthreads();
+    if (q == 0 && col < C2) {
+        float t = s[0][c];
+#pragma unroll
+        for (int k = 1; k < RED_GROUPS; ++k) t += s[k][c];
+        T* out = col < p.C ? (T*)p.dweight + col : (T*)p.dbias + (col - p.C);
+        *out = from_f32<T>(to_f32(*out) + t);
+    }
+}
+
+// ---- any shape / alignment --------------------------------------------------
+// dinp: one wave per row, two passes over the row with a stride of 64.
+template <typename T>
+__global__ __launch_bounds__(256) void ln_generic_dinp(LNParams p) {
+    const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, C = p.C;
+    if (r >= p.BT) return;
+    const T* d = (const T*)p.dout + r * C;
+    const T* x = (const T*)p.inp + r * C;
+    const T* w = (const T*)p.weight;
+    const float m = to_f32(((const T*)p.mean)[r]), s = to_f32(((const T*)p.rstd)[r]);
+    float sa = 0.f, sb = 0.f;
+    for (int i = lane; i < C; i += 64) {
+        const float dn = to_f32(w[i]) * to_f32(d[i]);
+        sa += dn;
+        sb += dn * (to_f32(x[i]) - m) * s;
+    }
+    const float a = wave_sum(sa) / (float)C, b = wave_sum(sb) / (float)C;
+    T* g = (T*)p.dinp + r * C;
+    for (int i = lane; i < C; i += 64) {
+        const float nrm = (to_f32(x[i]) - m) * s;
+        const float dn = to_f32(w[i]) * to_f32(d[i]);
+        g[i] = from_f32<T>(to_f32(g[i]) + (dn - a - nrm * b) * s);
+    }
+}
+
+// dweight / dbias: one thread per column, rows in order.
+template <typename T>
+__global__ __launch_bounds__(256) void ln_generic_dwb(LNParams p) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= p.C) return;
+    float sw = 0.f, sb = 0.f;
+    for (long long r = 0; r < p.BT; ++r) {
+        const float dv = to_f32(((const T*)p.dout)[r * p.C + i]);
+        const float nrm = (to_f32(((const T*)p.inp)[r * p.C + i]) - to_f32(((const T*)p.mean)[r])) *
+                          to_f32(((const T*)p.rstd)[r]);
+        sb += dv;
+        sw += nrm * dv;
+    }
+    T* dw = (T*)p.dweight + i;
+    T* db = (T*)p.dbias + i;
+    *dw = from_f32<T>(to_f32(*dw) + sw);
+    *db = from_f32<T>(to_f32(*db) + sb);
+}
+
+template <typename T, int NJ>
+hipError_t launch_rows(const LNParams& p, int G, hipStream_t s) {
+    hipLaunchKernelGGL((ln_bwd_rows<T, NJ>), dim3(G), dim3(LN_NT), 0, s, p);
+    hipLaunchKernelGGL((ln_bwd_reduce<T>), dim3((2 * p.C + RED_COLS - 1) / RED_COLS),
+                       dim3(RED_COLS * RED_GROUPS), 0, s, p, G);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_ln(const LNParams& p, int G, int nj, hipStream_t s) {
+    if (nj == 0) {
+        hipLaunchKernelGGL(ln_generic_dinp<T>, dim3((unsigned)((p.BT + 3) / 4)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(ln_generic_dwb<T>, dim3((p.C + 255) / 256), dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
+    if (nj == 1) return launch_rows<T, 1>(p, G, s);
+    if (nj == 2) return launch_rows<T, 2>(p, G, s);
+    if (nj == 4) return launch_rows<T, 4>(p, G, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int ln_vectors_per_lane(int dtype, int C) {
+    const int V = dtype == 1 ? 8 : 4;
+    const int nmax = 4;   // 8 vectors per lane would spill registers
+    if (C % V != 0) return 0;
+    const int nv = C / V;
+    for (int nj = 1; nj <= nmax; nj *= 2)
+        if (nv <= 64 * nj) return nj;
+    return 0;
+}
+
+hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, int nj, hipStream_t s) {
+    if (dtype == 1) return launch_ln<bf16_t>(p, G, nj, s);
+    return launch_ln<float>(p, G, nj, s);
+}
+
+}  // namespace mmb

@@ -56,6 +56,13 @@ _lib.mmb_release.argtypes = []
 _lib.mmb_release.restype = _i
 _lib.mmb_backward_sr.argtypes = [_vp] * 6 + [_i] * 4 + [ctypes.c_ulonglong, _vp]
 _lib.mmb_backward_sr.restype = _i
+_LN_ARGS = [_vp] * 8 + [_i] * 4
+_lib.mmb_layernorm_backward.argtypes = _LN_ARGS + [_vp]
+_lib.mmb_layernorm_backward.restype = _i
+_lib.mmb_layernorm_check_args.argtypes = _LN_ARGS
+_lib.mmb_layernorm_check_args.restype = _i
+_lib.mmb_layernorm_path.argtypes = _LN_ARGS
+_lib.mmb_layernorm_path.restype = _i
 _FWD_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i]
 for _f in ("mmb_forward", "mmb_forward_check_args", "mmb_forward_path"):
     getattr(_lib, _f).argtypes = _FWD_ARGS
@@ -120,6 +127,29 @@ def mmb_backward_sr(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, seed,
     st = _lib.mmb_backward_sr(*a, int(seed) & ((1 << 64) - 1), s or None)
     if st != 0:
         raise MmbError(st)
+
+
+def _ln_args(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C, dtype):
+    return tuple(_addr(t) for t in (dinp, dweight, dbias, dout, inp, weight, mean, rstd)) + (
+        int(B), int(T), int(C), int(dtype))
+
+
+def mmb_layernorm_backward(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C, dtype,
+                           stream) -> None:
+    """LayerNorm backward (all three outputs accumulate)."""
+    s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
+    st = _lib.mmb_layernorm_backward(*_ln_args(dinp, dweight, dbias, dout, inp, weight, mean,
+                                               rstd, B, T, C, dtype), s or None)
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_layernorm_check_args(*a) -> int:
+    return _lib.mmb_layernorm_check_args(*_ln_args(*a))
+
+
+def mmb_layernorm_path(*a) -> int:
+    return _lib.mmb_layernorm_path(*_ln_args(*a))
 
 
 def _fwd_args(out, inp, weight, bias, B, T, C, OC, dtype):

@@ -351,3 +351,56 @@ def test_forward_plan_split_override(mmb, monkeypatch):
     monkeypatch.setenv("MMB_SPLITS_FWD", "2,1,3")
     smax, units = mmb.mmb_forward_plan_units(2, 150, 264, 400, 1, True, 256)
     assert smax == 3 and {u[6] for u in units} == {1, 2, 3}
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm backward
+
+def largs(dtype=1, B=8, T=1024, C=1600):
+    return addrs(8) + [B, T, C, dtype]
+
+
+def test_layernorm_entry_points_declared():
+    for f in ("mmb_layernorm_backward", "mmb_layernorm_check_args", "mmb_layernorm_path"):
+        assert f in declared_functions()
+
+
+def test_layernorm_check_args(mmb):
+    assert mmb.mmb_layernorm_check_args(*largs()) == 0
+    for idx in range(8):
+        a = largs()
+        a[idx] = None
+        assert mmb.mmb_layernorm_check_args(*a) == -1
+    for idx in (8, 9, 10):
+        a = largs()
+        a[idx] = 0
+        assert mmb.mmb_layernorm_check_args(*a) == -2
+    assert mmb.mmb_layernorm_check_args(*largs(dtype=3)) == -3
+    assert mmb.mmb_layernorm_check_args(*largs(B=65536, T=32768, C=8)) == -4
+
+
+def test_layernorm_alias(mmb):
+    a = largs(dtype=0, B=1, T=2, C=8)          # fp32 dweight: 32 bytes
+    a[2] = a[1] + 16                           # dbias inside dweight
+    assert mmb.mmb_layernorm_check_args(*a) == -5
+    b = largs(dtype=0, B=1, T=2, C=8)
+    b[0] = b[7] + 4                            # dinp starting inside rstd
+    assert mmb.mmb_layernorm_check_args(*b) == -5
+    c = largs(dtype=0, B=1, T=2, C=8)
+    c[6] = c[7]                                # inputs may share memory
+    assert mmb.mmb_layernorm_check_args(*c) == 0
+
+
+def test_layernorm_path(mmb):
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=1600)) == 1
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=2048)) == 1
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=2056)) == 0    # wider than the row kernel
+    assert mmb.mmb_layernorm_path(*largs(dtype=0, C=1024)) == 1
+    assert mmb.mmb_layernorm_path(*largs(dtype=0, C=1600)) == 0
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=1604)) == 0    # not a multiple of 8
+    a = largs(dtype=1, C=768)
+    a[3] += 8                                  # dout 8-byte aligned only
+    assert mmb.mmb_layernorm_path(*a) == 0
+    b = largs(dtype=1, C=768)
+    b[6] += 2                                  # mean is read element by element
+    assert mmb.mmb_layernorm_path(*b) == 1
