@@ -13,14 +13,15 @@
 //    dealt out wave by wave.  Lane l owns the 16-byte column vectors
 //    l, l + 64, ... (NJ <= 4 of them: C <= 2048 in bf16, 1024 in fp32; wider
 //    rows take the generic kernels below), so each row
-//    is read with fully coalesced 16-byte loads and the lane's weight slice
-//    and its dweight / dbias sums stay in registers for all its rows.
-//  * The next row's dout and inp are loaded before the current row's
-//    reductions, so every wave keeps two rows in flight.
+//    is read with fully coalesced 16-byte loads; the weight row sits in LDS
+//    and the lane's dweight / dbias sums stay in registers for all its rows.
+//  * Each wave keeps two rows in flight: the loads of its next row (dout,
+//    inp, the old dinp, mean, rstd) are issued before it works on the
+//    current one.
 //  * The two row means are wave reductions (xor shuffles, fixed order).
 //  * dweight / dbias: each workgroup adds its 8 waves' sums in LDS in wave
 //    order and writes one fp32 partial row of 2C values; a second launch sums
-//    the partials of all workgroups in workgroup order (16 interleaved groups
+//    the partials of all workgroups in a fixed order (32 interleaved groups
 //    per column, then the groups in order), adds the old values and rounds
 //    once.  No atomics: results repeat bit for bit.
 //  * bf16 storage: values widen exactly to fp32, all arithmetic is fp32, each
@@ -74,11 +75,13 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
         const int col = V * (lane + 64 * j);
         off[j] = (uint32_t)(col * (int)sizeof(T)) | oob_if_ge(col, C);
     }
-    u32x4 w[NJ];
+    // the weight row, shared by the workgroup's waves: vector v at wl[v]
+    __shared__ u32x4 wl[64 * NJ];
     {
         const auto rw = make_rsrc(p.weight, rowbytes);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) w[j] = buffer_load16(rw, off[j], 0);
+        for (int v = tid; v < 64 * NJ; v += LN_NT)
+            wl[v] = buffer_load16(rw, (uint32_t)(V * v * (int)sizeof(T)) | oob_if_ge(V * v, C), 0);
+        __syncthreads();
     }
     float aw[NJ][V], ab[NJ][V];
 #pragma unroll
@@ -91,51 +94,75 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     const T* dout = (const T*)p.dout;
     const T* inp = (const T*)p.inp;
     T* dinp = (T*)p.dinp;
-    u32x4 d[NJ], x[NJ];
-    auto load_row = [&](long long row) {
+    // Everything a row needs, loaded one row ahead: while a wave works on
+    // row r, the loads of its next row (dout, inp, the old dinp, mean, rstd)
+    // are in flight.  Rows past the end load zeros from an empty range.
+    struct RowSet {
+        u32x4 d[NJ], x[NJ], g[NJ];
+        float m, s;
+    };
+    auto load_set = [&](RowSet& S, long long row) {
         const bool live = row < p.BT;
-        const auto rd = make_rsrc(dout + (live ? row : 0) * C, live ? rowbytes : 0);
-        const auto rx = make_rsrc(inp + (live ? row : 0) * C, live ? rowbytes : 0);
+        const long long rr = live ? row : 0;
+        const long long n = live ? rowbytes : 0;
+        const auto rd = make_rsrc(dout + rr * C, n);
+        const auto rx = make_rsrc(inp + rr * C, n);
+        const auto rg = make_rsrc(dinp + rr * C, n);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            d[j] = buffer_load16(rd, off[j], 0);
-            x[j] = buffer_load16(rx, off[j], 0);
+            S.d[j] = buffer_load16(rd, off[j], 0);
+            S.x[j] = buffer_load16(rx, off[j], 0);
+            S.g[j] = buffer_load16(rg, off[j], 0);
         }
+        S.m = to_f32(((const T*)p.mean)[rr]);
+        S.s = to_f32(((const T*)p.rstd)[rr]);
     };
-    load_row(r);
     const float invC = 1.0f / (float)C;
-    for (; r < p.BT; r += nwaves) {
-        const float m = to_f32(((const T*)p.mean)[r]);
-        const float s = to_f32(((const T*)p.rstd)[r]);
-        float nrm[NJ][V], dn[NJ][V];
+    auto process = [&](RowSet& S, long long row) {
         float sa = 0.f, sb = 0.f;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < NJ; ++j) {
+            const u32x4 wj = wl[lane + 64 * j];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float dv = elem<T>(d[j], e);
-                nrm[j][e] = (elem<T>(x[j], e) - m) * s;
-                dn[j][e] = elem<T>(w[j], e) * dv;
-                sa += dn[j][e];
-                sb += dn[j][e] * nrm[j][e];
+                const float dv = elem<T>(S.d[j], e);
+                const float nrm = (elem<T>(S.x[j], e) - S.m) * S.s;
+                const float dn = elem<T>(wj, e) * dv;
+                sa += dn;
+                sb += dn * nrm;
                 ab[j][e] += dv;
-                aw[j][e] += nrm[j][e] * dv;
+                aw[j][e] += nrm * dv;
             }
-        // the next row's loads fly during the reductions and the update
-        load_row(r + nwaves);
+        }
         const float a = wave_sum(sa) * invC, b = wave_sum(sb) * invC;
-        const auto rg = make_rsrc(dinp + r * C, rowbytes);
-        u32x4 g[NJ];
+        // widen dout and inp again below instead of keeping 2 * NJ * V floats
+        // live across the reductions (empty register barrier, no instruction)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) g[j] = buffer_load16(rg, off[j], 0);
+        for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(S.d[j]), "+v"(S.x[j]));
+        const auto rg = make_rsrc(dinp + row * C, rowbytes);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
+            const u32x4 wj = wl[lane + 64 * j];
             float o[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                o[e] = elem<T>(g[j], e) + (dn[j][e] - a - nrm[j][e] * b) * s;
+            for (int e = 0; e < V; ++e) {
+                const float nrm = (elem<T>(S.x[j], e) - S.m) * S.s;
+                const float dn = elem<T>(wj, e) * elem<T>(S.d[j], e);
+                o[e] = elem<T>(S.g[j], e) + (dn - a - nrm * b) * S.s;
+            }
             __builtin_amdgcn_raw_buffer_store_b128(pack<T>(o), rg, off[j], 0, 0);
         }
+    };
+    RowSet A, B;
+    load_set(A, r);
+    while (r < p.BT) {
+        load_set(B, r + nwaves);
+        process(A, r);
+        r += nwaves;
+        if (r >= p.BT) break;
+        load_set(A, r + nwaves);
+        process(B, r);
+        r += nwaves;
     }
     // the 8 waves' column sums, added in wave order: [dweight | dbias]
     for (int wv = 0; wv < LN_NW; ++wv) {
@@ -159,9 +186,10 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
 }
 
 // dweight[i] += sum_g partial[g][i], dbias[i] += sum_g partial[g][C + i]:
-// 64 columns per workgroup, 16 groups of workgroup partials g = q, q + 16, ...
-// summed in order, then the 16 group sums in order.
-constexpr int RED_COLS = 64, RED_GROUPS = 16;
+// 32 columns per workgroup; 32 groups of workgroup partials g = q, q + 32, ...
+// each summed in order (all of a thread's loads issued before its adds),
+// then the 32 group sums in order.
+constexpr int RED_COLS = 32, RED_GROUPS = 32, RED_BATCH = 8;
 
 template <typename T>
 __global__ __launch_bounds__(RED_COLS * RED_GROUPS) void ln_bwd_reduce(LNParams p, int G) {
@@ -170,16 +198,15 @@ __global__ __launch_bounds__(RED_COLS * RED_GROUPS) void ln_bwd_reduce(LNParams 
     const int col = blockIdx.x * RED_COLS + c;   // over 2C: dweight then dbias
     const int C2 = 2 * p.C;
     float acc = 0.f;
-    if (col < C2) {
-        int g = q;
-        for (; g + 3 * RED_GROUPS < G; g += 4 * RED_GROUPS) {
-            const float v0 = p.partial[(long long)g * C2 + col];
-            const float v1 = p.partial[(long long)(g + RED_GROUPS) * C2 + col];
-            const float v2 = p.partial[(long long)(g + 2 * RED_GROUPS) * C2 + col];
-            const float v3 = p.partial[(long long)(g + 3 * RED_GROUPS) * C2 + col];
-            acc = (((acc + v0) + v1) + v2) + v3;
+    for (int g0 = q; g0 < G; g0 += RED_BATCH * RED_GROUPS) {
+        float v[RED_BATCH];
+#pragma unroll
+        for (int k = 0; k < RED_BATCH; ++k) {
+            const int g = g0 + k * RED_GROUPS;
+            v[k] = (g < G && col < C2) ? p.partial[(long long)g * C2 + col] : 0.f;
         }
-        for (; g < G; g += RED_GROUPS) acc += p.partial[(long long)g * C2 + col];
+#pragma unroll
+        for (int k = 0; k < RED_BATCH; ++k) acc += v[k];
     }
     s[q][c] = acc;
     __syncthreads();
