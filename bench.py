@@ -145,10 +145,27 @@ def forward_flops(case) -> int:
     return 2 * case.BT * case.C * case.OC + (case.BT * case.OC if case.with_bias else 0)
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources: counters taken on other sources are stale."""
+# the sources each kernel's code and launch plan come from (the shared headers
+# and the planner included); counters taken on other sources are stale
+_COMMON = ["mmb_internal.h", "mmb_numeric.h", "mmb_tile_common.h", "mmb_api.hip"]
+KERNEL_SOURCES = {
+    "mmb_tiles_bf16_kernel": ["mmb_tiles_bf16.hip"] + _COMMON,
+    "mmb_tiles_bf16_sr_kernel": ["mmb_tiles_bf16.hip"] + _COMMON,
+    "mmb_fwd_bf16_kernel": ["mmb_tiles_bf16.hip"] + _COMMON,
+    "mmb_tiles_kernel": ["mmb_tiles.hip"] + _COMMON,
+    "mmb_fwd_kernel": ["mmb_tiles.hip"] + _COMMON,
+    "ln_bwd_rows": ["mmb_layernorm.hip"] + _COMMON,
+}
+
+
+def source_digest(kernel: str = None) -> str:
+    """sha256 over the HIP sources of `kernel` (all of them when None)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "linear_layer_backward_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "linear_layer_backward_amd", "csrc")
+    names = KERNEL_SOURCES.get(kernel)
+    files = ([os.path.join(csrc, n) for n in sorted(names)] if names
+             else sorted(glob.glob(os.path.join(csrc, "*"))))
+    for f in files:
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
@@ -168,7 +185,7 @@ def measured_traffic(kernel: str, cfg: int, slug: str = None):
     text = open(path).read()
     m = re.search(r"^source_digest:\s*(\w+)", text, re.M)
     b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m or not b or m.group(1) != source_digest():
+    if not m or not b or m.group(1) != source_digest(kernel):
         return None
     return float(b.group(1))
 
@@ -206,7 +223,7 @@ def summarize_counters(cfg: int, dirs, copy_mib: int, op: str = "backward") -> s
     lines = [
         f"kernel: {kernel}",
         f"workload: {wl.CONFIG_NAMES[cfg]}" + (" (forward product)" if op == "forward" else ""),
-        f"source_digest: {source_digest()}",
+        f"source_digest: {source_digest(kernel)}",
         f"copy calibration: {copy_mib} MiB each way; FETCH_SIZE {cf:.1f} ({ncf} dispatches), "
         f"WRITE_SIZE {cw:.1f} ({ncw}); scale fetch {sf:.4f}, write {sw:.4f}",
         f"kernel FETCH_SIZE mean {kf:.1f} over {nkf} dispatches -> {fetch_b:.4e} bytes",
