@@ -747,8 +747,14 @@ int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, con
         DeviceInfo di;
         st = device_info(dev, &di);
         if (st != MMB_OK) return st;
-        // one workgroup of 8 row-waves per CU (fewer for few rows)
-        G = (int)std::max(1LL, std::min<long long>(di.cus, (p.BT + 7) / 8));
+        // one workgroup of 8 row-waves per CU (fewer for few rows);
+        // MMB_LN_WORKGROUPS overrides the count (tuning aid)
+        long long want = di.cus;
+        if (const char* e = std::getenv("MMB_LN_WORKGROUPS")) {
+            const long v = std::strtol(e, nullptr, 10);
+            if (v > 0) want = std::min(v, 1L << 16);
+        }
+        G = (int)std::max(1LL, std::min<long long>(want, (p.BT + 7) / 8));
         Workspace& w = g_ws[{dev, s}];
         st = grow(&w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
         if (st != MMB_OK) return st;

@@ -64,7 +64,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <typename T, int NJ>
 __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     constexpr int V = Vec<T>::N;
-    __shared__ float red[2 * 64 * NJ * V];
+    constexpr int SLOT = 2 * 64 * NJ * V;     // one wave's [dweight | dbias] sums
+    __shared__ float red[LN_NW * SLOT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = p.C;
     const long long rowbytes = (long long)C * (long long)sizeof(T);
@@ -77,12 +78,6 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     }
     // the weight row, shared by the workgroup's waves: vector v at wl[v]
     __shared__ u32x4 wl[64 * NJ];
-    {
-        const auto rw = make_rsrc(p.weight, rowbytes);
-        for (int v = tid; v < 64 * NJ; v += LN_NT)
-            wl[v] = buffer_load16(rw, (uint32_t)(V * v * (int)sizeof(T)) | oob_if_ge(V * v, C), 0);
-        __syncthreads();
-    }
     float aw[NJ][V], ab[NJ][V];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -155,6 +150,13 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     };
     RowSet A, B;
     load_set(A, r);
+    // staged while the first row's loads fly
+    {
+        const auto rw = make_rsrc(p.weight, rowbytes);
+        for (int v = tid; v < 64 * NJ; v += LN_NT)
+            wl[v] = buffer_load16(rw, (uint32_t)(V * v * (int)sizeof(T)) | oob_if_ge(V * v, C), 0);
+        __syncthreads();
+    }
     while (r < p.BT) {
         load_set(B, r + nwaves);
         process(A, r);
@@ -164,24 +166,28 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
         process(B, r);
         r += nwaves;
     }
-    // the 8 waves' column sums, added in wave order: [dweight | dbias]
-    for (int wv = 0; wv < LN_NW; ++wv) {
-        if (wave == wv) {
+    // the 8 waves' column sums [dweight | dbias], each wave in its own slot,
+    // then added in wave order per column
+    float* mine = red + wave * SLOT;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const int i = V * (lane + 64 * j) + e;
-                    red[i] = wv == 0 ? aw[j][e] : red[i] + aw[j][e];
-                    red[64 * NJ * V + i] = wv == 0 ? ab[j][e] : red[64 * NJ * V + i] + ab[j][e];
-                }
+        for (int e = 0; e < V; ++e) {
+            const int i = V * (lane + 64 * j) + e;
+            mine[i] = aw[j][e];
+            mine[64 * NJ * V + i] = ab[j][e];
         }
-        __syncthreads();
-    }
+    __syncthreads();
     float* part = p.partial + (long long)blockIdx.x * 2 * C;
     for (int i = tid; i < C; i += LN_NT) {
-        part[i] = red[i];
-        part[C + i] = red[64 * NJ * V + i];
+        float sw = red[i], sb = red[64 * NJ * V + i];
+#pragma unroll
+        for (int wv = 1; wv < LN_NW; ++wv) {
+            sw += red[wv * SLOT + i];
+            sb += red[wv * SLOT + 64 * NJ * V + i];
+        }
+        part[i] = sw;
+        part[C + i] = sb;
     }
 }
 
