@@ -151,3 +151,16 @@ def test_sr_rejects_bad_arguments(dev):
     from linear_layer_backward_amd import mmb
     with pytest.raises(mmb.MmbError):
         mmb.mmb_backward_sr(0, 0, 0, 0, 0, 0, 1, 1, 8, 8, 1, None)
+
+
+def test_sr_without_bias(dev):
+    """dbias = NULL (the LM-head form): dweight bits still equal the oracle's,
+    on a shape with ragged tiles in every dimension."""
+    B, T, C, OC = 2, 300, 200, 392
+    case = wl.integer_case(B, T, C, OC, "bf16", seed=12, lo=-4, hi=4, with_bias=False)
+    gi, gw, gb = run_sr(case, dev, 77)
+    assert gb is None
+    ri, rw, _ = oracle.backward_sr(case.dout, case.inp, case.weight, case.dinp0, case.dweight0,
+                                   False, seed=77, B=B, T=T, C=C, OC=OC)
+    np.testing.assert_array_equal(gw, rw)
+    np.testing.assert_array_equal(gi, round_bf16(ri))
