@@ -64,8 +64,13 @@ struct K {
     static_assert(BM / E * 8 <= kThreads && BN / E * 8 <= kThreads, "one staging pass");
 };
 
+// 16-byte chunk c of LDS row r sits at c ^ ((r >> 1) & 7): a fragment read
+// (16 consecutive rows, one chunk, per pass of a wave's ds_read_b128) then
+// touches 16 distinct 16-byte bank groups of the 64-bank LDS (group
+// 8 (r & 1) + (c ^ ((r >> 1) & 7))), and so does a staging store of two
+// consecutive rows' 8 chunks.  (Keyed on r & 7, rows r and r + 8 collided.)
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+    return row * kRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 // ---- E x E transpose of one staged block ---------------------------------
@@ -86,34 +91,35 @@ __device__ __forceinline__ void add_columns(const u32x4 (&in)[4], float (&s)[4],
         for (int x = 0; x < 4; ++x) s[x] += __uint_as_float(in[r][x]);
 }
 
-// ---- MFMA step over one LDS stage ----------------------------------------
+// ---- MFMA steps of one LDS stage ------------------------------------------
+// The fragments of one 8-deep substep s (one ds_read_b128 per block and lane).
 template <typename T>
-__device__ __forceinline__ void mma_stage(const char* sa, const char* sb, int wm0, int wn0,
-                                          int lane, f32x16 (&acc)[K<T>::MB][K<T>::NB]) {
+struct Frags {
+    u32x4 a[K<T>::NB], b[K<T>::MB];
+};
+template <typename T>
+__device__ __forceinline__ void read_frags(const char* sa, const char* sb, int s, int wm0, int wn0,
+                                           int lane, Frags<T>& f) {
     using Kt = K<T>;
-    const int lr = lane & 31, half = lane >> 5;
+    const int lr = lane & 31, chunk = 2 * s + (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int chunk = 2 * s + half;
-        u32x4 fa[Kt::NB], fb[Kt::MB];
+    for (int nb = 0; nb < Kt::NB; ++nb) f.a[nb] = *(const u32x4*)(sb + swz(wn0 + nb * 32 + lr, chunk));
 #pragma unroll
-        for (int nb = 0; nb < Kt::NB; ++nb)
-            fa[nb] = *(const u32x4*)(sb + swz(wn0 + nb * 32 + lr, chunk));
+    for (int mb = 0; mb < Kt::MB; ++mb) f.b[mb] = *(const u32x4*)(sa + swz(wm0 + mb * 32 + lr, chunk));
+}
+// lane half h holds k = 8s + 4h + q in element q: MFMA q reduces over the
+// pair {8s + q, 8s + 4 + q}; all four cover the 8 k.
+template <typename T>
+__device__ __forceinline__ void mma_sub(const Frags<T>& f, f32x16 (&acc)[K<T>::MB][K<T>::NB]) {
+    using Kt = K<T>;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int mb = 0; mb < Kt::MB; ++mb)
-            fb[mb] = *(const u32x4*)(sa + swz(wm0 + mb * 32 + lr, chunk));
-        // lane half h holds k = 8s + 4h + q in element q: MFMA q reduces over
-        // the pair {8s + q, 8s + 4 + q}; all four cover the 8 k.
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int mb = 0; mb < Kt::MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < Kt::NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        __uint_as_float(fa[nb][q]), __uint_as_float(fb[mb][q]), acc[mb][nb], 0, 0,
-                        0);
-    }
+            for (int nb = 0; nb < Kt::NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    __uint_as_float(f.a[nb][q]), __uint_as_float(f.b[mb][q]), acc[mb][nb], 0, 0, 0);
 }
 
 // ---- one work unit ---------------------------------------------------------
@@ -157,46 +163,46 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     for (int x = 0; x < E; ++x) bsum[x] = 0.f;
 
     static_assert(Kt::BN * 8 / kThreads == E, "K-contiguous B: E vectors per thread");
+    static_assert(APER == E, "4 vectors per operand and thread");
+    // Buffer-load geometry, fixed per thread: byte offsets from the stage's
+    // origin in the operand (the origin moves each stage, so every offset
+    // stays below 2^31).  Out-of-range vectors load zeros: columns past N or
+    // M through an offset of 2^31, rows past the operand's end because they
+    // fall outside the buffer range, K-contiguous vectors at or past K
+    // through a per-stage mask.
+    //   K-contiguous operand: vector j = row (tid >> 3) + 32 j, K 4 (tid & 7)
+    //   M/N-contiguous: vector r = K-row 4 kg + r, columns 4 xg .. 4 xg + 3
+    const long long a_elems = (long long)p.BT * lda;
+    const long long b_elems = OP == Op::DWEIGHT ? (long long)p.BT * p.C : (long long)p.OC * p.C;
+    uint32_t a_off[E], b_off[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const long long kc_row = (long long)((tid >> 3) + 32 * j);
+        if constexpr (AK)
+            a_off[j] = (uint32_t)((kc_row * lda + (tid & 7) * E) * 4);
+        else
+            a_off[j] = (uint32_t)((((long long)(kg * E + j)) * lda + m0 + xg * E) * 4) |
+                       oob_if_ge(m0 + xg * E, M);
+        if constexpr (BKC)
+            b_off[j] = (uint32_t)((kc_row * ldb + (tid & 7) * E) * 4);
+        else
+            b_off[j] = (uint32_t)((((long long)(kg * E + j)) * ldb + n0 + xg * E) * 4) |
+                       oob_if_ge(n0 + xg * E, N);
+    }
     auto load = [&](int kt) {
         const int k0 = kt * BK;
-        if constexpr (BKC) {
-            // B: rows n, 16-byte vectors along K
+        const uint32_t kmask = oob_if_ge(k0 + (tid & 7) * E, Kd);
+        {
+            const long long o = BKC ? (long long)n0 * ldb + k0 : (long long)k0 * ldb;
+            const auto r = make_rsrc(Bop + o, (b_elems - o) * 4);
 #pragma unroll
-            for (int j = 0; j < E; ++j) {
-                const int n = n0 + (tid >> 3) + 32 * j;
-                const int k = k0 + (tid & 7) * E;
-                rb[j] = (n < N && k < Kd) ? *(const u32x4*)(Bop + (long long)n * ldb + k)
-                                          : u32x4{0, 0, 0, 0};
-            }
-        } else {
-            // B: rows k (K-strided), E columns starting at n0 + xg*E
-            const int n = n0 + xg * E;
-            const bool colok = b_active && n < N;
-#pragma unroll
-            for (int r = 0; r < E; ++r) {
-                const int k = k0 + kg * E + r;
-                rb[r] = (colok && k < Kd) ? *(const u32x4*)(Bop + (long long)k * ldb + n)
-                                          : u32x4{0, 0, 0, 0};
-            }
+            for (int j = 0; j < E; ++j) rb[j] = buffer_load16(r, b_off[j] | (BKC ? kmask : 0u), 0);
         }
-        if constexpr (AK) {
-            // A: rows m, 16-byte vectors along K
+        {
+            const long long o = AK ? (long long)m0 * lda + k0 : (long long)k0 * lda;
+            const auto r = make_rsrc(A + o, (a_elems - o) * 4);
 #pragma unroll
-            for (int j = 0; j < APER; ++j) {
-                const int m = m0 + (tid >> 3) + 32 * j;
-                const int k = k0 + (tid & 7) * E;
-                ra[j] = (m < M && k < Kd) ? *(const u32x4*)(A + (long long)m * lda + k)
-                                          : u32x4{0, 0, 0, 0};
-            }
-        } else {
-            const int m = m0 + xg * E;
-            const bool colok = a_active && m < M;
-#pragma unroll
-            for (int r = 0; r < E; ++r) {
-                const int k = k0 + kg * E + r;
-                ra[r] = (colok && k < Kd) ? *(const u32x4*)(A + (long long)k * lda + m)
-                                          : u32x4{0, 0, 0, 0};
-            }
+            for (int j = 0; j < E; ++j) ra[j] = buffer_load16(r, a_off[j] | (AK ? kmask : 0u), 0);
         }
     };
 
@@ -237,17 +243,33 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
 
     const int wm0 = (wave & 1) * Kt::WM, wn0 = (wave >> 1) * Kt::WN;
 
+    // Fragments are read one substep ahead of the MFMAs that use them, and
+    // the stage barrier sits before the last substep's MFMAs, so the next
+    // stage's first fragments are read while those run.
     load(kt0);
     store(0);
     __syncthreads();
+    Frags<T> f0, f1;
+    read_frags<T>(smem, smem + BM * kRowBytes, 0, wm0, wn0, lane, f0);
     for (int kt = kt0; kt < kt1; ++kt) {
         const int cur = (kt - kt0) & 1;
         const bool more = kt + 1 < kt1;
         if (more) load(kt + 1);
         const char* sa = smem + cur * Kt::STAGE_BYTES;
-        mma_stage<T>(sa, sa + BM * kRowBytes, wm0, wn0, lane, acc);
+        const char* sb = sa + BM * kRowBytes;
+        read_frags<T>(sa, sb, 1, wm0, wn0, lane, f1);
+        mma_sub<T>(f0, acc);
+        read_frags<T>(sa, sb, 2, wm0, wn0, lane, f0);
+        mma_sub<T>(f1, acc);
+        read_frags<T>(sa, sb, 3, wm0, wn0, lane, f1);
+        mma_sub<T>(f0, acc);
         if (more) store(cur ^ 1);
         __syncthreads();
+        if (more) {
+            const char* na = smem + (cur ^ 1) * Kt::STAGE_BYTES;
+            read_frags<T>(na, na + BM * kRowBytes, 0, wm0, wn0, lane, f0);
+        }
+        mma_sub<T>(f1, acc);
     }
 
     // dbias: combine the 8 K-groups of each column (lanes differing in bits 0..2)
