@@ -66,7 +66,11 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     constexpr int V = Vec<T>::N;
     constexpr int SLOT = 2 * 64 * NJ * V;     // one wave's [dweight | dbias] sums
     __shared__ float red[LN_NW * SLOT];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // uniform per wave: the row index, and so every buffer descriptor built
+    // from it, stays in scalar registers (a per-lane value would make the
+    // compiler wrap each buffer access in a readfirstlane loop)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int C = p.C;
     const long long rowbytes = (long long)C * (long long)sizeof(T);
     // lane's vector j covers columns V * (lane + 64 j) .. + V - 1
