@@ -18,7 +18,7 @@
 //  * Each wave keeps two rows in flight: the loads of its next row (dout,
 //    inp, the old dinp, mean, rstd) are issued before it works on the
 //    current one.
-//  * The two row means are wave reductions (xor shuffles, fixed order).
+//  * The two row means are wave reductions in a fixed order (DPP lane moves).
 //  * dweight / dbias: each workgroup adds its 8 waves' sums in LDS in wave
 //    order and writes one fp32 partial row of 2C values; a second launch sums
 //    the partials of all workgroups in a fixed order (32 interleaved groups
@@ -55,10 +55,24 @@ __device__ __forceinline__ u32x4 pack(const float (&f)[Vec<T>::N]) {
     return o;
 }
 
+// Sum over the 64 lanes of a wave, in a fixed order, with DPP lane moves
+// (no LDS round trips): row_shr 1, 2, 4, 8 leave each 16-lane row's sum in
+// its lane 15; row_bcast15 adds row 0's into row 1 and row 2's into row 3;
+// row_bcast31 adds lane 31 into rows 2 and 3, so lane 63 holds the total.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                              true);
+    return v + __builtin_bit_cast(float, t);
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-    return v;
+    v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+    v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+    v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+    v = dpp_add<0x118, 0xF>(v);   // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 template <typename T, int NJ>
