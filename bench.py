@@ -43,6 +43,28 @@ METRIC_LN = "layernorm-backward GB/s (dinp+dweight+dbias) at the page's B=8 T=10
 HBM_PEAK_GBS = 8000.0
 
 
+def flushed_launch_ms(step, stream, K: int, flush_mib: int) -> float:
+    """Average duration of K launches, each after streaming a flush_mib MiB
+    device copy (larger than the 256 MB last-level cache and the L2s), timed
+    with HIP events on the launch stream: the cold-cache counterpart of the
+    warm, back-to-back figures."""
+    import torch
+    n = flush_mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=stream.device).fill_(1.0)
+    b = torch.empty_like(a)
+    ms = []
+    for _ in range(K):
+        b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del a, b
+    return float(np.mean(ms))
+
+
 def layernorm_bytes(c) -> int:
     """Algorithmic HBM bytes of one LayerNorm backward: read dout, inp and
     the old dinp and write dinp (BT*C each), read weight, mean and rstd, read
@@ -93,6 +115,7 @@ def bench_layernorm(args):
     torch.cuda.synchronize(dev)
     launch_ms = float(np.mean([a.elapsed_time(z) for a, z in ev]))
     nbytes = layernorm_bytes(c)
+    cold_ms = flushed_launch_ms(step, stream, K, args.flush_mib) if args.flush_mib > 0 else None
     out = {
         "metric": METRIC_LN, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -104,7 +127,10 @@ def bench_layernorm(args):
                      "frac": round(nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("ln_bwd_rows", 0, LN_SLUG),
                      "kernel": "ln_bwd_rows + ln_bwd_reduce (one call)",
-                     "launch_ms": round(launch_ms, 5)},
+                     "launch_ms": round(launch_ms, 5),
+                     "launch_ms_flushed": None if cold_ms is None else round(cold_ms, 5),
+                     "achieved_flushed": None if cold_ms is None
+                     else round(nbytes / (cold_ms * 1e-3) / 1e9, 1)},
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
@@ -322,6 +348,9 @@ def main(argv=None):
                     help="backward (the metric), the forward product at the same shapes, or the "
                          "bf16 backward with stochastically rounded dweight/dbias")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=512, metavar="MIB",
+                    help="also time each launch after streaming MIB MiB through the caches "
+                         "(cold-cache figure; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
@@ -421,6 +450,7 @@ def main(argv=None):
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    cold_ms = flushed_launch_ms(step, stream, K, args.flush_mib) if args.flush_mib > 0 else None
 
     flops = sum(forward_flops(c) if fwd else c.flops() for c in cases)
     dtype = cases[0].dtype
@@ -451,7 +481,10 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel": kernel,
-                     "launch_ms": round(launch_ms, 5)},
+                     "launch_ms": round(launch_ms, 5),
+                     "launch_ms_flushed": None if cold_ms is None else round(cold_ms, 5),
+                     "achieved_flushed": None if cold_ms is None
+                     else round(flops / (cold_ms * 1e-3) / 1e12, 2)},
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

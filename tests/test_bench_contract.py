@@ -47,3 +47,5 @@ def test_json_line(argv):
     assert r["bound"] in ("mfma", "hbm") and r["achieved"] > 0 and r["peak"] > 0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert r["traffic"] is None or r["traffic"] > 0
+    # the cold-cache figure: each launch after a 512 MiB stream through the caches
+    assert r["launch_ms_flushed"] > 0 and r["achieved_flushed"] > 0
