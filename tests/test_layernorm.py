@@ -50,6 +50,8 @@ SHAPES = [  # (B, T, C, dtype): row kernel with 1, 2 and 4 vectors per lane, rag
     (2, 33, 1000, "bf16"), (2, 50, 768, "f32"), (1, 70, 1024, "f32"), (3, 9, 100, "f32"),
     # generic kernels: C not a multiple of the vector width, or wider than the row kernel
     (2, 11, 1603, "bf16"), (1, 9, 2056, "bf16"), (2, 13, 1600, "f32"), (1, 4, 7, "f32"),
+    # degenerate: one row (one busy wave), one channel
+    (1, 1, 768, "bf16"), (1, 1, 8, "f32"), (3, 1, 1, "f32"), (1, 2, 1, "bf16"),
 ]
 
 
