@@ -224,3 +224,23 @@ def test_forward_and_backward_share_the_workspace(dev, monkeypatch):
         check(case, b, run_fwd(case, b, dev), exact=True)
         check_exact(case, run(case, dev))
     assert TOL["f32"] == 1e-4
+
+
+def test_forward_unaligned_pointers_take_generic_path(dev):
+    """Shapes the tiles accept, but out and inp start 2 bytes into their
+    buffers: the call takes the generic kernel and still matches."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    B, T, C, OC = 2, 40, 64, 96
+    case = wl.random_case(B, T, C, OC, "bf16", seed=31)
+    bias = wl.normal(32, (OC,), 0.02, "bf16")
+    _, xs = to_dev(np.concatenate([[0.0], case.inp.ravel()]), "bf16", dev)
+    _, w = to_dev(case.weight, "bf16", dev)
+    _, b = to_dev(bias, "bf16", dev)
+    _, outs = to_dev(np.full(B * T * OC + 1, np.nan, np.float32), "bf16", dev)
+    x, out = xs[1:], outs[1:]
+    assert mmb.mmb_forward_path(out, x, w, b, B, T, C, OC, mmb.MMB_BF16) == 0
+    mmb.mmb_forward_stream(out, x, w, b, B, T, C, OC, mmb.MMB_BF16, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    got = from_dev(out, "bf16").reshape(B * T, OC)
+    check(case, bias, got)

@@ -92,3 +92,21 @@ def test_layernorm_deterministic(dev):
     b = run_ln(c, dev)
     for x, y in zip(a, b):
         assert x.tobytes() == y.tobytes()
+
+
+def test_layernorm_unaligned_pointers_take_generic_path(dev):
+    """C fits the row kernel, but dinp and dout start 2 bytes into their
+    buffers: the call takes the generic kernels and still matches."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    c = wl.layernorm_case(2, 30, 768, "bf16", seed=8, prefill=True)
+    _, gis = to_dev(np.concatenate([[0.0], c.dinp0.ravel()]), "bf16", dev)
+    _, ds = to_dev(np.concatenate([[0.0], c.dout.ravel()]), "bf16", dev)
+    gi, d = gis[1:], ds[1:]
+    ins = [to_dev(a, "bf16", dev)[1] for a in (c.inp, c.weight, c.mean, c.rstd)]
+    gw, gb = to_dev(c.dweight0, "bf16", dev)[1], to_dev(c.dbias0, "bf16", dev)[1]
+    args = (gi, gw, gb, d, *ins, c.B, c.T, c.C, mmb.MMB_BF16)
+    assert mmb.mmb_layernorm_path(*args) == 0
+    mmb.mmb_layernorm_backward(*args, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    check(c, (from_dev(gi, "bf16").reshape(c.BT, c.C), from_dev(gw, "bf16"), from_dev(gb, "bf16")))
