@@ -10,17 +10,19 @@
 // The op is bound by HBM: per row it reads dout, inp and the old dinp and
 // writes dinp; the flops are a few per element.  gfx950 design:
 //  * One wave64 per row, 8 waves per workgroup, one workgroup per CU, rows
-//    dealt out wave by wave.  Lane l owns the 16-byte column vectors
-//    l, l + 64, ... (NJ <= 4 of them: C <= 2048 in bf16, 1024 in fp32; wider
-//    rows take the generic kernels below), so each row
-//    is read with fully coalesced 16-byte loads; the weight row sits in LDS
-//    and the lane's dweight / dbias sums stay in registers for all its rows.
+//    dealt out wave by wave (the row index is wave-uniform, so every buffer
+//    descriptor lives in scalar registers).  Lane l owns the 16-byte column
+//    vectors l, l + 64, ... (NJ <= 4 of them: C <= 2048 in bf16, 1024 in
+//    fp32; wider rows take the generic kernels below), so each row is read
+//    with fully coalesced 16-byte loads; the weight row sits in LDS and the
+//    lane's dweight / dbias sums stay in registers for all its rows.
 //  * Each wave keeps two rows in flight: the loads of its next row (dout,
 //    inp, the old dinp, mean, rstd) are issued before it works on the
 //    current one.
 //  * The two row means are wave reductions in a fixed order (DPP lane moves).
-//  * dweight / dbias: each workgroup adds its 8 waves' sums in LDS in wave
-//    order and writes one fp32 partial row of 2C values; a second launch sums
+//  * dweight / dbias: each wave writes its sums to its own LDS slot, each
+//    column is added over the 8 waves in wave order, and the workgroup
+//    writes one fp32 partial row of 2C values; a second launch sums
 //    the partials of all workgroups in a fixed order (32 interleaved groups
 //    per column, then the groups in order), adds the old values and rounds
 //    once.  No atomics: results repeat bit for bit.
