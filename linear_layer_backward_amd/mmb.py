@@ -288,3 +288,59 @@ def forward(out, inp, weight, bias=None, B=None, T=None, stream=None) -> None:
         stream = torch.cuda.current_stream(inp.device)
     with torch.cuda.device(inp.device):
         mmb_forward_stream(out, inp, weight, bias, B, T, C, OC, torch_dtype_code(dt), stream)
+
+
+def backward_sr(dinp, dweight, dbias, dout, inp, weight, seed, B=None, T=None,
+                stream=None) -> None:
+    """As backward() for bfloat16 tensors, with dweight and dbias rounded
+    stochastically under `seed` (see mmb_backward_sr in include/mmb.h)."""
+    import torch
+    ts = [dinp, dweight, dout, inp, weight] + ([dbias] if dbias is not None else [])
+    for t in ts:
+        if (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16
+                or t.device != dout.device):
+            raise ValueError("tensors must be contiguous bfloat16 on one GPU")
+    OC = dout.shape[-1]
+    if B is None or T is None:
+        if dout.dim() != 3:
+            raise ValueError("give B and T for a 2-D dout")
+        B, T = dout.shape[0], dout.shape[1]
+    if dout.numel() != B * T * OC or weight.numel() % OC != 0:
+        raise ValueError("inconsistent shapes")
+    C = weight.numel() // OC
+    if inp.numel() != B * T * C or dinp.numel() != B * T * C or dweight.numel() != OC * C:
+        raise ValueError("inconsistent shapes")
+    if dbias is not None and dbias.numel() != OC:
+        raise ValueError("dbias must hold OC elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(dout.device)
+    with torch.cuda.device(dout.device):
+        mmb_backward_sr(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, seed, stream)
+
+
+def layernorm_backward(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B=None, T=None,
+                       stream=None) -> None:
+    """LayerNorm backward, every output accumulating (see
+    mmb_layernorm_backward in include/mmb.h).  Tensors contiguous on one GPU,
+    all float32 or all bfloat16: dout, inp, dinp [B, T, C] (or B*T*C elements
+    with B and T given), weight, dweight, dbias [C], mean, rstd [B*T]."""
+    import torch
+    ts = [dinp, dweight, dbias, dout, inp, weight, mean, rstd]
+    dt = dout.dtype
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.device != dout.device:
+            raise ValueError("tensors must be contiguous, on one GPU, and share one dtype")
+    C = weight.numel()
+    if B is None or T is None:
+        if dout.dim() != 3:
+            raise ValueError("give B and T for a 2-D dout")
+        B, T = dout.shape[0], dout.shape[1]
+    if dout.numel() != B * T * C or inp.numel() != B * T * C or dinp.numel() != B * T * C:
+        raise ValueError("inconsistent shapes")
+    if dweight.numel() != C or dbias.numel() != C or mean.numel() != B * T or rstd.numel() != B * T:
+        raise ValueError("inconsistent shapes")
+    if stream is None:
+        stream = torch.cuda.current_stream(dout.device)
+    with torch.cuda.device(dout.device):
+        mmb_layernorm_backward(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C,
+                               torch_dtype_code(dt), stream)

@@ -110,3 +110,22 @@ def test_layernorm_unaligned_pointers_take_generic_path(dev):
     mmb.mmb_layernorm_backward(*args, torch.cuda.current_stream(dev))
     torch.cuda.synchronize(dev)
     check(c, (from_dev(gi, "bf16").reshape(c.BT, c.C), from_dev(gw, "bf16"), from_dev(gb, "bf16")))
+
+
+def test_layernorm_tensor_binding(dev):
+    import torch
+    from linear_layer_backward_amd import mmb
+    c = wl.layernorm_case(2, 40, 768, "bf16", seed=9, prefill=True)
+
+    def t(a, shape=None):
+        x = torch.from_numpy(np.asarray(a, np.float32)).to(dev).to(torch.bfloat16)
+        return x.reshape(shape) if shape else x
+    gi = t(c.dinp0, (c.B, c.T, c.C))
+    gw, gb = t(c.dweight0), t(c.dbias0)
+    mmb.layernorm_backward(gi, gw, gb, t(c.dout, (c.B, c.T, c.C)), t(c.inp, (c.B, c.T, c.C)),
+                           t(c.weight), t(c.mean), t(c.rstd))
+    torch.cuda.synchronize(dev)
+    check(c, (gi.float().cpu().numpy().reshape(c.BT, c.C).astype(np.float64),
+              gw.float().cpu().numpy().astype(np.float64), gb.float().cpu().numpy().astype(np.float64)))
+    with pytest.raises(ValueError):
+        mmb.layernorm_backward(gi, gw.float(), gb, gi, gi, gw, t(c.mean), t(c.rstd))

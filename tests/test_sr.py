@@ -164,3 +164,25 @@ def test_sr_without_bias(dev):
                                    False, seed=77, B=B, T=T, C=C, OC=OC)
     np.testing.assert_array_equal(gw, rw)
     np.testing.assert_array_equal(gi, round_bf16(ri))
+
+
+def test_sr_tensor_binding(dev):
+    """The tensor-level call gives the same bits as the C entry point."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    B, T, C, OC = 2, 64, 128, 256
+    case = wl.integer_case(B, T, C, OC, "bf16", seed=13, lo=-4, hi=4)
+    gi_ref, gw_ref, gb_ref = run_sr(case, dev, 21)
+
+    def t(a, shape=None):
+        x = torch.from_numpy(np.asarray(a, np.float32)).to(dev).to(torch.bfloat16)
+        return x.reshape(shape) if shape else x
+    gi, gw, gb = t(case.dinp0, (B, T, C)), t(case.dweight0), torch.zeros(OC, device=dev,
+                                                                            dtype=torch.bfloat16)
+    mmb.backward_sr(gi, gw, gb, t(case.dout, (B, T, OC)), t(case.inp), t(case.weight), 21)
+    torch.cuda.synchronize(dev)
+    bits = lambda x: x.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    np.testing.assert_array_equal(bits(gw), gw_ref.ravel())
+    np.testing.assert_array_equal(bits(gb), gb_ref)
+    with pytest.raises(ValueError):
+        mmb.backward_sr(gi.float(), gw, gb, t(case.dout, (B, T, OC)), t(case.inp), t(case.weight), 1)
