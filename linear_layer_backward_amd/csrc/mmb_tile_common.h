@@ -230,6 +230,63 @@ __device__ __forceinline__ void write_tile_bias(T* D, long long ldd, int M, int 
     add_round_write<T, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0);
 }
 
+// beta = 0 with the bias added in registers (the bf16 forward): D = acc +
+// bias[n], rounded once, with no bias rows in LDS.  bv[nb][q] holds the 4
+// bias values (bf16) of the lane's columns n0 + wn0 + nb*32 + 8q + 4*(lane/32)
+// .. +3, loaded by load_bias_frags (zeros past N or without a bias); the
+// tile then leaves LDS row-contiguously as in add_round_write.
+template <int NB>
+__device__ __forceinline__ void load_bias_frags(const bf16_t* bias, int N, int n0, int wn0, int lane,
+                                                u32x2 (&bv)[NB][4]) {
+    const auto rb = make_rsrc(bias + (bias ? n0 : 0), bias ? (long long)(N - n0) * 2 : 0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = wn0 + nb * 32 + 8 * q + 4 * (lane >> 5);
+            bv[nb][q] = __builtin_amdgcn_raw_buffer_load_b64(
+                rb, (uint32_t)(2 * col) | oob_if_ge(n0 + col, N), 0, 0);
+        }
+}
+
+template <int MB, int NB, int NT, int BM, int BN>
+__device__ __forceinline__ void bias_round_write(bf16_t* D, long long ldd, int M, int N, int m0,
+                                                 int n0, const f32x16 (&acc)[MB][NB], char* smem,
+                                                 int tid, int lane, int wm0, int wn0,
+                                                 const u32x2 (&bv)[NB][4]) {
+    typedef OutMap<bf16_t, NT, BM, BN> OM;
+    constexpr int PITCH = out_pitch<bf16_t, BM, BN>();
+    const auto r = out_rsrc(D, ldd, M, m0, n0);
+    const int ch = tid % OM::CHUNKS, row0 = tid / OM::CHUNKS;
+    const int lr = lane & 31, half = lane >> 5;
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = wm0 + mb * 32 + lr, col = wn0 + nb * 32 + 8 * q + 4 * half;
+                const u32x2 b = bv[nb][q];
+                const float o0 = acc[mb][nb][4 * q] + __uint_as_float(b[0] << 16);
+                const float o1 = acc[mb][nb][4 * q + 1] + __uint_as_float(b[0] & 0xffff0000u);
+                const float o2 = acc[mb][nb][4 * q + 2] + __uint_as_float(b[1] << 16);
+                const float o3 = acc[mb][nb][4 * q + 3] + __uint_as_float(b[1] & 0xffff0000u);
+                u32x2 w;
+                w[0] = f32x2_to_bf16x2_bits(o0, o1);
+                w[1] = f32x2_to_bf16x2_bits(o2, o3);
+                *(u32x2*)(smem + row * PITCH + 2 * col) = w;
+            }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < OM::PASSES; ++i) {
+        const int row = row0 + OM::ROWS_PER_PASS * i;
+        __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * PITCH + 16 * ch), r,
+                                              out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, i),
+                                              0, 0);
+    }
+}
+
 // ---- split-K ---------------------------------------------------------------
 // A workgroup's partial tile (fp32), in fragment order: thread tid's group q
 // of block (mb, nb) lives at float ((mb * NB + nb) * 4 + q) * 4 * NT + tid * 4

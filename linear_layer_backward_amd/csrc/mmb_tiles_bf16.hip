@@ -246,6 +246,8 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const int bias_byte = bias_r * MN_PITCH + ((bias_c ^ sw_mn(bias_r)) << 4);
 
     const int wm0 = (wave & 1) * WM, wn0 = (wave >> 1) * WN;
+    // forward: the bias values of this lane's accumulator columns
+    u32x2 bv[NB][4];
 
     // Fragments of one 16-deep substep.
     struct Frag {
@@ -310,6 +312,9 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             constexpr bool LAST = decltype(last)::value;
             const int cur = it & 1;
             if (do_bias) bias_add(cur);
+            // the forward's bias, fetched while the last stage computes
+            if constexpr (LAST && OP == Op::FWD)
+                load_bias_frags<NB>((const bf16_t*)p.bias, N, n0, wn0, lane, bv);
             // substeps 0..2: pair j of stage it+1 to LDS, pair j of stage it+2
             // into the registers, fragments of substep j+1, MFMAs of substep j
 #pragma unroll
@@ -380,8 +385,9 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             write_tile_bias<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
                                                         wm0, wn0, (const bf16_t*)p.bias);
     } else if (!BETA1) {
-        write_tile_bias<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0,
-                                                    wn0, (const bf16_t*)p.bias);
+        if (nk == 0) load_bias_frags<NB>((const bf16_t*)p.bias, N, n0, wn0, lane, bv);
+        bias_round_write<MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0,
+                                             bv);
     } else if (nk > 0) {
         // the last K iteration loaded passes 0..7 of the old tile
         static_assert(LOADS == 4, "the old tile's first 8 passes sit in the 4 staging pairs");
