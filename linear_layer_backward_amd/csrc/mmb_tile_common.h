@@ -42,6 +42,10 @@ __device__ __forceinline__ uint32_t oob_if_ge(int i, int n) {
 // XCDs once the store has completed (s_waitcnt), with no L2 write-back or
 // invalidate of unrelated lines.
 constexpr int kAgentCoherent = 16;   // cache-policy bit SC1
+// Cache-policy bit NT (non-temporal): for output tiles that nothing in the
+// launch reads again, so that they do not displace the operand slabs that
+// later tiles reuse in L2.
+constexpr int kStreamOut = 2;
 __device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, kAgentCoherent);
 }
@@ -234,7 +238,9 @@ __device__ __forceinline__ void write_tile_bias(T* D, long long ldd, int M, int 
 // bias[n], rounded once, with no bias rows in LDS.  bv[nb][q] holds the 4
 // bias values (bf16) of the lane's columns n0 + wn0 + nb*32 + 8q + 4*(lane/32)
 // .. +3, loaded by load_bias_frags (zeros past N or without a bias); the
-// tile then leaves LDS row-contiguously as in add_round_write.
+// tile then leaves LDS row-contiguously as in add_round_write, with
+// non-temporal stores (measured 2-3 % faster on the forward; no change on
+// the backward's epilogues, which keep the default policy).
 template <int NB>
 __device__ __forceinline__ void load_bias_frags(const bf16_t* bias, int N, int n0, int wn0, int lane,
                                                 u32x2 (&bv)[NB][4]) {
@@ -283,7 +289,7 @@ __device__ __forceinline__ void bias_round_write(bf16_t* D, long long ldd, int M
         const int row = row0 + OM::ROWS_PER_PASS * i;
         __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(smem + row * PITCH + 16 * ch), r,
                                               out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, i),
-                                              0, 0);
+                                              0, kStreamOut);
     }
 }
 
