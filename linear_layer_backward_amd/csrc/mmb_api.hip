@@ -453,6 +453,36 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
             }
         }
     }
+    // Tail splits: with the dinp tiles unsplit, also try splitting only the
+    // dinp tiles of the last `rows` tile rows.  The launch order runs those
+    // last (more splits, shorter units), so they fill the slots that
+    // free up while the last wave of whole units is still running.  The
+    // model is optimistic about these layouts (GPT-2 XL fc, 8x1024x1600x6400
+    // bf16: 11 % predicted, 1-3 % measured), so one is taken only when it is
+    // modelled at least 5 % faster than the best uniform layout.
+    if (force_w.empty() && force_i.empty() && best_L.splits[UNIT_DINP][0] == 1) {
+        const GemmPlan& gi = g[UNIT_DINP];
+        const Layout base = best_L;
+        const double uniform_best = best;
+        best = uniform_best * 0.95;   // the margin a tail layout has to beat
+        for (int s2 = 2; s2 <= std::min(4, max_s[1]); ++s2)
+            for (int eighths = 1; eighths <= 4; ++eighths) {
+                const int rows = gi.tiles_m * eighths / 8;
+                if (rows < 1) continue;
+                Layout L = base;
+                for (int t = 0; t < ntiles[1]; ++t)
+                    if (t / gi.tiles_n >= gi.tiles_m - rows) L.splits[UNIT_DINP][t] = s2;
+                const double t = plan_cost(g, L, dev, cm, tile_bytes, trace ? 1e300 : best);
+                if (trace)
+                    std::fprintf(stderr, "mmb plan: dweight splits %d, dinp splits %d on the last %d "
+                                 "tile rows: cost %.2f us\n", L.splits[UNIT_DWEIGHT][0], s2, rows, t);
+                if (t < best - 1e-9) {
+                    best = t;
+                    best_L = L;
+                }
+            }
+        if (best >= uniform_best * 0.95) best = uniform_best;   // none cleared the margin
+    }
     const std::vector<int>* lists[2] = {&force_w, &force_i};
     for (int k = 0; k < 2; ++k) {
         if (lists[k]->size() <= 1) continue;

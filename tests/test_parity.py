@@ -346,9 +346,13 @@ def test_full_config(dev, cfg):
 
 
 @pytest.mark.parametrize("shape", [(8, 1024, 768, 2304, "f32"), (8, 1024, 3072, 768, "f32"),
-                                   (16, 1024, 768, 3072, "bf16"), (8, 1024, 768, 50304, "bf16")],
-                         ids=["qkv", "fc_proj", "fc_bf16", "lm_head"])
+                                   (16, 1024, 768, 3072, "bf16"), (8, 1024, 768, 50304, "bf16"),
+                                   (8, 1024, 1600, 6400, "bf16")],
+                         ids=["qkv", "fc_proj", "fc_bf16", "lm_head", "xl_fc_tail_split"])
 def test_full_shape_integer_exact(dev, shape):
+    """Exact at full GPT-2 shapes (sampled rows, all of dbias).  The GPT-2 XL
+    fc shape is one whose default plan splits only the dinp tiles that run
+    last (dinp split 2 on the last 12 of 32 tile rows)."""
     B, T, C, OC, dt = shape
     case = wl.integer_case(B, T, C, OC, dt, seed=OC, with_bias=OC != 50304, prefill=True)
     print(f"[parity] {case.name}", flush=True)
