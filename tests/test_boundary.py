@@ -130,7 +130,7 @@ def test_path_choice(mmb):
 @pytest.mark.parametrize("shape", [
     (16, 1024, 768, 3072, 1, True), (8, 1024, 768, 50304, 1, False),
     (8, 1024, 768, 2304, 0, True), (8, 1024, 3072, 768, 0, True), (2, 16, 64, 192, 0, True),
-    (3, 100, 200, 328, 0, True), (1, 1, 8, 8, 1, True)])
+    (3, 100, 200, 328, 0, True), (1, 1, 8, 8, 1, True), (8, 1024, 1600, 6400, 1, True)])
 @pytest.mark.parametrize("cus", [256, 32])
 def test_plan_covers_every_tile_and_split_once(mmb, shape, cus):
     B, T, C, OC, dt, bias = shape
@@ -230,6 +230,22 @@ def test_plan_picks_the_measured_best_splits(mmb, monkeypatch, shape, want):
     B, T, C, OC, dt, bias = shape
     (sw, si), _ = mmb.mmb_plan_units(B, T, C, OC, dt, bias, 256)
     assert (sw, si) == want
+
+
+def test_plan_tail_layout_on_gpt2_xl_fc(mmb, monkeypatch):
+    """GPT-2 XL fc (bf16, 256 CUs): the planner splits only the dinp tiles of
+    the last 12 of 32 tile rows, 2 ways, and those units launch after every
+    unsplit dinp unit, so they fill the slots that free up at the end."""
+    for k in ("MMB_SPLITS_DWEIGHT", "MMB_SPLITS_DINP", "MMB_PLAN_MODEL"):
+        monkeypatch.delenv(k, raising=False)
+    (sw, si), units = mmb.mmb_plan_units(8, 1024, 1600, 6400, 1, True, 256)
+    assert (sw, si) == (1, 2)
+    dinp = [(i, u) for i, u in enumerate(units) if u[0] == 1]
+    split = {(u[1], u[2]) for _, u in dinp if u[6] == 2}
+    assert split == {(m, n) for m in range(20, 32) for n in range(7)}
+    assert all(u[6] == 1 for u in units if u[0] == 0)
+    last_whole = max(i for i, u in dinp if u[6] == 1)
+    assert all(i > last_whole for i, u in dinp if u[6] == 2)
 
 
 def test_plan_model_override(mmb, monkeypatch):
