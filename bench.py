@@ -65,6 +65,52 @@ def flushed_launch_ms(step, stream, K: int, flush_mib: int) -> float:
     return float(np.mean(ms))
 
 
+def warm_up(step, stream, W: int, min_ms: float):
+    """W steps, then more, back to back, until at least min_ms of GPU time has
+    gone by: the GPU raises its clocks over the first tens of milliseconds of
+    continuous work, and a few warm-up steps would time that ramp instead of
+    the steady state a training loop runs in.  Returns (steps run, GPU ms)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n = 0
+    for _ in range(W):
+        step()
+        n += 1
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    while ms < min_ms:
+        # estimate the per-step time from what ran so far, then enqueue the rest
+        # in one batch (a probe of 4 steps when none ran yet)
+        per = ms / n if n else 0.0
+        batch = 4 if per <= 0 else max(1, min(100000, int((min_ms - ms) / per) + 1))
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(batch):
+            step()
+        b1.record(stream)
+        b1.synchronize()
+        ms += b0.elapsed_time(b1)
+        n += batch
+    return n, ms
+
+
+def backward_bytes(c) -> int:
+    """Algorithmic HBM bytes of one backward call: read dout, inp and weight
+    once, read and write dinp and dweight once, write dbias."""
+    es = 2 if c.dtype == "bf16" else 4
+    return es * (c.BT * c.OC + c.BT * c.C + c.OC * c.C + 2 * c.BT * c.C + 2 * c.OC * c.C
+                 + (c.OC if c.with_bias else 0))
+
+
+def forward_bytes(c) -> int:
+    """Algorithmic HBM bytes of one forward call: read inp, weight and the
+    bias once, write out."""
+    es = 2 if c.dtype == "bf16" else 4
+    return es * (c.BT * c.C + c.OC * c.C + (c.OC if c.with_bias else 0) + c.BT * c.OC)
+
+
 def layernorm_bytes(c) -> int:
     """Algorithmic HBM bytes of one LayerNorm backward: read dout, inp and
     the old dinp and write dinp (BT*C each), read weight, mean and rstd, read
@@ -93,8 +139,7 @@ def bench_layernorm(args):
     def step():
         mmb.mmb_layernorm_backward(*b, c.B, c.T, c.C, mmb.MMB_BF16, stream)
 
-    for _ in range(args.warmup):
-        step()
+    warm_steps, warm_ms = warm_up(step, stream, args.warmup, args.min_warmup_ms)
     torch.cuda.synchronize(dev)
     K = args.steps
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -118,7 +163,8 @@ def bench_layernorm(args):
     cold_ms = flushed_launch_ms(step, stream, K, args.flush_mib) if args.flush_mib > 0 else None
     out = {
         "metric": METRIC_LN, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "warmup_steps_run": warm_steps,
+        "warmup_ms": round(warm_ms, 1), "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": c.name, "B": c.B, "T": c.T, "C": c.C, "bytes_per_step": nbytes},
@@ -126,6 +172,7 @@ def bench_layernorm(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("ln_bwd_rows", 0, LN_SLUG),
+                     "lds_busy": measured_util("ln_bwd_rows", 0, "lds_util_pct", LN_SLUG),
                      "kernel": "ln_bwd_rows + ln_bwd_reduce (one call)",
                      "launch_ms": round(launch_ms, 5),
                      "launch_ms_flushed": None if cold_ms is None else round(cold_ms, 5),
@@ -214,6 +261,54 @@ def measured_traffic(kernel: str, cfg: int, slug: str = None):
     if not m or not b or m.group(1) != source_digest(kernel):
         return None
     return float(b.group(1))
+
+
+def measured_util(kernel: str, cfg: int, field: str, slug: str = None):
+    """A utilisation figure (percent) from the committed rocprofv3 counter
+    summary of this workload (<kernel>_<workload>_util.txt), if it was taken
+    on the current kernel sources."""
+    from linear_layer_backward_amd import workloads as wl
+    slug = slug or wl.CONFIG_SLUGS[cfg]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{slug}_util.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^source_digest:\s*(\w+)", text, re.M)
+    b = re.search(rf"^{field}:\s*([0-9.eE+-]+)", text, re.M)
+    if not m or not b or m.group(1) != source_digest(kernel):
+        return None
+    return float(b.group(1))
+
+
+# one rocprofv3 --pmc pass of utilisation counters (8 SQ counters and
+# GRBM_GUI_ACTIVE, within one pass's hardware limits)
+UTIL_COUNTERS = ["MfmaUtil", "LdsUtil", "VALUBusy", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_MFMA", "SQ_INSTS_LDS"]
+
+
+def summarize_util(kernel: str, workload: str, run_dir: str, digest_kernel: str = None) -> str:
+    """Text summary of one rocprofv3 --pmc pass of UTIL_COUNTERS over a
+    workload: the matrix-core busy share (MfmaUtil: MFMA busy cycles over the
+    SIMDs' active cycles), the LDS busy share (LdsUtil), VALU busy, the share
+    of wave cycles spent waiting on LDS instructions, and LDS bank conflicts
+    per LDS-active cycle."""
+    mean = {c: _counter_mean(run_dir, c, kernel)[0] for c in UTIL_COUNTERS}
+    n = _counter_mean(run_dir, "MfmaUtil", kernel)[1]
+    lds_wait = mean["SQ_WAIT_INST_LDS"] / mean["SQ_WAVE_CYCLES"] if mean["SQ_WAVE_CYCLES"] else 0
+    lines = [
+        f"kernel: {kernel}",
+        f"workload: {workload}",
+        f"source_digest: {source_digest(digest_kernel or kernel)}",
+        f"dispatches: {n}",
+        f"mfma_util_pct: {mean['MfmaUtil']:.2f}",
+        f"lds_util_pct: {mean['LdsUtil']:.2f}",
+        f"valu_busy_pct: {mean['VALUBusy']:.2f}",
+        f"lds_wait_share_of_wave_cycles_pct: {100 * lds_wait:.2f}",
+        f"lds_bank_conflict_cycles: {mean['SQ_LDS_BANK_CONFLICT']:.4e}",
+        f"mfma_instructions: {mean['SQ_INSTS_MFMA']:.4e}",
+        f"lds_instructions: {mean['SQ_INSTS_LDS']:.4e}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def _counter_mean(run_dir: str, counter: str, kernel: str):
@@ -342,6 +437,9 @@ def main(argv=None):
     # the GPU needs a few tens of milliseconds of back-to-back work to reach its
     # steady clocks: fewer warm-up steps measure the ramp, not the kernel
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0, metavar="MS",
+                    help="keep warming up, whatever --warmup says, until this much GPU time of "
+                         "back-to-back steps has run (the clocks ramp over the first tens of ms)")
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--op", default="backward",
                     choices=["backward", "forward", "backward_sr", "layernorm"],
@@ -353,11 +451,25 @@ def main(argv=None):
                          "(cold-cache figure; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-util", metavar="DIR",
+                    help="print the utilisation summary (MFMA, LDS, VALU busy) of the dominant "
+                         "kernel from a rocprofv3 --pmc run of bench.UTIL_COUNTERS in DIR")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
                     help="print the HBM-traffic summary from rocprofv3 --pmc output dirs: "
                          "workload FETCH_SIZE, workload WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
                          "(the copy run made with --copy-calibration MIB)")
     args = ap.parse_args(argv)
+
+    if args.summarize_util:
+        from linear_layer_backward_amd import workloads as wl
+        if args.op == "layernorm":
+            k, name = "ln_bwd_rows", "LayerNorm backward bf16 B=8 T=1024 C=1600"
+        else:
+            k = kernel_name(args.op, "bf16" if args.config >= 4 else "f32")
+            name = wl.CONFIG_NAMES[args.config] + (" (forward product)" if args.op == "forward"
+                                                    else "")
+        print(summarize_util(k, name, args.summarize_util), end="")
+        return 0
 
     if args.summarize_counters:
         print(summarize_counters(args.config, args.summarize_counters,
@@ -420,8 +532,7 @@ def main(argv=None):
                 mmb.mmb_backward_stream(b["dinp"], b["dweight"], b["dbias"], b["dout"], b["inp"],
                                         b["weight"], c.B, c.T, c.C, c.OC, code, stream)
 
-    for _ in range(args.warmup):
-        step()
+    warm_steps, warm_ms = warm_up(step, stream, args.warmup, args.min_warmup_ms)
     torch.cuda.synchronize(dev)
 
     # The K timed steps run back to back with nothing between them: an event
@@ -459,6 +570,8 @@ def main(argv=None):
     peak = PEAK_TFLOPS[dtype]
     kernel = kernel_name(args.op, dtype)
     traffic = measured_traffic(kernel, args.config)
+    nbytes = sum(forward_bytes(c) if fwd else backward_bytes(c) for c in cases)
+    gbs = lambda b: round(b / (launch_ms * 1e-3) / 1e9, 1)
 
     out = {
         "metric": METRIC_FORWARD if fwd else (METRIC_SR if sr else METRIC),
@@ -467,6 +580,8 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -477,11 +592,18 @@ def main(argv=None):
                    + (" (stochastic rounding)" if sr else ""),
                    "calls": [{"B": c.B, "T": c.T, "C": c.C, "OC": c.OC, "bias": c.with_bias}
                              for c in cases],
-                   "flops_per_step": flops},
+                   "flops_per_step": flops, "bytes_per_step": nbytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel": kernel,
                      "launch_ms": round(launch_ms, 5),
+                     # HBM rates against the 8 TB/s peak: algorithmic bytes, and the
+                     # copy-calibrated counter bytes, each over the launch duration
+                     "hbm_gbs_algorithmic": gbs(nbytes),
+                     "hbm_gbs_measured": None if traffic is None else gbs(traffic),
+                     "hbm_peak_gbs": HBM_PEAK_GBS,
+                     # matrix-core busy share of the kernel's cycles (rocprofv3 MfmaUtil)
+                     "mfma_busy": measured_util(kernel, args.config, "mfma_util_pct"),
                      "launch_ms_flushed": None if cold_ms is None else round(cold_ms, 5),
                      "achieved_flushed": None if cold_ms is None
                      else round(flops / (cold_ms * 1e-3) / 1e12, 2)},

@@ -43,6 +43,20 @@
  * in a fixed order).  Calls on different streams are independent; calls on
  * one stream are ordered by it.
  *
+ * Blocking: no entry point but mmb_release waits for the device.  The first
+ * call of a shape plans it on the host (up to about 0.1 s); the first call of
+ * a plan on a stream allocates that stream's copy of the work list
+ * (stream-ordered hipMallocAsync where the device supports memory pools) and
+ * copies it from pinned host memory with hipMemcpyAsync; a workspace that is
+ * too small is replaced in stream order (hipMallocAsync / hipFreeAsync).
+ * Where memory pools are missing, plain hipMalloc is used and replaced
+ * buffers are kept until mmb_release.
+ *
+ * Tuning variables (MMB_SPLITS_DWEIGHT, MMB_SPLITS_DINP, MMB_SPLITS_FWD,
+ * MMB_PLAN_MODEL, MMB_PLAN_TRACE, MMB_LN_WORKGROUPS) are read from the
+ * environment once, when the library is loaded; later changes to the
+ * environment have no effect.  mmb_set_tuning replaces one at run time.
+ *
  * All functions return MMB_OK (0) or a negative mmb_status; none of them
  * exits or aborts.
  */
@@ -66,7 +80,8 @@ typedef enum {
     MMB_ERR_OVERFLOW = -4,  /* B*T >= 2^31                                      */
     MMB_ERR_ALIAS = -5,     /* an output range overlaps another buffer's range */
     MMB_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed      */
-    MMB_ERR_NOMEM = -7      /* the workspace could not be allocated            */
+    MMB_ERR_NOMEM = -7,     /* the workspace could not be allocated            */
+    MMB_ERR_NAME = -8       /* mmb_set_tuning: not a tuning variable           */
 } mmb_status;
 
 /* The backward pass on the calling thread's current device, enqueued on the
@@ -93,8 +108,13 @@ int mmb_backward_stream(void* dinp, void* dweight, void* dbias,
  * (Salmon et al., SC 2011) keyed by (seed, tag), tag 1 for dweight and 2 for
  * dbias: element (row, col) (dbias: row 0, col o) uses bits 16*(col%4) ..
  * 16*(col%4)+15 of word (col%32)/8 of the block with counter
- * (row, 2*(col/32) + (col/4)%2, 0, 0).  The same seed gives the same bits on
- * every run and every split plan; non-finite values round to nearest. */
+ * (row, 2*(col/32) + (col/4)%2, 0, 0).  The random bits of an element depend
+ * only on (seed, tag, row, col), never on the launch plan, and the same seed
+ * gives the same output bits on every run of a plan.  The fp32 value being
+ * rounded is a sum whose order depends on the split-K plan (and so on the
+ * device's CU count and the split overrides): output bits are
+ * plan-independent only where those fp32 sums are exact (a different plan may
+ * move an element by one bf16 step).  Non-finite values round to nearest. */
 int mmb_backward_sr(void* dinp, void* dweight, void* dbias,
                     const void* dout, const void* inp, const void* weight,
                     int B, int T, int C, int OC, unsigned long long seed, void* stream);
@@ -219,6 +239,13 @@ int mmb_layernorm_path(const void* dinp, const void* dweight, const void* dbias,
 /* Synchronise every device the library has used, then free its workspaces.
  * The next call allocates again. */
 int mmb_release(void);
+
+/* Replace one tuning variable (see the file comment) for the rest of the
+ * process, or clear it when value is NULL; the planner's choices for later
+ * calls follow (plans already made for other values stay cached).  For
+ * tuning sweeps and tests.  Host only.  Returns MMB_OK, MMB_ERR_NULL for a
+ * NULL name or MMB_ERR_NAME for a name that is not a tuning variable. */
+int mmb_set_tuning(const char* name, const char* value);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,9 @@ def sources():
 
 def build(verbose: bool = False, extra=()) -> str:
     tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra, *sources(), "-o", tmp]
+    # roctx ranges around planning and launching (no-ops without a profiler)
+    libs = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
+    cmd = [HIPCC, *FLAGS, *extra, *sources(), *libs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

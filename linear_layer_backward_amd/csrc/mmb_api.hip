@@ -7,6 +7,7 @@
 // when the pointer is not NULL.  That launcher aborts the process on errors;
 // this one returns a status instead.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cstdint>
@@ -29,11 +30,11 @@ namespace {
 
 size_t elem_size(int dtype) { return dtype == MMB_BF16 ? 2 : 4; }
 
-struct Range {
+struct Span {
     uintptr_t lo, hi;  // [lo, hi)
 };
 
-bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
 
 int check(const void* dinp, const void* dweight, const void* dbias, const void* dout,
           const void* inp, const void* weight, int B, int T, int C, int OC, int dtype) {
@@ -44,11 +45,11 @@ int check(const void* dinp, const void* dweight, const void* dbias, const void* 
     if (BT > 0x7fffffffLL) return MMB_ERR_OVERFLOW;
     const uintptr_t es = elem_size(dtype);
     auto R = [&](const void* p, long long n) {
-        return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
+        return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
     };
-    const Range outs[3] = {R(dinp, BT * C), R(dweight, (long long)OC * C),
-                           dbias ? R(dbias, OC) : Range{0, 0}};
-    const Range ins[3] = {R(dout, BT * OC), R(inp, BT * C), R(weight, (long long)OC * C)};
+    const Span outs[3] = {R(dinp, BT * C), R(dweight, (long long)OC * C),
+                          dbias ? R(dbias, OC) : Span{0, 0}};
+    const Span ins[3] = {R(dout, BT * OC), R(inp, BT * C), R(weight, (long long)OC * C)};
     const int n_out = dbias ? 3 : 2;
     for (int a = 0; a < n_out; ++a) {
         for (int b = a + 1; b < n_out; ++b)
@@ -70,12 +71,12 @@ int check_fwd(const void* out, const void* inp, const void* weight, const void* 
     if (BT > 0x7fffffffLL) return MMB_ERR_OVERFLOW;
     const uintptr_t es = elem_size(dtype);
     auto R = [&](const void* p, long long n) {
-        return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
+        return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
     };
-    const Range o = R(out, BT * OC);
-    const Range ins[3] = {R(inp, BT * C), R(weight, (long long)OC * C),
-                          bias ? R(bias, OC) : Range{0, 0}};
-    for (const Range& r : ins)
+    const Span o = R(out, BT * OC);
+    const Span ins[3] = {R(inp, BT * C), R(weight, (long long)OC * C),
+                         bias ? R(bias, OC) : Span{0, 0}};
+    for (const Span& r : ins)
         if (overlap(o, r)) return MMB_ERR_ALIAS;
     return MMB_OK;
 }
@@ -107,6 +108,48 @@ int choose_path(const void* dinp, const void* dweight, const void* dout, const v
         if ((uintptr_t)p % 16 != 0) return 0;
     return 1;
 }
+
+// ---------------------------------------------------------------------------
+// tuning overrides
+
+// The MMB_* tuning variables (split overrides, planner constants, plan trace,
+// LayerNorm workgroup count) are read from the environment once, when the
+// library is loaded, so that a variable set later in the process cannot
+// change production plans; mmb_set_tuning replaces a value explicitly
+// (tuning sweeps, tests).  Guarded by g_mu.
+enum Tune { T_SPLITS_DWEIGHT, T_SPLITS_DINP, T_SPLITS_FWD, T_PLAN_MODEL, T_PLAN_TRACE,
+            T_LN_WORKGROUPS, T_COUNT };
+const char* const kTuneNames[T_COUNT] = {"MMB_SPLITS_DWEIGHT", "MMB_SPLITS_DINP",
+                                         "MMB_SPLITS_FWD",     "MMB_PLAN_MODEL",
+                                         "MMB_PLAN_TRACE",     "MMB_LN_WORKGROUPS"};
+
+struct Tuning {
+    bool set[T_COUNT];
+    std::string val[T_COUNT];
+    const char* get(int k) const { return set[k] ? val[k].c_str() : nullptr; }
+};
+
+Tuning load_tuning() {
+    Tuning t;
+    for (int k = 0; k < T_COUNT; ++k) {
+        const char* e = std::getenv(kTuneNames[k]);
+        t.set[k] = e != nullptr;
+        t.val[k] = e ? e : "";
+    }
+    return t;
+}
+
+std::mutex g_mu;                  // guards the tuning values, plans and workspaces
+Tuning g_tune = load_tuning();
+
+// A profiler range (roctx) around planning and launching, so that a trace
+// shows host cost next to kernel time; free when no profiler is attached.
+struct TraceRange {
+    explicit TraceRange(const char* what) { roctxRangePushA(what); }
+    ~TraceRange() { roctxRangePop(); }
+    TraceRange(const TraceRange&) = delete;
+    TraceRange& operator=(const TraceRange&) = delete;
+};
 
 // ---------------------------------------------------------------------------
 // planner
@@ -167,11 +210,11 @@ struct CostModel {
 // MMB_PLAN_MODEL="t_dweight,t_dinp,slow,busy_lo,busy_hi,prologue,epilogue,
 // publish,fix0,fix_per_partial,write,bytes_per_us" replaces the constants
 // (tuning aid for other devices or kernels).
-CostModel cost_model(int dtype) {
+CostModel cost_model(int dtype, const char* v) {
     CostModel cm = dtype == MMB_BF16
                        ? CostModel{{1.402, 1.263}, 0.7245, 0.9688, 0.9688, 0.78, 3.82, 8.47, 2.07, 2.51, 4.40, 10.16e6}
                        : CostModel{{3.356, 2.463}, 0.470, 0.130, 0.416, 1.22, 3.31, 3.93, 1.79, 1.68, 0.06, 20.73e6};
-    if (const char* v = std::getenv("MMB_PLAN_MODEL")) {
+    if (v) {
         double x[12];
         if (std::sscanf(v, "%lf,%lf,%lf,%lf,%lf,%lf,%lf,%lf,%lf,%lf,%lf,%lf", &x[0], &x[1], &x[2],
                         &x[3], &x[4], &x[5], &x[6], &x[7], &x[8], &x[9], &x[10], &x[11]) == 12)
@@ -413,8 +456,30 @@ std::vector<int> parse_splits(const char* v) {
     return out;
 }
 
+// What the planner takes from the tuning overrides.
+struct PlanOptions {
+    std::vector<int> force_w, force_i;   // split overrides (dweight / dinp, or the forward)
+    const char* model = nullptr;         // MMB_PLAN_MODEL constants, or NULL
+    bool trace = false;                  // print every modelled candidate to stderr
+};
+
+PlanOptions plan_options(const Tuning& t, bool fwd) {
+    PlanOptions o;
+    if (fwd) {
+        o.force_i = parse_splits(t.get(T_SPLITS_FWD));
+    } else {
+        o.force_w = parse_splits(t.get(T_SPLITS_DWEIGHT));
+        o.force_i = parse_splits(t.get(T_SPLITS_DINP));
+    }
+    o.model = t.get(T_PLAN_MODEL);
+    o.trace = t.get(T_PLAN_TRACE) != nullptr;
+    return o;
+}
+
 Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& dev,
-                const std::vector<int>& force_w, const std::vector<int>& force_i) {
+                const PlanOptions& opt) {
+    const std::vector<int>& force_w = opt.force_w;
+    const std::vector<int>& force_i = opt.force_i;
     const TileShape ts = tile_shape(dtype);
     GemmPlan g[2];
     // dweight[OC,C] += dout^T[OC,BT] . inp[BT,C]
@@ -423,12 +488,10 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     g[UNIT_DINP] = GemmPlan{BT, C, OC, cdiv(BT, ts.BM), cdiv(C, ts.BN), cdiv(OC, ts.BK), 0};
     g[UNIT_DINP].tile_base = g[UNIT_DWEIGHT].tiles_m * g[UNIT_DWEIGHT].tiles_n;
     const int ntiles[2] = {g[0].tiles_m * g[0].tiles_n, g[1].tiles_m * g[1].tiles_n};
-    const CostModel cm = cost_model(dtype);
+    const CostModel cm = cost_model(dtype, opt.model);
     const double tile_bytes = 4.0 * ts.BM * ts.BN;
     const int max_s[2] = {std::min(16, g[UNIT_DWEIGHT].kiters), std::min(8, g[UNIT_DINP].kiters)};
-
-    // MMB_PLAN_TRACE=1 prints the modelled cost of every candidate to stderr
-    const bool trace = std::getenv("MMB_PLAN_TRACE") != nullptr;
+    const bool trace = opt.trace;
     // one split count per GEMM (the unit encoding allows a count per tile)
     Layout best_L;
     double best = 1e300;
@@ -459,8 +522,10 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     // free up while the last wave of whole units is still running.  The
     // model is optimistic about these layouts (GPT-2 XL fc, 8x1024x1600x6400
     // bf16: 11 % predicted, 1-3 % measured), so one is taken only when it is
-    // modelled at least 5 % faster than the best uniform layout.
-    if (force_w.empty() && force_i.empty() && best_L.splits[UNIT_DINP][0] == 1) {
+    // modelled at least 5 % faster than the best uniform layout, and only for
+    // bf16, the kernel on which a tail layout was measured.
+    if (dtype == MMB_BF16 && force_w.empty() && force_i.empty() &&
+        best_L.splits[UNIT_DINP][0] == 1) {
         const GemmPlan& gi = g[UNIT_DINP];
         const Layout base = best_L;
         const double uniform_best = best;
@@ -517,16 +582,17 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
 // only its epilogue differs, adding the bias instead of the old output).
 // MMB_SPLITS_FWD forces the count as MMB_SPLITS_DINP does for dinp.
 Plan build_plan_forward(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& dev,
-                        const std::vector<int>& force) {
+                        const PlanOptions& opt) {
+    const std::vector<int>& force = opt.force_i;
     const TileShape ts = tile_shape(dtype);
     GemmPlan g[2];
     g[UNIT_DWEIGHT] = GemmPlan{0, 0, 0, 0, 0, 0, 0};
     g[UNIT_FWD] = GemmPlan{BT, OC, C, cdiv(BT, ts.BM), cdiv(OC, ts.BN), cdiv(C, ts.BK), 0};
     const int ntiles = g[UNIT_FWD].tiles_m * g[UNIT_FWD].tiles_n;
-    const CostModel cm = cost_model(dtype);
+    const CostModel cm = cost_model(dtype, opt.model);
     const double tile_bytes = 4.0 * ts.BM * ts.BN;
     const int max_s = std::min(8, g[UNIT_FWD].kiters);
-    const bool trace = std::getenv("MMB_PLAN_TRACE") != nullptr;
+    const bool trace = opt.trace;
     Layout best_L;
     double best = 1e300;
     for (int si = 1; si <= max_s; ++si) {
@@ -567,20 +633,41 @@ Plan build_plan_forward(int dtype, int BT, int C, int OC, bool bias, const Devic
 }
 
 // ---------------------------------------------------------------------------
-// state: plans per (device, shape) and workspaces per (device, stream)
+// state: plans per (device, shape, overrides) and workspaces per (device,
+// stream).  Nothing here waits for the device: a plan is never replaced (a
+// change of the overrides makes a new one), workspaces grow with
+// stream-ordered allocations, and a plan's work list reaches each stream with
+// an asynchronous copy on that stream.  Only mmb_release synchronises.
 
-struct Workspace {
-    void* counters = nullptr;
-    size_t counter_bytes = 0;
-    void* partials = nullptr;
-    size_t partial_bytes = 0;
+// Device memory in stream order where the device supports memory pools
+// (hipMallocAsync / hipFreeAsync), else plain hipMalloc; buffers of the
+// second kind that a kernel may still read are kept until mmb_release.
+struct DevAlloc {
+    void* ptr = nullptr;
+    bool async = false;
 };
 
-std::mutex g_mu;
+struct Workspace {
+    DevAlloc counters;
+    size_t counter_bytes = 0;
+    DevAlloc partials;
+    size_t partial_bytes = 0;
+    std::map<const void*, DevAlloc> tables;   // this stream's copy of each plan's work list
+};
+
+struct PlanEntry {
+    Plan plan;
+    int4* host_units = nullptr;   // pinned copy of the work list, source of the uploads
+};
+
+// key: device, dtype, BT, C, OC, bias, forward (1) or backward (0), and the
+// override string the plan was made with
+typedef std::tuple<int, int, int, int, int, bool, int, std::string> PlanKey;
 std::map<int, DeviceInfo> g_dev;
-// key: device, dtype, BT, C, OC, bias, forward (1) or backward (0)
-std::map<std::tuple<int, int, int, int, int, bool, int>, Plan> g_plans;
+std::map<int, bool> g_pools;       // device -> supports hipMallocAsync
+std::map<PlanKey, PlanEntry> g_plans;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_retired;   // (device, buffer) freed at release
 
 int device_info(int dev, DeviceInfo* out) {
     auto it = g_dev.find(dev);
@@ -594,6 +681,10 @@ int device_info(int dev, DeviceInfo* out) {
     // MI355X in its single-partition mode spreads 256 CUs over 8 XCDs, each
     // with its own L2; smaller partitions expose one XCD's CUs.
     set_topology(&d);
+    int pools = 0;
+    if (hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported, dev) != hipSuccess)
+        pools = 0;
+    g_pools[dev] = pools != 0;
     g_dev[dev] = d;
     *out = d;
     return MMB_OK;
@@ -601,80 +692,126 @@ int device_info(int dev, DeviceInfo* out) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int get_plan(int dev, int dtype, int BT, int C, int OC, bool bias, bool fwd, Plan** out) {
-    // MMB_SPLITS_DWEIGHT / MMB_SPLITS_DINP (backward) and MMB_SPLITS_FWD
-    // (forward) force the split counts (tuning sweeps, tests); unset lets the
-    // planner choose.
-    const char* ew = fwd ? nullptr : std::getenv("MMB_SPLITS_DWEIGHT");
-    const char* ei = std::getenv(fwd ? "MMB_SPLITS_FWD" : "MMB_SPLITS_DINP");
-    const std::string forced = std::string(ew ? ew : "") + "/" + (ei ? ei : "");
-    const auto key = std::make_tuple(dev, dtype, BT, C, OC, bias, fwd ? 1 : 0);
+int dev_alloc(int dev, DevAlloc* a, size_t bytes, hipStream_t s) {
+    a->ptr = nullptr;
+    a->async = g_pools[dev];
+    const hipError_t e = a->async ? hipMallocAsync(&a->ptr, bytes, s) : hipMalloc(&a->ptr, bytes);
+    if (e != hipSuccess) {
+        a->ptr = nullptr;
+        return MMB_ERR_NOMEM;
+    }
+    return MMB_OK;
+}
+
+// Free a buffer that work already enqueued on `s` may still use.
+void dev_retire(int dev, DevAlloc* a, hipStream_t s) {
+    if (!a->ptr) return;
+    if (a->async)
+        (void)hipFreeAsync(a->ptr, s);
+    else
+        g_retired.emplace_back(dev, a->ptr);
+    a->ptr = nullptr;
+}
+
+// The override string a plan is keyed by.
+std::string tuning_signature(const Tuning& t, bool fwd) {
+    const int keys[4] = {fwd ? T_SPLITS_FWD : T_SPLITS_DWEIGHT, fwd ? -1 : T_SPLITS_DINP,
+                         T_PLAN_MODEL, -1};
+    std::string sig;
+    for (int k : keys) {
+        if (k < 0) continue;
+        sig += t.set[k] ? "=" + t.val[k] : "-";
+        sig += "/";
+    }
+    return sig;
+}
+
+// The plan of a shape (made on first use; planning a new shape takes up to
+// about 0.1 s of host time and makes no HIP call).
+int find_plan(int dev, int dtype, int BT, int C, int OC, bool bias, bool fwd, PlanEntry** out) {
+    const PlanKey key(dev, dtype, BT, C, OC, bias, fwd ? 1 : 0, tuning_signature(g_tune, fwd));
     auto it = g_plans.find(key);
     if (it != g_plans.end()) {
-        if (it->second.forced == forced) {
-            *out = &it->second;
-            return MMB_OK;
-        }
-        // a kernel of the old plan may still read its unit table
-        if (hipDeviceSynchronize() != hipSuccess) return MMB_ERR_HIP;
-        (void)hipFree(it->second.d_units);
-        g_plans.erase(it);
+        *out = &it->second;
+        return MMB_OK;
     }
+    TraceRange range("mmb plan");
     DeviceInfo di;
     int st = device_info(dev, &di);
     if (st != MMB_OK) return st;
     di.slots = tiles_resident(dtype);
-    Plan p = fwd ? build_plan_forward(dtype, BT, C, OC, bias, di, parse_splits(ei))
-                 : build_plan(dtype, BT, C, OC, bias, di, parse_splits(ew), parse_splits(ei));
-    p.forced = forced;
-    const size_t ub = p.units.size() * sizeof(Unit);
-    if (hipMalloc(&p.d_units, ub) != hipSuccess) return MMB_ERR_NOMEM;
-    if (hipMemcpy(p.d_units, p.units.data(), ub, hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipFree(p.d_units);
-        return MMB_ERR_HIP;
-    }
-    p.proto.units = p.d_units;
+    const PlanOptions opt = plan_options(g_tune, fwd);
+    PlanEntry e;
+    e.plan = fwd ? build_plan_forward(dtype, BT, C, OC, bias, di, opt)
+                 : build_plan(dtype, BT, C, OC, bias, di, opt);
     static_assert(sizeof(Unit) == 2 * sizeof(int4), "two int4 per unit");
-    auto res = g_plans.emplace(key, std::move(p));
+    auto res = g_plans.emplace(key, std::move(e));
     *out = &res.first->second;
     return MMB_OK;
 }
 
-// Workspace: two allocations per (device, stream).  `counters` holds one
-// arrival counter per output tile and is only ever used for counters: it is
-// zeroed when allocated and every counter is reset by the last arriver of
-// its tile, so it is all zero at rest whatever plan ran before.  `partials`
-// holds [bias partials fp32][tile partials fp32] (each part 256-byte
-// aligned) and needs no initial value.
-int grow(void** buf, size_t* cap, size_t need, bool zero, hipStream_t s) {
-    if (need <= *cap) return MMB_OK;
-    const size_t want = std::max(need, *cap * 2);
-    if (*buf) {
-        if (hipStreamSynchronize(s) != hipSuccess) return MMB_ERR_HIP;
-        (void)hipFree(*buf);
-        *buf = nullptr;
-        *cap = 0;
+// This stream's device copy of a plan's work list: allocated and uploaded
+// (from a pinned host copy, asynchronously, in stream order) on the first
+// call of the plan on the stream.
+int stream_units(int dev, hipStream_t s, PlanEntry& e, Workspace& w, const int4** out) {
+    auto it = w.tables.find(&e);
+    if (it != w.tables.end()) {
+        *out = (const int4*)it->second.ptr;
+        return MMB_OK;
     }
-    if (hipMalloc(buf, want) != hipSuccess) {
-        *buf = nullptr;
-        return MMB_ERR_NOMEM;
+    const size_t ub = e.plan.units.size() * sizeof(Unit);
+    if (!e.host_units) {
+        if (hipHostMalloc((void**)&e.host_units, ub, hipHostMallocDefault) != hipSuccess) {
+            e.host_units = nullptr;
+            return MMB_ERR_NOMEM;
+        }
+        std::memcpy(e.host_units, e.plan.units.data(), ub);
     }
-    *cap = want;
-    if (zero && hipMemsetAsync(*buf, 0, want, s) != hipSuccess) return MMB_ERR_HIP;
+    DevAlloc t;
+    int st = dev_alloc(dev, &t, ub, s);
+    if (st != MMB_OK) return st;
+    if (hipMemcpyAsync(t.ptr, e.host_units, ub, hipMemcpyHostToDevice, s) != hipSuccess) {
+        dev_retire(dev, &t, s);
+        return MMB_ERR_HIP;
+    }
+    w.tables[&e] = t;
+    *out = (const int4*)t.ptr;
     return MMB_OK;
 }
 
-int get_workspace(int dev, hipStream_t s, const Plan& p, TilesParams* tp) {
+// Workspace: two buffers per (device, stream).  `counters` holds one arrival
+// counter per output tile and is only ever used for counters: it is zeroed
+// when allocated and every counter is reset by the last arriver of its tile,
+// so it is all zero at rest whatever plan ran before.  `partials` holds [bias
+// partials fp32][tile partials fp32] (each part 256-byte aligned) and needs
+// no initial value.  A buffer that is too small is replaced by one twice as
+// large (or as large as needed); the old one is freed in stream order.
+int grow(int dev, DevAlloc* buf, size_t* cap, size_t need, bool zero, hipStream_t s) {
+    if (need <= *cap) return MMB_OK;
+    const size_t want = std::max(need, *cap * 2);
+    dev_retire(dev, buf, s);
+    *cap = 0;
+    int st = dev_alloc(dev, buf, want, s);
+    if (st != MMB_OK) return st;
+    *cap = want;
+    if (zero && hipMemsetAsync(buf->ptr, 0, want, s) != hipSuccess) return MMB_ERR_HIP;
+    return MMB_OK;
+}
+
+int get_workspace(int dev, hipStream_t s, PlanEntry& e, TilesParams* tp) {
+    const Plan& p = e.plan;
     const size_t cb = (size_t)p.n_counters * 4;
     const size_t bb = align_up((size_t)p.ws_bias_floats * 4, 256);
     const size_t wb = align_up((size_t)p.ws_floats * 4, 256);
     Workspace& w = g_ws[{dev, s}];
-    int st = grow(&w.counters, &w.counter_bytes, cb, true, s);
+    int st = grow(dev, &w.counters, &w.counter_bytes, cb, true, s);
     if (st != MMB_OK) return st;
-    st = grow(&w.partials, &w.partial_bytes, bb + wb, false, s);
+    st = grow(dev, &w.partials, &w.partial_bytes, bb + wb, false, s);
     if (st != MMB_OK) return st;
-    char* b = (char*)w.partials;
-    tp->counters = (int*)w.counters;
+    st = stream_units(dev, s, e, w, &tp->units);
+    if (st != MMB_OK) return st;
+    char* b = (char*)w.partials.ptr;
+    tp->counters = (int*)w.counters.ptr;
     tp->ws_bias = (float*)b;
     tp->ws = (float*)(b + bb);
     return MMB_OK;
@@ -688,6 +825,7 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     if (st != MMB_OK) return st;
     const int BT = B * T;
     if (!choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype)) {
+        TraceRange range("mmb launch (generic)");
         return launch_generic(dtype, dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s, sr,
                               seed) == hipSuccess
                    ? MMB_OK
@@ -696,10 +834,11 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mu);
-    Plan* plan = nullptr;
-    st = get_plan(dev, dtype, BT, C, OC, dbias != nullptr, false, &plan);
+    PlanEntry* plan = nullptr;
+    st = find_plan(dev, dtype, BT, C, OC, dbias != nullptr, false, &plan);
     if (st != MMB_OK) return st;
-    TilesParams tp = plan->proto;
+    TraceRange range("mmb launch");
+    TilesParams tp = plan->plan.proto;
     st = get_workspace(dev, s, *plan, &tp);
     if (st != MMB_OK) return st;
     tp.dinp = dinp;
@@ -726,14 +865,14 @@ int check_ln(const void* dinp, const void* dweight, const void* dbias, const voi
     if (BT > 0x7fffffffLL) return MMB_ERR_OVERFLOW;
     const uintptr_t es = elem_size(dtype);
     auto R = [&](const void* p, long long n) {
-        return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
+        return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)n * es};
     };
-    const Range outs[3] = {R(dinp, BT * C), R(dweight, C), R(dbias, C)};
-    const Range ins[5] = {R(dout, BT * C), R(inp, BT * C), R(weight, C), R(mean, BT), R(rstd, BT)};
+    const Span outs[3] = {R(dinp, BT * C), R(dweight, C), R(dbias, C)};
+    const Span ins[5] = {R(dout, BT * C), R(inp, BT * C), R(weight, C), R(mean, BT), R(rstd, BT)};
     for (int a = 0; a < 3; ++a) {
         for (int b = a + 1; b < 3; ++b)
             if (overlap(outs[a], outs[b])) return MMB_ERR_ALIAS;
-        for (const Range& r : ins)
+        for (const Span& r : ins)
             if (overlap(outs[a], r)) return MMB_ERR_ALIAS;
     }
     return MMB_OK;
@@ -780,16 +919,17 @@ int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, con
         // one workgroup of 8 row-waves per CU (fewer for few rows);
         // MMB_LN_WORKGROUPS overrides the count (tuning aid)
         long long want = di.cus;
-        if (const char* e = std::getenv("MMB_LN_WORKGROUPS")) {
+        if (const char* e = g_tune.get(T_LN_WORKGROUPS)) {
             const long v = std::strtol(e, nullptr, 10);
             if (v > 0) want = std::min(v, 1L << 16);
         }
         G = (int)std::max(1LL, std::min<long long>(want, (p.BT + 7) / 8));
         Workspace& w = g_ws[{dev, s}];
-        st = grow(&w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
+        st = grow(dev, &w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
         if (st != MMB_OK) return st;
-        p.partial = (float*)w.partials;
+        p.partial = (float*)w.partials.ptr;
     }
+    TraceRange range("mmb layernorm launch");
     return launch_layernorm_backward(dtype, p, G, nj, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }
 
@@ -798,17 +938,20 @@ int forward_impl(void* out, const void* inp, const void* weight, const void* bia
     int st = check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
     const int BT = B * T;
-    if (!choose_path_fwd(out, inp, weight, bias, C, OC, dtype))
+    if (!choose_path_fwd(out, inp, weight, bias, C, OC, dtype)) {
+        TraceRange range("mmb forward launch (generic)");
         return launch_fwd_generic(dtype, out, inp, weight, bias, BT, C, OC, s) == hipSuccess
                    ? MMB_OK
                    : MMB_ERR_HIP;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mu);
-    Plan* plan = nullptr;
-    st = get_plan(dev, dtype, BT, C, OC, bias != nullptr, true, &plan);
+    PlanEntry* plan = nullptr;
+    st = find_plan(dev, dtype, BT, C, OC, bias != nullptr, true, &plan);
     if (st != MMB_OK) return st;
-    TilesParams tp = plan->proto;
+    TraceRange range("mmb forward launch");
+    TilesParams tp = plan->plan.proto;
     st = get_workspace(dev, s, *plan, &tp);
     if (st != MMB_OK) return st;
     tp.out = out;
@@ -909,6 +1052,7 @@ const char* mmb_strerror(int status) {
         case MMB_ERR_ALIAS: return "an output buffer overlaps another buffer";
         case MMB_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case MMB_ERR_NOMEM: return "the workspace could not be allocated";
+        case MMB_ERR_NAME: return "not a tuning variable of the library";
         default: return "unknown mmb status";
     }
 }
@@ -923,9 +1067,12 @@ int mmb_plan_units(int B, int T, int C, int OC, int dtype, int has_bias, int num
     di.cus = num_cus;
     mmb::set_topology(&di);
     di.slots = mmb::tiles_resident(dtype);
-    const mmb::Plan p = mmb::build_plan(dtype, B * T, C, OC, has_bias != 0, di,
-                                        mmb::parse_splits(std::getenv("MMB_SPLITS_DWEIGHT")),
-                                        mmb::parse_splits(std::getenv("MMB_SPLITS_DINP")));
+    mmb::PlanOptions opt;
+    {
+        std::lock_guard<std::mutex> lock(mmb::g_mu);
+        opt = mmb::plan_options(mmb::g_tune, false);
+    }
+    const mmb::Plan p = mmb::build_plan(dtype, B * T, C, OC, has_bias != 0, di, opt);
     splits[0] = p.max_splits[mmb::UNIT_DWEIGHT];
     splits[1] = p.max_splits[mmb::UNIT_DINP];
     if (units) {
@@ -949,8 +1096,12 @@ int mmb_forward_plan_units(int B, int T, int C, int OC, int dtype, int has_bias,
     di.cus = num_cus;
     mmb::set_topology(&di);
     di.slots = mmb::tiles_resident(dtype);
-    const mmb::Plan p = mmb::build_plan_forward(dtype, B * T, C, OC, has_bias != 0, di,
-                                                mmb::parse_splits(std::getenv("MMB_SPLITS_FWD")));
+    mmb::PlanOptions opt;
+    {
+        std::lock_guard<std::mutex> lock(mmb::g_mu);
+        opt = mmb::plan_options(mmb::g_tune, true);
+    }
+    const mmb::Plan p = mmb::build_plan_forward(dtype, B * T, C, OC, has_bias != 0, di, opt);
     splits[0] = p.max_splits[mmb::UNIT_FWD];
     if (units) {
         const int n = std::min<int>(max_units, (int)p.units.size());
@@ -978,21 +1129,50 @@ int mmb_release(void) {
     int prev = 0;
     (void)hipGetDevice(&prev);
     int st = MMB_OK;
+    std::map<int, bool> synced;
+    auto sync = [&](int dev) {
+        if (synced[dev]) return;
+        synced[dev] = true;
+        (void)hipSetDevice(dev);
+        if (hipDeviceSynchronize() != hipSuccess) st = MMB_ERR_HIP;
+    };
+    for (auto& kv : mmb::g_ws) sync(kv.first.first);
+    for (auto& kv : mmb::g_retired) sync(kv.first);
+    for (auto& kv : mmb::g_plans) sync(std::get<0>(kv.first));
+    // everything enqueued has finished: free in any order
+    auto release = [](mmb::DevAlloc& a) {
+        if (a.ptr) (void)hipFree(a.ptr);
+        a.ptr = nullptr;
+    };
     for (auto& kv : mmb::g_ws) {
         (void)hipSetDevice(kv.first.first);
-        if (hipDeviceSynchronize() != hipSuccess) st = MMB_ERR_HIP;
-        if (kv.second.counters) (void)hipFree(kv.second.counters);
-        if (kv.second.partials) (void)hipFree(kv.second.partials);
+        release(kv.second.counters);
+        release(kv.second.partials);
+        for (auto& t : kv.second.tables) release(t.second);
     }
     mmb::g_ws.clear();
-    for (auto& kv : mmb::g_plans) {
-        (void)hipSetDevice(std::get<0>(kv.first));
-        if (hipDeviceSynchronize() != hipSuccess) st = MMB_ERR_HIP;
-        (void)hipFree(kv.second.d_units);
+    for (auto& kv : mmb::g_retired) {
+        (void)hipSetDevice(kv.first);
+        (void)hipFree(kv.second);
     }
+    mmb::g_retired.clear();
+    for (auto& kv : mmb::g_plans)
+        if (kv.second.host_units) (void)hipHostFree(kv.second.host_units);
     mmb::g_plans.clear();
     (void)hipSetDevice(prev);
     return st;
+}
+
+int mmb_set_tuning(const char* name, const char* value) {
+    if (!name) return MMB_ERR_NULL;
+    std::lock_guard<std::mutex> lock(mmb::g_mu);
+    for (int k = 0; k < mmb::T_COUNT; ++k)
+        if (std::strcmp(name, mmb::kTuneNames[k]) == 0) {
+            mmb::g_tune.set[k] = value != nullptr;
+            mmb::g_tune.val[k] = value ? value : "";
+            return MMB_OK;
+        }
+    return MMB_ERR_NAME;
 }
 
 }  // extern "C"

@@ -29,6 +29,7 @@ MMB_BF16 = 1
 STATUS = {
     0: "MMB_OK", -1: "MMB_ERR_NULL", -2: "MMB_ERR_DIM", -3: "MMB_ERR_DTYPE",
     -4: "MMB_ERR_OVERFLOW", -5: "MMB_ERR_ALIAS", -6: "MMB_ERR_HIP", -7: "MMB_ERR_NOMEM",
+    -8: "MMB_ERR_NAME",
 }
 
 if not os.path.exists(LIBRARY):
@@ -71,6 +72,15 @@ _lib.mmb_forward_stream.argtypes = _FWD_ARGS + [_vp]
 _lib.mmb_forward_stream.restype = _i
 _lib.mmb_forward_plan_units.argtypes = [_i] * 7 + [ctypes.POINTER(_i), ctypes.POINTER(_i), _i]
 _lib.mmb_forward_plan_units.restype = _i
+_lib.mmb_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
+_lib.mmb_set_tuning.restype = _i
+
+# The library reads its MMB_* tuning variables from the environment once, at
+# load; this mirror of the values set through mmb_set_tuning lets `tuning`
+# restore them.
+_TUNING_NAMES = ("MMB_SPLITS_DWEIGHT", "MMB_SPLITS_DINP", "MMB_SPLITS_FWD", "MMB_PLAN_MODEL",
+                 "MMB_PLAN_TRACE", "MMB_LN_WORKGROUPS")
+_tuning_now = {k: os.environ.get(k) for k in _TUNING_NAMES}
 
 
 class MmbError(RuntimeError):
@@ -94,6 +104,35 @@ def _args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype):
 
 def mmb_strerror(status: int) -> str:
     return _lib.mmb_strerror(int(status)).decode()
+
+
+def mmb_set_tuning(name: str, value) -> None:
+    """Set one tuning variable of the library (None clears it)."""
+    st = _lib.mmb_set_tuning(name.encode(), None if value is None else str(value).encode())
+    if st != 0:
+        raise MmbError(st)
+    _tuning_now[name] = None if value is None else str(value)
+
+
+class tuning:
+    """Context manager: ``with mmb.tuning(MMB_SPLITS_DWEIGHT="4"):`` sets the
+    given tuning variables (None clears one) and restores the previous values
+    on exit."""
+
+    def __init__(self, **values):
+        self.values = values
+        self.saved = {}
+
+    def __enter__(self):
+        for k, v in self.values.items():
+            self.saved[k] = _tuning_now.get(k)
+            mmb_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            mmb_set_tuning(k, v)
+        return False
 
 
 def mmb_check_args(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype) -> int:

@@ -41,11 +41,17 @@ def test_json_line(argv):
               "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 3
+    # the warm-up runs on past --warmup until 300 ms of GPU time have gone by
+    assert d["warmup_steps_run"] >= 3 and d["warmup_ms"] >= 300
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
     assert d["data"] == "synthetic" and "workload" in d["config"]
     r = d["roofline"]
     assert r["bound"] in ("mfma", "hbm") and r["achieved"] > 0 and r["peak"] > 0
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert r["traffic"] is None or r["traffic"] > 0
+    if r["bound"] == "mfma":
+        assert r["hbm_gbs_algorithmic"] > 0 and r["hbm_peak_gbs"] == 8000.0
+        assert (r["hbm_gbs_measured"] is None) == (r["traffic"] is None)
+        assert r["mfma_busy"] is None or 0 < r["mfma_busy"] <= 100
     # the cold-cache figure: each launch after a 512 MiB stream through the caches
     assert r["launch_ms_flushed"] > 0 and r["achieved_flushed"] > 0

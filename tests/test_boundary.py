@@ -175,9 +175,9 @@ def test_tile_shape(mmb):
 
 
 @pytest.mark.parametrize("lists", [("2,3,5", "1,2"), ("16,1", "8")])
-def test_plan_per_tile_split_lists(mmb, monkeypatch, lists):
-    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", lists[0])
-    monkeypatch.setenv("MMB_SPLITS_DINP", lists[1])
+def test_plan_per_tile_split_lists(mmb, tune, lists):
+    tune.set("MMB_SPLITS_DWEIGHT", lists[0])
+    tune.set("MMB_SPLITS_DINP", lists[1])
     test_plan_covers_every_tile_and_split_once(mmb, (1, 700, 520, 600, 1, True), 256)
     B, T, C, OC = 1, 700, 520, 600
     BM, BN, BK = mmb.mmb_tile_shape(1)
@@ -192,19 +192,19 @@ def test_plan_per_tile_split_lists(mmb, monkeypatch, lists):
         assert u[6] == min(want[kind][t % len(want[kind])], kit[kind])
 
 
-def test_plan_split_override(mmb, monkeypatch):
-    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", "3")
-    monkeypatch.setenv("MMB_SPLITS_DINP", "2")
+def test_plan_split_override(mmb, tune):
+    tune.set("MMB_SPLITS_DWEIGHT", "3")
+    tune.set("MMB_SPLITS_DINP", "2")
     (sw, si), units = mmb.mmb_plan_units(2, 150, 264, 400, 1, True, 256)
     assert (sw, si) == (3, 2)
     assert all(u[6] == (3 if u[0] == 0 else 2) for u in units)
 
 
-def test_plan_deals_each_split_level_evenly_over_xcds(mmb, monkeypatch):
+def test_plan_deals_each_split_level_evenly_over_xcds(mmb, tune):
     """Workgroup i runs on XCD i % 8; every run of equal split counts of a
     GEMM is spread over the 8 XCDs within one unit of each other."""
-    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", "4")
-    monkeypatch.setenv("MMB_SPLITS_DINP", ",".join(["1"] * 5 + ["2", "3"]))
+    tune.set("MMB_SPLITS_DWEIGHT", "4")
+    tune.set("MMB_SPLITS_DINP", ",".join(["1"] * 5 + ["2", "3"]))
     _, units = mmb.mmb_plan_units(16, 1024, 768, 3072, 1, True, 256)
     levels = {}
     for i, u in enumerate(units):
@@ -221,23 +221,23 @@ def test_plan_deals_each_split_level_evenly_over_xcds(mmb, monkeypatch):
     ((8, 1024, 768, 3072, 0, True), (2, 4)),      # GPT-2 fc, fp32
     ((8, 1024, 3072, 768, 0, True), (2, 1)),      # GPT-2 fc_proj, fp32
 ], ids=["fc_bf16", "lm_head_bf16", "qkv_f32", "fc_f32", "fc_proj_f32"])
-def test_plan_picks_the_measured_best_splits(mmb, monkeypatch, shape, want):
+def test_plan_picks_the_measured_best_splits(mmb, tune, shape, want):
     """On a 256-CU MI355X the planner's model picks the split counts that
     timed fastest in forced-split sweeps of these shapes."""
-    monkeypatch.delenv("MMB_SPLITS_DWEIGHT", raising=False)
-    monkeypatch.delenv("MMB_SPLITS_DINP", raising=False)
-    monkeypatch.delenv("MMB_PLAN_MODEL", raising=False)
+    tune.clear("MMB_SPLITS_DWEIGHT")
+    tune.clear("MMB_SPLITS_DINP")
+    tune.clear("MMB_PLAN_MODEL")
     B, T, C, OC, dt, bias = shape
     (sw, si), _ = mmb.mmb_plan_units(B, T, C, OC, dt, bias, 256)
     assert (sw, si) == want
 
 
-def test_plan_tail_layout_on_gpt2_xl_fc(mmb, monkeypatch):
+def test_plan_tail_layout_on_gpt2_xl_fc(mmb, tune):
     """GPT-2 XL fc (bf16, 256 CUs): the planner splits only the dinp tiles of
     the last 12 of 32 tile rows, 2 ways, and those units launch after every
     unsplit dinp unit, so they fill the slots that free up at the end."""
     for k in ("MMB_SPLITS_DWEIGHT", "MMB_SPLITS_DINP", "MMB_PLAN_MODEL"):
-        monkeypatch.delenv(k, raising=False)
+        tune.clear(k)
     (sw, si), units = mmb.mmb_plan_units(8, 1024, 1600, 6400, 1, True, 256)
     assert (sw, si) == (1, 2)
     dinp = [(i, u) for i, u in enumerate(units) if u[0] == 1]
@@ -248,17 +248,86 @@ def test_plan_tail_layout_on_gpt2_xl_fc(mmb, monkeypatch):
     assert all(i > last_whole for i, u in dinp if u[6] == 2)
 
 
-def test_plan_model_override(mmb, monkeypatch):
-    """MMB_PLAN_MODEL replaces the cost constants; a malformed value is
-    ignored."""
-    monkeypatch.delenv("MMB_SPLITS_DWEIGHT", raising=False)
-    monkeypatch.delenv("MMB_SPLITS_DINP", raising=False)
+# The planner's choices (largest dweight and dinp split counts, and whether
+# the dinp tiles take a tail layout) on the bf16 linear layers of the four
+# GPT-2 sizes at B=8, T=1024, for the 256 CUs of an MI355X and a 32-CU
+# partition.  Only the 1558M fc layer on 256 CUs takes a tail layout.
+GPT2_WIDTHS = {"124M": 768, "350M": 1024, "774M": 1280, "1558M": 1600}
+GPT2_PLANS = {
+    ("124M", 256): {"qkv": (5, 1), "attn_proj": (8, 1), "fc": (4, 1), "fc_proj": (4, 1)},
+    ("124M", 32): {"qkv": (1, 1), "attn_proj": (3, 1), "fc": (1, 1), "fc_proj": (1, 1)},
+    ("350M", 256): {"qkv": (2, 1), "attn_proj": (7, 1), "fc": (2, 1), "fc_proj": (2, 1)},
+    ("350M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (1, 1), "fc_proj": (1, 1)},
+    ("774M", 256): {"qkv": (1, 1), "attn_proj": (6, 1), "fc": (1, 3), "fc_proj": (1, 1)},
+    ("774M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (1, 2), "fc_proj": (1, 1)},
+    ("1558M", 256): {"qkv": (2, 1), "attn_proj": (3, 1), "fc": (1, 2), "fc_proj": (1, 1)},
+    ("1558M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (3, 2), "fc_proj": (1, 1)},
+}
+
+
+@pytest.mark.parametrize("model,cus", sorted(GPT2_PLANS))
+def test_plan_choices_on_gpt2_layers(mmb, tune, model, cus):
+    for k in ("MMB_SPLITS_DWEIGHT", "MMB_SPLITS_DINP", "MMB_PLAN_MODEL"):
+        tune.clear(k)
+    C = GPT2_WIDTHS[model]
+    shapes = {"qkv": (C, 3 * C), "attn_proj": (C, C), "fc": (C, 4 * C), "fc_proj": (4 * C, C)}
+    for layer, (c, oc) in shapes.items():
+        (sw, si), units = mmb.mmb_plan_units(8, 1024, c, oc, 1, True, cus)
+        assert (sw, si) == GPT2_PLANS[(model, cus)][layer], (model, cus, layer)
+        counts = {k: {u[6] for u in units if u[0] == k} for k in (0, 1)}
+        tail = (model, cus, layer) == ("1558M", 256, "fc")
+        assert len(counts[0]) == 1
+        assert len(counts[1]) == (2 if tail else 1), (model, cus, layer)
+
+
+def test_plan_tail_layouts_are_bf16_only(mmb, tune):
+    """fp32 takes one split count per GEMM on the same shapes (no tail layout
+    was measured on the fp32 kernel)."""
+    for k in ("MMB_SPLITS_DWEIGHT", "MMB_SPLITS_DINP", "MMB_PLAN_MODEL"):
+        tune.clear(k)
+    for C in GPT2_WIDTHS.values():
+        for c, oc in ((C, 3 * C), (C, C), (C, 4 * C), (4 * C, C)):
+            for cus in (256, 32):
+                _, units = mmb.mmb_plan_units(8, 1024, c, oc, 0, True, cus)
+                for k in (0, 1):
+                    assert len({u[6] for u in units if u[0] == k}) <= 1
+
+
+def test_tuning_is_read_once_at_load(mmb, tune, monkeypatch):
+    """The environment is read when the library loads: a variable set later
+    changes nothing; mmb_set_tuning does."""
+    tune.clear("MMB_SPLITS_DWEIGHT")
+    tune.clear("MMB_SPLITS_DINP")
+    tune.clear("MMB_PLAN_MODEL")
     shape = (16, 1024, 768, 3072, 1, True)
     base = mmb.mmb_plan_units(*shape, 256)[0]
-    monkeypatch.setenv("MMB_PLAN_MODEL", "1,2,3")
+    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", "7")
+    assert mmb.mmb_plan_units(*shape, 256)[0] == base
+    tune.set("MMB_SPLITS_DWEIGHT", "7")
+    assert mmb.mmb_plan_units(*shape, 256)[0][0] == 7
+    tune.clear("MMB_SPLITS_DWEIGHT")
+    assert mmb.mmb_plan_units(*shape, 256)[0] == base
+
+
+def test_set_tuning_rejects_unknown_names(mmb):
+    assert mmb._lib.mmb_set_tuning(b"MMB_NOT_A_VARIABLE", b"1") == -8
+    assert mmb._lib.mmb_set_tuning(None, b"1") == -1
+    with pytest.raises(mmb.MmbError):
+        mmb.mmb_set_tuning("MMB_SPLITS", "2")
+    assert "tuning" in mmb.mmb_strerror(-8)
+
+
+def test_plan_model_override(mmb, tune):
+    """MMB_PLAN_MODEL replaces the cost constants; a malformed value is
+    ignored."""
+    tune.clear("MMB_SPLITS_DWEIGHT")
+    tune.clear("MMB_SPLITS_DINP")
+    shape = (16, 1024, 768, 3072, 1, True)
+    base = mmb.mmb_plan_units(*shape, 256)[0]
+    tune.set("MMB_PLAN_MODEL", "1,2,3")
     assert mmb.mmb_plan_units(*shape, 256)[0] == base
     # splitting made ruinous: every partial costs a millisecond of traffic
-    monkeypatch.setenv("MMB_PLAN_MODEL", "1.4,1.26,0.72,0.97,0.97,0.8,3.8,8.5,2.1,2.5,4.4,1e-3")
+    tune.set("MMB_PLAN_MODEL", "1.4,1.26,0.72,0.97,0.97,0.8,3.8,8.5,2.1,2.5,4.4,1e-3")
     assert mmb.mmb_plan_units(*shape, 256)[0] == (1, 1)
 
 
@@ -360,11 +429,11 @@ def test_forward_plan_covers_every_tile_once(mmb, shape, cus):
     assert smax == max(u[6] for u in units)
 
 
-def test_forward_plan_split_override(mmb, monkeypatch):
-    monkeypatch.setenv("MMB_SPLITS_FWD", "3")
+def test_forward_plan_split_override(mmb, tune):
+    tune.set("MMB_SPLITS_FWD", "3")
     smax, units = mmb.mmb_forward_plan_units(2, 150, 264, 400, 1, True, 256)
     assert smax == 3 and all(u[6] == 3 for u in units)
-    monkeypatch.setenv("MMB_SPLITS_FWD", "2,1,3")
+    tune.set("MMB_SPLITS_FWD", "2,1,3")
     smax, units = mmb.mmb_forward_plan_units(2, 150, 264, 400, 1, True, 256)
     assert smax == 3 and {u[6] for u in units} == {1, 2, 3}
 

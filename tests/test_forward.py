@@ -97,10 +97,10 @@ def test_forward_small_integer_exact(dev, shape):
 @pytest.mark.parametrize("splits", ["2", "3", "5", "2,1,3", "4,2"])
 @pytest.mark.parametrize("shape", [(3, 100, 200, 328, "f32"), (2, 150, 264, 400, "bf16"),
                                    (1, 300, 520, 264, "bf16")], ids=lambda s: "x".join(map(str, s)))
-def test_forward_forced_splits(dev, monkeypatch, shape, splits):
+def test_forward_forced_splits(dev, tune, shape, splits):
     """Split-K forward tiles: partials summed by the last arriver, then the
     bias epilogue; exact with integer inputs."""
-    monkeypatch.setenv("MMB_SPLITS_FWD", splits)
+    tune.set("MMB_SPLITS_FWD", splits)
     B, T, C, OC, dt = shape
     case = wl.integer_case(B, T, C, OC, dt, seed=17)
     b = make_bias(OC, 5, integer=True)
@@ -121,8 +121,8 @@ def test_forward_guard_bands(dev, shape):
     assert np.all(host[:g] == 12288.0) and np.all(host[-g:] == 12288.0)
 
 
-def test_forward_deterministic(dev, monkeypatch):
-    monkeypatch.setenv("MMB_SPLITS_FWD", "3")
+def test_forward_deterministic(dev, tune):
+    tune.set("MMB_SPLITS_FWD", "3")
     case = wl.random_case(2, 150, 264, 400, "bf16", seed=4)
     b = make_bias(400, 3)
     a = run_fwd(case, b, dev)
@@ -212,13 +212,13 @@ def test_forward_tensor_binding(dev):
         mmb.forward(out, x, w.float(), b)
 
 
-def test_forward_and_backward_share_the_workspace(dev, monkeypatch):
+def test_forward_and_backward_share_the_workspace(dev, tune):
     """Split forward and split backward calls alternate on one stream: the
     shared tile counters and partial buffers stay consistent."""
     from test_parity import check_exact, run
     for n in range(3):
-        monkeypatch.setenv("MMB_SPLITS_FWD", str(2 + n))
-        monkeypatch.setenv("MMB_SPLITS_DWEIGHT", str(3 + n))
+        tune.set("MMB_SPLITS_FWD", str(2 + n))
+        tune.set("MMB_SPLITS_DWEIGHT", str(3 + n))
         case = wl.integer_case(2, 150, 264, 400, "bf16", seed=90 + n)
         b = make_bias(400, n, integer=True)
         check(case, b, run_fwd(case, b, dev), exact=True)

@@ -188,10 +188,10 @@ def test_small_integer_exact(dev, shape):
 @pytest.mark.parametrize("splits", [(2, 1), (3, 2), (5, 3), (1, 4)])
 @pytest.mark.parametrize("shape", [(3, 100, 200, 328, "f32"), (2, 150, 264, 400, "bf16")],
                          ids=["f32", "bf16"])
-def test_forced_splits(dev, monkeypatch, shape, splits):
+def test_forced_splits(dev, tune, shape, splits):
     """The split-K / last-arriver path at every split count, exact and random."""
-    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", str(splits[0]))
-    monkeypatch.setenv("MMB_SPLITS_DINP", str(splits[1]))
+    tune.set("MMB_SPLITS_DWEIGHT", str(splits[0]))
+    tune.set("MMB_SPLITS_DINP", str(splits[1]))
     B, T, C, OC, dt = shape
     case = wl.integer_case(B, T, C, OC, dt, seed=3)
     check_exact(case, run(case, dev))
@@ -202,11 +202,11 @@ def test_forced_splits(dev, monkeypatch, shape, splits):
 @pytest.mark.parametrize("splits", [("2,3,5", "1,2"), ("7,1,4", "3,1,2,1,5")])
 @pytest.mark.parametrize("shape", [(3, 100, 200, 328, "f32"), (2, 150, 264, 400, "bf16"),
                                    (1, 700, 520, 600, "bf16")], ids=["f32", "bf16", "bf16-big"])
-def test_uneven_tile_splits(dev, monkeypatch, shape, splits):
+def test_uneven_tile_splits(dev, tune, shape, splits):
     """Tiles of one GEMM cut into different numbers of K ranges (per-tile
     split counts, workspace slots and arrival counts), exact and random."""
-    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", splits[0])
-    monkeypatch.setenv("MMB_SPLITS_DINP", splits[1])
+    tune.set("MMB_SPLITS_DWEIGHT", splits[0])
+    tune.set("MMB_SPLITS_DINP", splits[1])
     B, T, C, OC, dt = shape
     case = wl.integer_case(B, T, C, OC, dt, seed=5)
     check_exact(case, run(case, dev))
@@ -242,9 +242,9 @@ def test_guard_bands(dev, shape):
 
 
 @pytest.mark.parametrize("split", [None, "4"])
-def test_deterministic(dev, monkeypatch, split):
+def test_deterministic(dev, tune, split):
     if split:
-        monkeypatch.setenv("MMB_SPLITS_DWEIGHT", split)
+        tune.set("MMB_SPLITS_DWEIGHT", split)
     case = wl.random_case(4, 128, 256, 512, "bf16", seed=13)
     a = run(case, dev)
     b = run(case, dev)
@@ -359,13 +359,13 @@ def test_full_shape_integer_exact(dev, shape):
     check_sampled(case, run(case, dev), seed=5, exact=True)
 
 
-def test_plan_changes_between_calls(dev, monkeypatch):
+def test_plan_changes_between_calls(dev, tune):
     """Shapes and split plans alternate on one stream; the workspace is
     reused and regrown, and every result stays exact."""
     seq = [((3, 100, 200, 328, "f32"), "5"), ((2, 150, 264, 400, "bf16"), "3"),
            ((8, 64, 256, 512, "bf16"), "2"), ((3, 100, 200, 328, "f32"), "4"),
            ((2, 150, 264, 400, "bf16"), "5")]
     for n, ((B, T, C, OC, dt), sw) in enumerate(seq):
-        monkeypatch.setenv("MMB_SPLITS_DWEIGHT", sw)
+        tune.set("MMB_SPLITS_DWEIGHT", sw)
         case = wl.integer_case(B, T, C, OC, dt, seed=40 + n)
         check_exact(case, run(case, dev))

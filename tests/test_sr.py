@@ -80,10 +80,10 @@ def test_sr_integer_exact(dev, shape):
 
 
 @pytest.mark.parametrize("splits", ["2", "3", "5", "2,3,1,4"])
-def test_sr_split_k(dev, monkeypatch, splits):
+def test_sr_split_k(dev, tune, splits):
     """The split-K fix-up rounds once, with the element's bits, whatever the
     plan: bits equal the oracle's for every split count."""
-    monkeypatch.setenv("MMB_SPLITS_DWEIGHT", splits)
+    tune.set("MMB_SPLITS_DWEIGHT", splits)
     B, T, C, OC = 4, 300, 264, 520
     case = wl.integer_case(B, T, C, OC, "bf16", seed=7, lo=-4, hi=4)
     gi, gw, gb = run_sr(case, dev, 99)
