@@ -81,7 +81,9 @@ typedef enum {
     MMB_ERR_ALIAS = -5,     /* an output range overlaps another buffer's range */
     MMB_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed      */
     MMB_ERR_NOMEM = -7,     /* the workspace could not be allocated            */
-    MMB_ERR_NAME = -8       /* mmb_set_tuning: not a tuning variable           */
+    MMB_ERR_NAME = -8,      /* mmb_set_tuning: not a tuning variable           */
+    MMB_ERR_SCRATCH = -9    /* mmb_backward_noalloc: the call needs more than
+                               MMB_NOALLOC_SCRATCH_BYTES of scratch            */
 } mmb_status;
 
 /* The backward pass on the calling thread's current device, enqueued on the
@@ -118,6 +120,29 @@ int mmb_backward_stream(void* dinp, void* dweight, void* dbias,
 int mmb_backward_sr(void* dinp, void* dweight, void* dbias,
                     const void* dout, const void* inp, const void* weight,
                     int B, int T, int C, int OC, unsigned long long seed, void* stream);
+
+/* Scratch that mmb_backward_noalloc holds on each device (128 MiB). */
+#define MMB_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * backward pass as mmb_backward_stream (same arguments, plan, kernels and
+ * result bits), but the split-K counters, the work list and the split
+ * partials live in a fixed MMB_NOALLOC_SCRATCH_BYTES device array that each
+ * device holds from library load to process end, the work list reaches it
+ * through kernel arguments and the counters are cleared by a small fill
+ * kernel.  The call makes no hipMalloc, hipFree, pinned allocation or
+ * host-to-device copy (the first call of a shape plans it on the host, as
+ * mmb_backward_stream does).  Returns MMB_ERR_SCRATCH, without enqueuing
+ * anything, when the plan needs more scratch than that (the GPT-2 124M
+ * layers at B*T = 8192 or 16384 need at most 115 MiB in fp32 and 48 MiB in
+ * bf16).  Every call on a device shares that device's
+ * scratch, which keeps the last call's contents: calls that overlap on one
+ * device (several streams, or host threads) race and give wrong results;
+ * order them on one stream. */
+int mmb_backward_noalloc(void* dinp, void* dweight, void* dbias,
+                         const void* dout, const void* inp, const void* weight,
+                         int B, int T, int C, int OC, int dtype, void* stream);
 
 /* Host-only validation of an argument set, exactly the checks that
  * mmb_backward performs before touching the GPU.  Makes no HIP call. */

@@ -25,6 +25,13 @@
 #include "../../include/mmb.h"
 #include "mmb_internal.h"
 
+// Device memory of the allocation-free entry point (mmb_backward_noalloc):
+// split-K counters, the work list and the split partials of one call.  Each
+// device the library runs on holds its own copy until the process ends; host
+// code reaches it only through the per-device address hipGetSymbolAddress
+// returns (noalloc_scratch below), never through this name.
+static __device__ __align__(256) char scratch[MMB_NOALLOC_SCRATCH_BYTES];
+
 namespace mmb {
 namespace {
 
@@ -852,6 +859,111 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     return e == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// the allocation-free backward: the same plans and kernels as backward_impl,
+// with the workspace carved out of the static `scratch` array and the work
+// list passed through kernel arguments, so that a call makes no allocation
+// and no host-to-device copy.
+
+// One launch of mmb_put_units carries up to kChunkUnits units (3.5 KB of
+// arguments) to their place in the scratch work list; the first launch of a
+// call also clears the call's tile counters.
+constexpr int kChunkUnits = 112;
+struct UnitChunk {
+    int4 u[2 * kChunkUnits];
+    int4* dst;      // destination of u[0]
+    int n;          // int4s to copy
+    int* zero;      // counters to clear (n_zero ints), or NULL
+    int n_zero;
+};
+
+__global__ __launch_bounds__(256) void mmb_put_units(UnitChunk c) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x, nt = gridDim.x * blockDim.x;
+    for (int i = t; i < c.n; i += nt) c.dst[i] = c.u[i];
+    for (int i = t; i < c.n_zero; i += nt) c.zero[i] = 0;
+}
+
+std::map<int, char*> g_scratch;   // device -> address of its `scratch`
+
+// The device address of `scratch` on the current device `dev` (looked up
+// once per device).
+int noalloc_scratch(int dev, char** out) {
+    auto it = g_scratch.find(dev);
+    if (it != g_scratch.end()) {
+        *out = it->second;
+        return MMB_OK;
+    }
+    char* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return MMB_ERR_HIP;
+    g_scratch[dev] = ptr;
+    *out = ptr;
+    return MMB_OK;
+}
+
+int backward_noalloc_impl(void* dinp, void* dweight, void* dbias, const void* dout,
+                          const void* inp, const void* weight, int B, int T, int C, int OC,
+                          int dtype, hipStream_t s) {
+    int st = check(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype);
+    if (st != MMB_OK) return st;
+    const int BT = B * T;
+    if (!choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype)) {
+        // the generic kernels use no workspace
+        TraceRange range("mmb launch (generic)");
+        return launch_generic(dtype, dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s) ==
+                       hipSuccess
+                   ? MMB_OK
+                   : MMB_ERR_HIP;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    PlanEntry* entry = nullptr;
+    st = find_plan(dev, dtype, BT, C, OC, dbias != nullptr, false, &entry);
+    if (st != MMB_OK) return st;
+    const Plan& plan = entry->plan;
+    // scratch layout: counters, work list, dbias partials, tile partials
+    // (each part 256-byte aligned), all sizes in 64 bits
+    const size_t cb = align_up((size_t)plan.n_counters * 4, 256);
+    const size_t ub = align_up(plan.units.size() * sizeof(Unit), 256);
+    const size_t bb = align_up((size_t)plan.ws_bias_floats * 4, 256);
+    const size_t wb = align_up((size_t)plan.ws_floats * 4, 256);
+    if (cb + ub + bb + wb > (size_t)MMB_NOALLOC_SCRATCH_BYTES) return MMB_ERR_SCRATCH;
+    char* base = nullptr;
+    st = noalloc_scratch(dev, &base);
+    if (st != MMB_OK) return st;
+    TraceRange range("mmb launch (no allocation)");
+    int* counters = (int*)base;
+    int4* units = (int4*)(base + cb);
+    const int n4 = (int)(2 * plan.units.size());
+    const int4* src = (const int4*)plan.units.data();
+    UnitChunk c;
+    for (int first = 0; first < n4 || first == 0; first += 2 * kChunkUnits) {
+        c.n = std::min(2 * kChunkUnits, n4 - first);
+        std::memcpy(c.u, src + first, (size_t)c.n * sizeof(int4));
+        c.dst = units + first;
+        c.zero = first == 0 ? counters : nullptr;
+        c.n_zero = first == 0 ? plan.n_counters : 0;
+        const int work = std::max(c.n, c.n_zero);
+        const int blocks = std::max(1, std::min(1024, (work + 255) / 256));
+        hipLaunchKernelGGL(mmb_put_units, dim3(blocks), dim3(256), 0, s, c);
+        if (hipGetLastError() != hipSuccess) return MMB_ERR_HIP;
+    }
+    TilesParams tp = plan.proto;
+    tp.units = units;
+    tp.counters = counters;
+    tp.ws_bias = (float*)(base + cb + ub);
+    tp.ws = (float*)(base + cb + ub + bb);
+    tp.dinp = dinp;
+    tp.dweight = dweight;
+    tp.dbias = dbias;
+    tp.dout = dout;
+    tp.inp = inp;
+    tp.weight = weight;
+    tp.seed = 0;
+    return launch_tiles(dtype, tp, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+}
+
 // LayerNorm backward: every pointer required; the three outputs may not
 // overlap each other or any input.
 int check_ln(const void* dinp, const void* dweight, const void* dbias, const void* dout,
@@ -1036,6 +1148,13 @@ int mmb_backward_sr(void* dinp, void* dweight, void* dbias, const void* dout, co
                               (hipStream_t)stream, true, seed);
 }
 
+int mmb_backward_noalloc(void* dinp, void* dweight, void* dbias, const void* dout,
+                         const void* inp, const void* weight, int B, int T, int C, int OC,
+                         int dtype, void* stream) {
+    return mmb::backward_noalloc_impl(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype,
+                                      (hipStream_t)stream);
+}
+
 int mmb_backward(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
                  const void* weight, int B, int T, int C, int OC, int dtype) {
     return mmb::backward_impl(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype,
@@ -1053,6 +1172,9 @@ const char* mmb_strerror(int status) {
         case MMB_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case MMB_ERR_NOMEM: return "the workspace could not be allocated";
         case MMB_ERR_NAME: return "not a tuning variable of the library";
+        case MMB_ERR_SCRATCH:
+            return "the call needs more device memory than mmb_backward_noalloc's fixed scratch "
+                   "(MMB_NOALLOC_SCRATCH_BYTES) holds";
         default: return "unknown mmb status";
     }
 }

@@ -29,8 +29,9 @@ MMB_BF16 = 1
 STATUS = {
     0: "MMB_OK", -1: "MMB_ERR_NULL", -2: "MMB_ERR_DIM", -3: "MMB_ERR_DTYPE",
     -4: "MMB_ERR_OVERFLOW", -5: "MMB_ERR_ALIAS", -6: "MMB_ERR_HIP", -7: "MMB_ERR_NOMEM",
-    -8: "MMB_ERR_NAME",
+    -8: "MMB_ERR_NAME", -9: "MMB_ERR_SCRATCH",
 }
+MMB_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 if not os.path.exists(LIBRARY):
     raise ImportError(f"{LIBRARY} is not built; run `python -m linear_layer_backward_amd.build`")
@@ -43,6 +44,8 @@ _lib.mmb_backward.argtypes = _ARGS
 _lib.mmb_backward.restype = _i
 _lib.mmb_backward_stream.argtypes = _ARGS + [_vp]
 _lib.mmb_backward_stream.restype = _i
+_lib.mmb_backward_noalloc.argtypes = _ARGS + [_vp]
+_lib.mmb_backward_noalloc.restype = _i
 _lib.mmb_check_args.argtypes = _ARGS
 _lib.mmb_check_args.restype = _i
 _lib.mmb_path.argtypes = _ARGS
@@ -154,6 +157,17 @@ def mmb_backward_stream(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dt
     s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
     st = _lib.mmb_backward_stream(*_args(dinp, dweight, dbias, dout, inp, weight,
                                          B, T, C, OC, dtype), s or None)
+    if st != 0:
+        raise MmbError(st)
+
+
+def mmb_backward_noalloc(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype,
+                         stream) -> None:
+    """mmb_backward_stream with the library's fixed per-device scratch instead
+    of allocated workspace (no allocation, no host-to-device copy)."""
+    s = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
+    st = _lib.mmb_backward_noalloc(*_args(dinp, dweight, dbias, dout, inp, weight,
+                                          B, T, C, OC, dtype), s or None)
     if st != 0:
         raise MmbError(st)
 

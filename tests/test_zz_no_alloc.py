@@ -1,0 +1,138 @@
+"""The allocation-free entry point (mmb_backward_noalloc) against the
+allocating one (mmb_backward_stream), through the C ABI.
+
+Both take the same plan and kernels, so their outputs must be bit-identical;
+the smaller cases are also checked against the CPU oracle (max |g - r| /
+max |r| <= 1e-4 fp32, 2e-2 bf16).  Calls come in pairs, the second on a
+smaller input than the first, so that the fixed scratch (tile counters, work
+list, split partials) is reused with different contents: the counters must
+be cleared and the work list replaced on every call.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from linear_layer_backward_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from linear_layer_backward_amd import mmb  # noqa: F401  (fails loudly if unbuilt)
+    return torch.device("cuda:0")
+
+
+def up(x, dtype, dev):
+    import torch
+    raw = wl.storage(np.asarray(x, np.float32).ravel(), dtype)
+    if dtype == "bf16":
+        return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(raw.copy()).to(dev)
+
+
+def down(t, dtype):
+    import torch
+    if dtype == "bf16":
+        return wl.from_storage(t.view(torch.int16).cpu().numpy().view(np.uint16), dtype)
+    return wl.from_storage(t.cpu().numpy(), dtype)
+
+
+def both(case, dev):
+    """Run the case through mmb_backward_stream and mmb_backward_noalloc on
+    separate, identically prefilled outputs; return both results (raw bits)."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    dt = case.dtype
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+    dout, inp, w = (up(a, dt, dev) for a in (case.dout, case.inp, case.weight))
+    s = torch.cuda.current_stream(dev)
+    outs = []
+    for fn in (mmb.mmb_backward_stream, mmb.mmb_backward_noalloc):
+        gi, gw = up(case.dinp0, dt, dev), up(case.dweight0, dt, dev)
+        gb = up(np.full(case.OC, np.nan, np.float32), dt, dev) if case.with_bias else None
+        print(f"[noalloc] {fn.__name__} {dt} B={case.B} T={case.T} C={case.C} OC={case.OC}",
+              flush=True)
+        fn(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, code, s)
+        torch.cuda.synchronize(dev)
+        outs.append((down(gi, dt), down(gw, dt), None if gb is None else down(gb, dt)))
+    return outs
+
+
+def check(case, dev, with_oracle):
+    ref, got = both(case, dev)
+    for name, a, b in zip(("dinp", "dweight", "dbias"), ref, got):
+        if a is None:
+            continue
+        np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                      b.view(np.uint32) if b.dtype == np.float32 else b,
+                                      err_msg=name)
+    if with_oracle:
+        ri, rw, rb = oracle.case_backward(case)
+        for name, g, r in (("dinp", got[0], ri), ("dweight", got[1], rw), ("dbias", got[2], rb)):
+            if r is None:
+                continue
+            g = np.asarray(g, np.float64).reshape(r.shape)
+            err = np.max(np.abs(g - r)) / np.max(np.abs(r))
+            assert err <= TOL[case.dtype], f"{name}: {err:.3e}"
+
+
+# pairs (larger, then smaller); the fp32 pair's first plan has 732 units, so
+# its work list takes several argument-passing launches
+PAIRS = [
+    ((4, 512, 768, 1024, "bf16"), (2, 150, 264, 400, "bf16")),
+    ((2, 512, 768, 2304, "f32"), (1, 300, 132, 260, "f32")),
+    ((16, 1024, 768, 3072, "bf16"), (1, 513, 200, 136, "bf16")),
+]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=lambda p: "_then_".join(
+    "x".join(map(str, s)) for s in p))
+def test_noalloc_matches_the_allocating_call(dev, pair):
+    for i, (B, T, C, OC, dt) in enumerate(pair):
+        case = wl.random_case(B, T, C, OC, dt, seed=40 + i,
+                              with_bias=(i == 0 or dt == "f32"))
+        check(case, dev, with_oracle=B * T * C * OC <= 1 << 27)
+
+
+def test_noalloc_with_split_partials(dev, tune):
+    """Forced split counts put partial tiles and dbias partials in the scratch."""
+    tune.set("MMB_SPLITS_DWEIGHT", "3")
+    tune.set("MMB_SPLITS_DINP", "2")
+    check(wl.random_case(2, 300, 520, 600, "bf16", seed=44), dev, with_oracle=True)
+    tune.set("MMB_SPLITS_DWEIGHT", "2,5")
+    check(wl.random_case(1, 200, 264, 136, "bf16", seed=45), dev, with_oracle=True)
+
+
+def test_noalloc_generic_path(dev):
+    """C not a multiple of 8 (bf16): the generic kernels, which use no scratch."""
+    check(wl.random_case(3, 5, 33, 17, "bf16", seed=46), dev, with_oracle=True)
+
+
+def test_noalloc_rejects_plans_larger_than_the_scratch(dev, tune):
+    """16 dweight splits of the GPT-2 fc shape need 144 MiB of partials: the
+    call returns MMB_ERR_SCRATCH and enqueues nothing (the outputs keep their
+    contents)."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    tune.set("MMB_SPLITS_DWEIGHT", "16")
+    B, T, C, OC = 16, 1024, 768, 3072
+    bf = torch.bfloat16
+    dout = torch.zeros(B * T * OC, dtype=bf, device=dev)
+    inp = torch.zeros(B * T * C, dtype=bf, device=dev)
+    w = torch.zeros(OC * C, dtype=bf, device=dev)
+    gi = torch.full((B * T * C,), 3.0, dtype=bf, device=dev)
+    gw = torch.full((OC * C,), 3.0, dtype=bf, device=dev)
+    gb = torch.full((OC,), 3.0, dtype=bf, device=dev)
+    st = mmb._lib.mmb_backward_noalloc(gi.data_ptr(), gw.data_ptr(), gb.data_ptr(),
+                                       dout.data_ptr(), inp.data_ptr(), w.data_ptr(),
+                                       B, T, C, OC, mmb.MMB_BF16, None)
+    assert st == -9 and "scratch" in mmb.mmb_strerror(st)
+    torch.cuda.synchronize(dev)
+    for t in (gi, gw, gb):
+        assert bool((t == 3.0).all())
