@@ -220,14 +220,14 @@ def forward_flops(case) -> int:
 
 # the sources each kernel's code and launch plan come from (the shared headers
 # and the planner included); counters taken on other sources are stale
-_COMMON = ["mmb_internal.h", "mmb_numeric.h", "mmb_tile_common.h", "mmb_api.hip"]
+_COMMON = ["mmb_internal.h", "mmb_numeric.h", "mmb_tile_common.h", "mmb_plan.h", "mmb_plan.hip"]
 KERNEL_SOURCES = {
     "mmb_tiles_bf16_kernel": ["mmb_tiles_bf16.hip"] + _COMMON,
     "mmb_tiles_bf16_sr_kernel": ["mmb_tiles_bf16.hip"] + _COMMON,
     "mmb_fwd_bf16_kernel": ["mmb_tiles_bf16.hip"] + _COMMON,
     "mmb_tiles_kernel": ["mmb_tiles.hip"] + _COMMON,
     "mmb_fwd_kernel": ["mmb_tiles.hip"] + _COMMON,
-    "ln_bwd_rows": ["mmb_layernorm.hip"] + _COMMON,
+    "ln_bwd_rows": ["mmb_layernorm.hip", "mmb_internal.h", "mmb_numeric.h"],
 }
 
 
