@@ -441,6 +441,9 @@ def main(argv=None):
                     help="keep warming up, whatever --warmup says, until this much GPU time of "
                          "back-to-back steps has run (the clocks ramp over the first tens of ms)")
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--unpadded-vocab", action="store_true",
+                    help="with --config 5: the LM head at the real vocabulary (OC = 50257, "
+                         "ragged rows, packed copies on the MFMA tiles) instead of 50304")
     ap.add_argument("--op", default="backward",
                     choices=["backward", "forward", "backward_sr", "layernorm"],
                     help="backward (the metric), the forward product at the same shapes, or the "
@@ -504,6 +507,11 @@ def main(argv=None):
     fwd = args.op == "forward"
     sr = args.op == "backward_sr"
     cases = wl.config_cases(args.config)
+    if args.unpadded_vocab:
+        if args.config != 5:
+            print("--unpadded-vocab goes with --config 5", file=sys.stderr)
+            return 2
+        cases = [wl.lm_head_unpadded_case()]
     if sr and cases[0].dtype != "bf16":
         print("--op backward_sr needs a bf16 workload (--config 4 or 5)", file=sys.stderr)
         return 2
@@ -569,7 +577,8 @@ def main(argv=None):
     achieved = flops / (launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
     kernel = kernel_name(args.op, dtype)
-    traffic = measured_traffic(kernel, args.config)
+    # counter summaries exist for the five workloads, not the unpadded LM head
+    traffic = None if args.unpadded_vocab else measured_traffic(kernel, args.config)
     nbytes = sum(forward_bytes(c) if fwd else backward_bytes(c) for c in cases)
     gbs = lambda b: round(b / (launch_ms * 1e-3) / 1e9, 1)
 
@@ -588,7 +597,9 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl.CONFIG_NAMES[args.config] + (" (forward product)" if fwd else "")
+        "config": {"workload": (wl.CONFIG_NAMES[args.config].replace("OC=50304", "OC=50257")
+                                if args.unpadded_vocab else wl.CONFIG_NAMES[args.config])
+                   + (" (forward product)" if fwd else "")
                    + (" (stochastic rounding)" if sr else ""),
                    "calls": [{"B": c.B, "T": c.T, "C": c.C, "OC": c.OC, "bias": c.with_bias}
                              for c in cases],
@@ -603,7 +614,8 @@ def main(argv=None):
                      "hbm_gbs_measured": None if traffic is None else gbs(traffic),
                      "hbm_peak_gbs": HBM_PEAK_GBS,
                      # matrix-core busy share of the kernel's cycles (rocprofv3 MfmaUtil)
-                     "mfma_busy": measured_util(kernel, args.config, "mfma_util_pct"),
+                     "mfma_busy": None if args.unpadded_vocab
+                     else measured_util(kernel, args.config, "mfma_util_pct"),
                      "launch_ms_flushed": None if cold_ms is None else round(cold_ms, 5),
                      "achieved_flushed": None if cold_ms is None
                      else round(flops / (cold_ms * 1e-3) / 1e12, 2)},

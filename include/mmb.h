@@ -31,8 +31,13 @@
  * caller.  dout, inp, weight are read only; dinp and dweight are read and
  * written; dbias is written only.  Output buffers may not overlap each other
  * or any input (MMB_ERR_ALIAS).  Any alignment and any dims >= 1 are
- * accepted; 16-byte aligned pointers with C and OC multiples of 8 (bf16) or
- * 4 (fp32) take the MFMA path, anything else a slower generic path.
+ * accepted.  16-byte aligned pointers take the MFMA path: directly when C and
+ * OC are multiples of 8 (bf16) or 4 (fp32); otherwise the tensors whose rows
+ * are not whole 16-byte vectors (dout when OC is ragged; inp, weight, dinp
+ * and dweight when C is) are copied into zero-padded row pitches in the
+ * workspace first, and dinp and dweight copied back after (an extra pass over
+ * those tensors).  Pointers off the 16-byte alignment take a slower generic
+ * path.
  *
  * The library owns only a per-(device, stream) workspace (split-K partial
  * sums, tile counters and work lists), allocated on first use, grown on
@@ -139,7 +144,8 @@ int mmb_backward_sr(void* dinp, void* dweight, void* dbias,
  * bf16).  Every call on a device shares that device's
  * scratch, which keeps the last call's contents: calls that overlap on one
  * device (several streams, or host threads) race and give wrong results;
- * order them on one stream. */
+ * order them on one stream.  Ragged rows (see the file comment) keep their
+ * packed copies in the scratch too. */
 int mmb_backward_noalloc(void* dinp, void* dweight, void* dbias,
                          const void* dout, const void* inp, const void* weight,
                          int B, int T, int C, int OC, int dtype, void* stream);
@@ -153,8 +159,9 @@ int mmb_check_args(const void* dinp, const void* dweight, const void* dbias,
 /* Static English text for a status code (never NULL). */
 const char* mmb_strerror(int status);
 
-/* Which kernel path a call with these arguments takes: 1 = MFMA tiles,
- * 0 = generic path, or a negative mmb_status.  Host only, no HIP call. */
+/* Which kernel path a call with these arguments takes: 1 = MFMA tiles
+ * (directly or on packed copies of ragged rows), 0 = generic path, or a
+ * negative mmb_status.  Host only, no HIP call. */
 int mmb_path(const void* dinp, const void* dweight, const void* dbias,
              const void* dout, const void* inp, const void* weight,
              int B, int T, int C, int OC, int dtype);

@@ -102,19 +102,95 @@ int choose_path_fwd(const void* out, const void* inp, const void* weight, const 
     return 1;
 }
 
-// 1 when the MFMA tiles can take the call: 16-byte vectors never straddle a
-// row end (C and OC multiples of the vector width) and every streamed buffer
-// is 16-byte aligned.  dbias is written one element at a time.
+// Path of a backward call: 0 the generic kernels (a streamed buffer not
+// 16-byte aligned, or a dimension too large for the tiles' 32-bit offsets),
+// 1 the MFMA tiles on the caller's buffers, 2 the MFMA tiles on packed
+// copies (C or OC not a multiple of the 16-byte vector, so vectors would
+// straddle row ends; see Packing).  dbias is written one element at a time.
 int choose_path(const void* dinp, const void* dweight, const void* dout, const void* inp,
                 const void* weight, int C, int OC, int dtype) {
     const int vec = dtype == MMB_BF16 ? 8 : 4;
-    if (C % vec != 0 || OC % vec != 0) return 0;
     // the tiles address one 64-row K slab of an operand with 32-bit offsets
     if (C > (1 << 22) || OC > (1 << 22)) return 0;
     const void* ptrs[5] = {dinp, dweight, dout, inp, weight};
     for (const void* p : ptrs)
         if ((uintptr_t)p % 16 != 0) return 0;
-    return 1;
+    return (C % vec != 0 || OC % vec != 0) ? 2 : 1;
+}
+
+// Ragged shapes on the MFMA tiles: the tensors whose rows are not whole
+// 16-byte vectors are copied into zero-padded row pitches (dout when OC is
+// ragged; inp, weight, dinp and dweight when C is), the tiles run on the
+// copies with those pitches (the zero pads add nothing to any sum, and the
+// epilogue writes only the logical columns), and dinp and dweight are copied
+// back.  Offsets into one buffer, each part 256-byte aligned.
+struct Packing {
+    bool oc = false, c = false;   // dout / the C-wide tensors packed
+    long long ldo = 0, ldc = 0;   // row pitches the tiles use
+    size_t dout = 0, inp = 0, weight = 0, dinp = 0, dweight = 0, bytes = 0;
+};
+
+Packing plan_packing(int dtype, long long BT, int C, int OC) {
+    const int vec = dtype == MMB_BF16 ? 8 : 4;
+    const size_t es = elem_size(dtype);
+    Packing k;
+    k.oc = OC % vec != 0;
+    k.c = C % vec != 0;
+    k.ldo = (OC + vec - 1) / vec * vec;
+    k.ldc = (C + vec - 1) / vec * vec;
+    if (!k.oc) k.ldo = OC;
+    if (!k.c) k.ldc = C;
+    auto part = [&](size_t* off, long long rows, long long pitch) {
+        *off = k.bytes;
+        k.bytes += (size_t)rows * (size_t)pitch * es;
+        k.bytes = (k.bytes + 255) / 256 * 256;
+    };
+    if (k.oc) part(&k.dout, BT, k.ldo);
+    if (k.c) {
+        part(&k.inp, BT, k.ldc);
+        part(&k.dinp, BT, k.ldc);
+        part(&k.weight, OC, k.ldc);
+        part(&k.dweight, OC, k.ldc);
+    }
+    return k;
+}
+
+// Enqueue the packing copies on `s` and point the tile parameters at them.
+hipError_t pack_operands(const Packing& k, char* base, TilesParams* tp, int dtype, hipStream_t s) {
+    const int es = (int)elem_size(dtype);
+    const long long BT = tp->BT;
+    hipError_t e = hipSuccess;
+    if (k.oc) {
+        e = launch_pack(base + k.dout, k.ldo, tp->dout, tp->OC, BT, tp->OC, es, s);
+        if (e != hipSuccess) return e;
+        tp->dout = base + k.dout;
+    }
+    if (k.c) {
+        const void* src[4] = {tp->inp, tp->dinp, tp->weight, tp->dweight};
+        const size_t off[4] = {k.inp, k.dinp, k.weight, k.dweight};
+        const long long rows[4] = {BT, BT, tp->OC, tp->OC};
+        for (int i = 0; i < 4; ++i) {
+            e = launch_pack(base + off[i], k.ldc, src[i], tp->C, rows[i], tp->C, es, s);
+            if (e != hipSuccess) return e;
+        }
+        tp->inp = base + k.inp;
+        tp->dinp = base + k.dinp;
+        tp->weight = base + k.weight;
+        tp->dweight = base + k.dweight;
+    }
+    tp->ldo = (int)k.ldo;
+    tp->ldc = (int)k.ldc;
+    return hipSuccess;
+}
+
+// Copy the packed dinp and dweight back to the caller's buffers.
+hipError_t unpack_outputs(const Packing& k, const char* base, void* dinp, void* dweight, long long BT,
+                          int C, int OC, int dtype, hipStream_t s) {
+    if (!k.c) return hipSuccess;
+    const int es = (int)elem_size(dtype);
+    hipError_t e = launch_unpack(dinp, C, base + k.dinp, k.ldc, BT, C, es, s);
+    if (e != hipSuccess) return e;
+    return launch_unpack(dweight, C, base + k.dweight, k.ldc, OC, C, es, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -192,6 +268,8 @@ struct Workspace {
     size_t counter_bytes = 0;
     DevAlloc partials;
     size_t partial_bytes = 0;
+    DevAlloc packed;              // padded copies of ragged operands
+    size_t packed_bytes = 0;
     std::map<const void*, DevAlloc> tables;   // this stream's copy of each plan's work list
 };
 
@@ -364,7 +442,8 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     int st = check(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
     const int BT = B * T;
-    if (!choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype)) {
+    const int path = choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype);
+    if (path == 0) {
         TraceRange range("mmb launch (generic)");
         return launch_generic(dtype, dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s, sr,
                               seed) == hipSuccess
@@ -377,7 +456,7 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     PlanEntry* plan = nullptr;
     st = find_plan(dev, dtype, BT, C, OC, dbias != nullptr, false, &plan);
     if (st != MMB_OK) return st;
-    TraceRange range("mmb launch");
+    TraceRange range(path == 2 ? "mmb launch (packed)" : "mmb launch");
     TilesParams tp = plan->plan.proto;
     st = get_workspace(dev, s, *plan, &tp);
     if (st != MMB_OK) return st;
@@ -388,8 +467,21 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     tp.inp = inp;
     tp.weight = weight;
     tp.seed = seed;
+    Packing pk;
+    char* pbase = nullptr;
+    if (path == 2) {
+        pk = plan_packing(dtype, BT, C, OC);
+        Workspace& w = g_ws[{dev, s}];
+        st = grow(dev, &w.packed, &w.packed_bytes, pk.bytes, false, s);
+        if (st != MMB_OK) return st;
+        pbase = (char*)w.packed.ptr;
+        if (pack_operands(pk, pbase, &tp, dtype, s) != hipSuccess) return MMB_ERR_HIP;
+    }
     const hipError_t e = sr ? launch_tiles_bf16_sr(tp, s) : launch_tiles(dtype, tp, s);
-    return e == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+    if (e != hipSuccess) return MMB_ERR_HIP;
+    if (path == 2 && unpack_outputs(pk, pbase, dinp, dweight, BT, C, OC, dtype, s) != hipSuccess)
+        return MMB_ERR_HIP;
+    return MMB_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -440,7 +532,8 @@ int backward_noalloc_impl(void* dinp, void* dweight, void* dbias, const void* do
     int st = check(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
     const int BT = B * T;
-    if (!choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype)) {
+    const int path = choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype);
+    if (path == 0) {
         // the generic kernels use no workspace
         TraceRange range("mmb launch (generic)");
         return launch_generic(dtype, dinp, dweight, dbias, dout, inp, weight, BT, C, OC, s) ==
@@ -455,13 +548,16 @@ int backward_noalloc_impl(void* dinp, void* dweight, void* dbias, const void* do
     st = find_plan(dev, dtype, BT, C, OC, dbias != nullptr, false, &entry);
     if (st != MMB_OK) return st;
     const Plan& plan = entry->plan;
-    // scratch layout: counters, work list, dbias partials, tile partials
-    // (each part 256-byte aligned), all sizes in 64 bits
+    // scratch layout: counters, work list, dbias partials, tile partials,
+    // packed copies of ragged operands (each part 256-byte aligned), all
+    // sizes in 64 bits
     const size_t cb = align_up((size_t)plan.n_counters * 4, 256);
     const size_t ub = align_up(plan.units.size() * sizeof(Unit), 256);
     const size_t bb = align_up((size_t)plan.ws_bias_floats * 4, 256);
     const size_t wb = align_up((size_t)plan.ws_floats * 4, 256);
-    if (cb + ub + bb + wb > (size_t)MMB_NOALLOC_SCRATCH_BYTES) return MMB_ERR_SCRATCH;
+    Packing pk;
+    if (path == 2) pk = plan_packing(dtype, BT, C, OC);
+    if (cb + ub + bb + wb + pk.bytes > (size_t)MMB_NOALLOC_SCRATCH_BYTES) return MMB_ERR_SCRATCH;
     char* base = nullptr;
     st = noalloc_scratch(dev, &base);
     if (st != MMB_OK) return st;
@@ -494,7 +590,12 @@ int backward_noalloc_impl(void* dinp, void* dweight, void* dbias, const void* do
     tp.inp = inp;
     tp.weight = weight;
     tp.seed = 0;
-    return launch_tiles(dtype, tp, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+    char* pbase = base + cb + ub + bb + wb;
+    if (path == 2 && pack_operands(pk, pbase, &tp, dtype, s) != hipSuccess) return MMB_ERR_HIP;
+    if (launch_tiles(dtype, tp, s) != hipSuccess) return MMB_ERR_HIP;
+    if (path == 2 && unpack_outputs(pk, pbase, dinp, dweight, BT, C, OC, dtype, s) != hipSuccess)
+        return MMB_ERR_HIP;
+    return MMB_OK;
 }
 
 // LayerNorm backward: every pointer required; the three outputs may not
@@ -664,7 +765,7 @@ int mmb_path(const void* dinp, const void* dweight, const void* dbias, const voi
              const void* inp, const void* weight, int B, int T, int C, int OC, int dtype) {
     const int st = mmb::check(dinp, dweight, dbias, dout, inp, weight, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
-    return mmb::choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype);
+    return mmb::choose_path(dinp, dweight, dout, inp, weight, C, OC, dtype) > 0 ? 1 : 0;
 }
 
 int mmb_backward_stream(void* dinp, void* dweight, void* dbias, const void* dout,
@@ -803,6 +904,7 @@ int mmb_release(void) {
         (void)hipSetDevice(kv.first.first);
         release(kv.second.counters);
         release(kv.second.partials);
+        release(kv.second.packed);
         for (auto& t : kv.second.tables) release(t.second);
     }
     mmb::g_ws.clear();

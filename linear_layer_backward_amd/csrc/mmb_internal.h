@@ -36,6 +36,9 @@ struct TilesParams {
     const void* inp;
     const void* weight;
     int BT, C, OC;
+    // row pitches in elements: ldo of dout (backward) or out (forward), ldc of
+    // inp, weight, dinp and dweight; OC and C, or larger for packed copies
+    int ldo, ldc;
     GemmPlan g[2];        // [UNIT_DWEIGHT], [UNIT_DINP]
     const int4* units;    // two int4 per unit (see above), in launch order
     int n_units;
@@ -89,6 +92,14 @@ int ln_vectors_per_lane(int dtype, int C);
 // G workgroups for the row kernel (partial holds G * 2C floats); nj from
 // ln_vectors_per_lane.  Two launches on `s` (rows, then the column reduce).
 hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, int nj, hipStream_t s);
+
+// Row-pitch copies for shapes whose rows are not whole 16-byte vectors:
+// pack: dst[r, c] = src[r, c] for c < cols, 0 for cols <= c < ld_dst;
+// unpack: dst[r, c] = src[r, c] for c < cols.  es: element size (2 or 4).
+hipError_t launch_pack(void* dst, long long ld_dst, const void* src, long long ld_src,
+                       long long rows, int cols, int es, hipStream_t s);
+hipError_t launch_unpack(void* dst, long long ld_dst, const void* src, long long ld_src,
+                         long long rows, int cols, int es, hipStream_t s);
 
 // sr: bf16 only, dweight and dbias stochastically rounded under `seed`
 hipError_t launch_generic(int dtype, void* dinp, void* dweight, void* dbias,

@@ -386,6 +386,8 @@ Plan build_plan(int dtype, int BT, int C, int OC, bool bias, const DeviceInfo& d
     p.proto.BT = BT;
     p.proto.C = C;
     p.proto.OC = OC;
+    p.proto.ldo = OC;
+    p.proto.ldc = C;
     p.proto.g[0] = g[0];
     p.proto.g[1] = g[1];
     p.proto.n_units = (int)p.units.size();
@@ -442,6 +444,8 @@ Plan build_plan_forward(int dtype, int BT, int C, int OC, bool bias, const Devic
     p.proto.BT = BT;
     p.proto.C = C;
     p.proto.OC = OC;
+    p.proto.ldo = OC;
+    p.proto.ldc = C;
     p.proto.g[0] = g[0];
     p.proto.g[1] = g[1];
     p.proto.n_units = (int)p.units.size();

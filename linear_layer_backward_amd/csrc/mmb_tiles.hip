@@ -148,7 +148,8 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const T* A = (const T*)(OP == Op::FWD ? p.inp : p.dout);
     const T* Bop = (const T*)(OP == Op::DWEIGHT ? p.inp : p.weight);   // ld = C
     T* D = (T*)(OP == Op::DINP ? p.dinp : OP == Op::DWEIGHT ? p.dweight : p.out);
-    const long long lda = OP == Op::FWD ? p.C : p.OC, ldb = p.C, ldd = OP == Op::FWD ? p.OC : p.C;
+    // row pitches: dout (out) rows ldo, the C-wide tensors' rows ldc
+    const long long lda = OP == Op::FWD ? p.ldc : p.ldo, ldb = p.ldc, ldd = OP == Op::FWD ? p.ldo : p.ldc;
     const bool do_bias = OP == Op::DWEIGHT && p.dbias != nullptr && tile_n == 0;
 
     // staging thread roles
@@ -173,7 +174,7 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     //   K-contiguous operand: vector j = row (tid >> 3) + 32 j, K 4 (tid & 7)
     //   M/N-contiguous: vector r = K-row 4 kg + r, columns 4 xg .. 4 xg + 3
     const long long a_elems = (long long)p.BT * lda;
-    const long long b_elems = OP == Op::DWEIGHT ? (long long)p.BT * p.C : (long long)p.OC * p.C;
+    const long long b_elems = OP == Op::DWEIGHT ? (long long)p.BT * ldb : (long long)p.OC * ldb;
     uint32_t a_off[E], b_off[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) {

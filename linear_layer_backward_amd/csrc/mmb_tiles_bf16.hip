@@ -155,9 +155,10 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
     const bf16_t* A = (const bf16_t*)(OP == Op::FWD ? p.inp : p.dout);
     const bf16_t* Bp = (const bf16_t*)(OP == Op::DWEIGHT ? p.inp : p.weight);
     bf16_t* D = (bf16_t*)(OP == Op::DINP ? p.dinp : OP == Op::DWEIGHT ? p.dweight : p.out);
-    const long long lda = OP == Op::FWD ? p.C : p.OC, ldb = p.C, ldd = OP == Op::FWD ? p.OC : p.C;
+    // row pitches: dout (out) rows ldo, the C-wide tensors' rows ldc
+    const long long lda = OP == Op::FWD ? p.ldc : p.ldo, ldb = p.ldc, ldd = OP == Op::FWD ? p.ldo : p.ldc;
     const long long a_elems = (long long)p.BT * lda;
-    const long long b_elems = OP == Op::DWEIGHT ? (long long)p.BT * p.C : (long long)p.OC * p.C;
+    const long long b_elems = OP == Op::DWEIGHT ? (long long)p.BT * ldb : (long long)p.OC * ldb;
     const bool do_bias = OP == Op::DWEIGHT && p.dbias != nullptr && tile_n == 0;
 
     // Load geometry.  Wave w's i-th load of a region fills 1 KB block

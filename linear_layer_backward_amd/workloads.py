@@ -221,6 +221,20 @@ def config_cases(cfg: int) -> list:
     raise ValueError(f"no config {cfg}")
 
 
+def lm_head_unpadded_case() -> Case:
+    """The LM-head workload at the real GPT-2 vocabulary, OC = 50257 columns
+    (not a multiple of 8): the same draws as config 5 without its 47 zero pad
+    columns of dout and pad rows of the weight."""
+    B, T, C, OC = 8, 1024, 768, GPT2_VOCAB
+    s = 5000
+    inp = normal(s + INP, (B * T, C), 1.0, "bf16")
+    weight = normal(s + WEIGHT, (OC, C), 0.02, "bf16")
+    dout = lm_head_dout(s + LOGITS, s + TARGETS, B * T, GPT2_VOCAB, OC, "bf16")
+    return Case("lm_head bf16 B8 T1024 C768 OC50257", "bf16", B, T, C, OC, inp, weight, dout,
+                np.zeros((B * T, C), np.float32), np.zeros((OC, C), np.float32),
+                None, meta={"config": 5, "seed_base": s, "vocab": GPT2_VOCAB})
+
+
 # ---------------------------------------------------------------------------
 # cases for tests
 

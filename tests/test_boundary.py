@@ -115,9 +115,12 @@ def test_strerror(mmb):
 
 def test_path_choice(mmb):
     assert mmb.mmb_path(*args(dtype=1)) == 1
-    assert mmb.mmb_path(*args(dtype=1, C=764)) == 0          # C % 8 for bf16
-    assert mmb.mmb_path(*args(dtype=0, C=764)) == 1          # C % 4 is enough for fp32
-    assert mmb.mmb_path(*args(dtype=0, OC=3070)) == 0
+    # ragged rows take the MFMA tiles on packed copies
+    assert mmb.mmb_path(*args(dtype=1, C=764)) == 1          # C % 8 != 0 (bf16)
+    assert mmb.mmb_path(*args(dtype=0, C=764)) == 1          # C % 4 == 0 (fp32)
+    assert mmb.mmb_path(*args(dtype=0, OC=3070)) == 1
+    assert mmb.mmb_path(*args(dtype=1, B=8, C=768, OC=50257, bias=False)) == 1
+    assert mmb.mmb_path(*args(dtype=1, C=1 << 23)) == 0      # beyond the tiles' offsets
     a = args(dtype=1)
     a[4] += 8                                                  # inp only 8-byte aligned
     assert mmb.mmb_path(*a) == 0

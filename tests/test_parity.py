@@ -163,7 +163,7 @@ SMALL = [
     (1, 513, 200, 136, "bf16"),
     (1, 1, 8, 8, "bf16"),
     (1, 1, 4, 4, "f32"),
-    # generic path: C or OC not a multiple of the vector width
+    # C or OC not a multiple of the vector width: MFMA tiles on packed copies
     (2, 7, 65, 129, "f32"),
     (3, 5, 33, 17, "bf16"),
     (1, 3, 12, 10, "bf16"),
@@ -313,6 +313,57 @@ def test_tensor_binding(dev):
     torch.cuda.synchronize()
     check_full(case, (gi.cpu().numpy().astype(np.float64), gw.cpu().numpy().astype(np.float64),
                       gb.cpu().numpy().astype(np.float64)))
+
+
+# ---------------------------------------------------------------------------
+# ragged rows (C or OC not a multiple of the 16-byte vector): the tiles run on
+# zero-padded copies of the ragged tensors; every element compared
+
+RAGGED = [
+    (2, 150, 264, 401, "bf16"),    # OC ragged: dout packed
+    (2, 150, 266, 400, "bf16"),    # C ragged: inp, weight, dinp, dweight packed
+    (1, 300, 130, 261, "bf16"),    # both
+    (2, 64, 770, 1027, "bf16"),    # both, several tiles each way
+    (3, 100, 202, 330, "f32"),     # C ragged (fp32 vector: 4)
+    (3, 100, 200, 331, "f32"),     # OC ragged
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_shapes_take_the_tiles(dev, shape):
+    import torch
+    from linear_layer_backward_amd import mmb
+    B, T, C, OC, dt = shape
+    bufs = [torch.empty(n, dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=dev)
+            for n in (B * T * C, OC * C, OC, B * T * OC, B * T * C, OC * C)]
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+    assert mmb.mmb_path(*bufs, B, T, C, OC, code) == 1
+    case = wl.random_case(B, T, C, OC, dt, seed=OC)
+    check_full(case, run(case, dev))
+    case = wl.integer_case(B, T, C, OC, dt, seed=C)
+    check_exact(case, run(case, dev))
+
+
+@pytest.mark.parametrize("splits", [("3", "2"), ("2,5", "1,3")])
+def test_ragged_shapes_with_split_k(dev, tune, splits):
+    tune.set("MMB_SPLITS_DWEIGHT", splits[0])
+    tune.set("MMB_SPLITS_DINP", splits[1])
+    case = wl.integer_case(1, 300, 130, 261, "bf16", seed=3)
+    check_exact(case, run(case, dev))
+    case = wl.random_case(1, 300, 130, 261, "bf16", seed=4)
+    check_full(case, run(case, dev))
+
+
+def test_lm_head_unpadded_vocabulary(dev):
+    """The LM head at the real GPT-2 vocabulary (OC = 50257): MFMA tiles on a
+    packed copy of dout; sampled rows against the oracle, and exact with
+    integer inputs."""
+    case = wl.lm_head_unpadded_case()
+    print(f"[parity] {case.name}", flush=True)
+    check_sampled(case, run(case, dev), seed=11)
+    icase = wl.integer_case(8, 1024, 768, 50257, "bf16", seed=50257, with_bias=False)
+    print(f"[parity] {icase.name}", flush=True)
+    check_sampled(icase, run(icase, dev), seed=12, exact=True)
 
 
 # ---------------------------------------------------------------------------

@@ -109,9 +109,36 @@ def test_noalloc_with_split_partials(dev, tune):
     check(wl.random_case(1, 200, 264, 136, "bf16", seed=45), dev, with_oracle=True)
 
 
+def test_noalloc_ragged_rows(dev):
+    """C or OC not a multiple of the 16-byte vector: the packed copies live in
+    the scratch too (larger shape first, then a smaller one)."""
+    check(wl.random_case(2, 64, 770, 1027, "bf16", seed=46), dev, with_oracle=True)
+    check(wl.random_case(3, 5, 33, 17, "bf16", seed=47), dev, with_oracle=True)
+    check(wl.random_case(3, 100, 202, 330, "f32", seed=48), dev, with_oracle=True)
+
+
 def test_noalloc_generic_path(dev):
-    """C not a multiple of 8 (bf16): the generic kernels, which use no scratch."""
-    check(wl.random_case(3, 5, 33, 17, "bf16", seed=46), dev, with_oracle=True)
+    """An input 8 bytes off the 16-byte alignment: the generic kernels, which
+    use no scratch; same result as the allocating call."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    case = wl.random_case(2, 20, 64, 96, "bf16", seed=49)
+    outs = []
+    for fn in (mmb.mmb_backward_stream, mmb.mmb_backward_noalloc):
+        raw = torch.empty(case.BT * case.C + 8, dtype=torch.bfloat16, device=dev)
+        inp = raw[4:4 + case.BT * case.C]
+        inp.copy_(up(case.inp, "bf16", dev))
+        gi, gw = up(case.dinp0, "bf16", dev), up(case.dweight0, "bf16", dev)
+        gb = up(np.zeros(case.OC, np.float32), "bf16", dev)
+        assert mmb.mmb_path(gi, gw, gb, up(case.dout, "bf16", dev), inp,
+                            up(case.weight, "bf16", dev), case.B, case.T, case.C, case.OC,
+                            mmb.MMB_BF16) == 0
+        fn(gi, gw, gb, up(case.dout, "bf16", dev), inp, up(case.weight, "bf16", dev), case.B,
+           case.T, case.C, case.OC, mmb.MMB_BF16, torch.cuda.current_stream(dev))
+        torch.cuda.synchronize(dev)
+        outs.append([down(t, "bf16") for t in (gi, gw, gb)])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 def test_noalloc_rejects_plans_larger_than_the_scratch(dev, tune):
