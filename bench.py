@@ -126,18 +126,22 @@ def bench_layernorm(args):
     from linear_layer_backward_amd import mmb
     from linear_layer_backward_amd import workloads as wl
     dev = torch.device("cuda:0")
-    c = wl.layernorm_case(8, 1024, 1600, "bf16", seed=1)
+    dt = args.ln_dtype
+    c = wl.layernorm_case(8, 1024, 1600, dt, seed=1)
     print(f"[bench] workload: {c.name}", file=sys.stderr, flush=True)
 
     def up(a):
         raw = wl.storage(np.asarray(a, np.float32).ravel(), c.dtype)
-        return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        if dt == "bf16":
+            return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(raw.copy()).to(dev)
 
     b = [up(a) for a in (c.dinp0, c.dweight0, c.dbias0, c.dout, c.inp, c.weight, c.mean, c.rstd)]
     stream = torch.cuda.current_stream(dev)
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
 
     def step():
-        mmb.mmb_layernorm_backward(*b, c.B, c.T, c.C, mmb.MMB_BF16, stream)
+        mmb.mmb_layernorm_backward(*b, c.B, c.T, c.C, code, stream)
 
     warm_steps, warm_ms = warm_up(step, stream, args.warmup, args.min_warmup_ms)
     torch.cuda.synchronize(dev)
@@ -165,14 +169,14 @@ def bench_layernorm(args):
         "metric": METRIC_LN, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "warmup_steps_run": warm_steps,
         "warmup_ms": round(warm_ms, 1), "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
         "config": {"workload": c.name, "B": c.B, "T": c.T, "C": c.C, "bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (launch_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("ln_bwd_rows", 0, LN_SLUG),
-                     "lds_busy": measured_util("ln_bwd_rows", 0, "lds_util_pct", LN_SLUG),
+                     "traffic": measured_traffic("ln_bwd_rows", 0, ln_slug(dt)),
+                     "lds_busy": measured_util("ln_bwd_rows", 0, "lds_util_pct", ln_slug(dt)),
                      "kernel": "ln_bwd_rows + ln_bwd_reduce (one call)",
                      "launch_ms": round(launch_ms, 5),
                      "launch_ms_flushed": None if cold_ms is None else round(cold_ms, 5),
@@ -189,14 +193,14 @@ def bench_layernorm(args):
             oracle.layernorm_backward(c.dout, c.inp, c.weight, c.mean, c.rstd, B=c.B, T=c.T,
                                       C=c.C)
             reps += 1
-            dt = time.perf_counter() - t
-            if dt >= 2.0:
+            dt_s = time.perf_counter() - t
+            if dt_s >= 2.0:
                 break
         sb = reps * nbytes
-        out["cpu_baseline"] = {"value": sb / dt / 1e9, "unit": "GB/s", "cores": oracle.threads(),
+        out["cpu_baseline"] = {"value": sb / dt_s / 1e9, "unit": "GB/s", "cores": oracle.threads(),
                                "kind": "oracle",
                                "sample": f"{c.name}: the whole call {reps} times; fp64 OpenMP, "
-                                         f"{dt:.2f} s for {sb:.3e} bf16-equivalent bytes"}
+                                         f"{dt_s:.2f} s for {sb:.3e} bytes"}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -244,7 +248,11 @@ def source_digest(kernel: str = None) -> str:
     return h.hexdigest()[:16]
 
 
-LN_SLUG = "layernorm_bf16_B8_T1024_C1600"
+def ln_slug(dtype: str = "bf16") -> str:
+    return f"layernorm_{dtype}_B8_T1024_C1600"
+
+
+LN_SLUG = ln_slug("bf16")
 
 
 def measured_traffic(kernel: str, cfg: int, slug: str = None):
@@ -448,6 +456,8 @@ def main(argv=None):
                     choices=["backward", "forward", "backward_sr", "layernorm"],
                     help="backward (the metric), the forward product at the same shapes, or the "
                          "bf16 backward with stochastically rounded dweight/dbias")
+    ap.add_argument("--ln-dtype", default="bf16", choices=["bf16", "f32"],
+                    help="storage type of --op layernorm (the page's build is bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=512, metavar="MIB",
                     help="also time each launch after streaming MIB MiB through the caches "
@@ -466,7 +476,7 @@ def main(argv=None):
     if args.summarize_util:
         from linear_layer_backward_amd import workloads as wl
         if args.op == "layernorm":
-            k, name = "ln_bwd_rows", "LayerNorm backward bf16 B=8 T=1024 C=1600"
+            k, name = "ln_bwd_rows", f"LayerNorm backward {args.ln_dtype} B=8 T=1024 C=1600"
         else:
             k = kernel_name(args.op, "bf16" if args.config >= 4 else "f32")
             name = wl.CONFIG_NAMES[args.config] + (" (forward product)" if args.op == "forward"

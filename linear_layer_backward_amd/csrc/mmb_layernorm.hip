@@ -12,13 +12,13 @@
 //  * One wave64 per row, 8 waves per workgroup, one workgroup per CU, rows
 //    dealt out wave by wave (the row index is wave-uniform, so every buffer
 //    descriptor lives in scalar registers).  Lane l owns the 16-byte column
-//    vectors l, l + 64, ... (NJ <= 4 of them: C <= 2048 in bf16, 1024 in
-//    fp32; wider rows take the generic kernels below), so each row is read
+//    vectors l, l + 64, ... (NJ <= 4 of them in bf16, C <= 2048; NJ <= 8 in
+//    fp32, C <= 2048; wider rows take the generic kernels below), so each row is read
 //    with fully coalesced 16-byte loads; the weight row sits in LDS and the
 //    lane's dweight / dbias sums stay in registers for all its rows.
-//  * Each wave keeps two rows in flight: the loads of its next row (dout,
-//    inp, the old dinp, mean, rstd) are issued before it works on the
-//    current one.
+//  * With up to 4 vectors per lane each wave keeps two rows in flight: the
+//    loads of its next row (dout, inp, the old dinp, mean, rstd) are issued
+//    before it works on the current one; with 8, one row.
 //  * The two row means are wave reductions in a fixed order (DPP lane moves).
 //  * dweight / dbias: each wave writes its sums to its own LDS slot, each
 //    column is added over the 8 waves in wave order, and the workgroup
@@ -80,7 +80,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <typename T, int NJ>
 __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     constexpr int V = Vec<T>::N;
-    constexpr int SLOT = 2 * 64 * NJ * V;     // one wave's [dweight | dbias] sums
+    // Rows in flight per wave: two up to 4 vectors per lane; with 8 (wide
+    // rows) one, as two would not fit the registers (an fp32 row of 8
+    // vectors per lane is as many bytes as a bf16 row of 4, so the bytes in
+    // flight per CU stay the same).
+    constexpr bool PIPE2 = NJ <= 4;
+    static_assert(NJ <= 4 || sizeof(T) == 4, "8 bf16 vectors per lane would spill registers");
+    constexpr int COLS = 64 * NJ * V;
+    constexpr int SLOT = 2 * COLS;            // one wave's [dweight | dbias] sums
     __shared__ float red[LN_NW * SLOT];
     const int tid = threadIdx.x, lane = tid & 63;
     // uniform per wave: the row index, and so every buffer descriptor built
@@ -177,14 +184,22 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
             wl[v] = buffer_load16(rw, (uint32_t)(V * v * (int)sizeof(T)) | oob_if_ge(V * v, C), 0);
         __syncthreads();
     }
-    while (r < p.BT) {
-        load_set(B, r + nwaves);
-        process(A, r);
-        r += nwaves;
-        if (r >= p.BT) break;
-        load_set(A, r + nwaves);
-        process(B, r);
-        r += nwaves;
+    if constexpr (PIPE2) {
+        while (r < p.BT) {
+            load_set(B, r + nwaves);
+            process(A, r);
+            r += nwaves;
+            if (r >= p.BT) break;
+            load_set(A, r + nwaves);
+            process(B, r);
+            r += nwaves;
+        }
+    } else {
+        while (r < p.BT) {
+            process(A, r);
+            r += nwaves;
+            if (r < p.BT) load_set(A, r);
+        }
     }
     // the 8 waves' column sums [dweight | dbias], each wave in its own slot,
     // then added in wave order per column
@@ -195,16 +210,16 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
         for (int e = 0; e < V; ++e) {
             const int i = V * (lane + 64 * j) + e;
             mine[i] = aw[j][e];
-            mine[64 * NJ * V + i] = ab[j][e];
+            mine[COLS + i] = ab[j][e];
         }
     __syncthreads();
     float* part = p.partial + (long long)blockIdx.x * 2 * C;
     for (int i = tid; i < C; i += LN_NT) {
-        float sw = red[i], sb = red[64 * NJ * V + i];
+        float sw = red[i], sb = red[COLS + i];
 #pragma unroll
         for (int wv = 1; wv < LN_NW; ++wv) {
             sw += red[wv * SLOT + i];
-            sb += red[wv * SLOT + 64 * NJ * V + i];
+            sb += red[wv * SLOT + COLS + i];
         }
         part[i] = sw;
         part[C + i] = sb;
@@ -308,6 +323,8 @@ hipError_t launch_ln(const LNParams& p, int G, int nj, hipStream_t s) {
     if (nj == 1) return launch_rows<T, 1>(p, G, s);
     if (nj == 2) return launch_rows<T, 2>(p, G, s);
     if (nj == 4) return launch_rows<T, 4>(p, G, s);
+    if constexpr (sizeof(T) == 4)
+        if (nj == 8) return launch_rows<T, 8>(p, G, s);
     return hipErrorInvalidValue;
 }
 
@@ -315,7 +332,9 @@ hipError_t launch_ln(const LNParams& p, int G, int nj, hipStream_t s) {
 
 int ln_vectors_per_lane(int dtype, int C) {
     const int V = dtype == 1 ? 8 : 4;
-    const int nmax = 4;   // 8 vectors per lane would spill registers
+    // 8 vectors per lane fit the registers (one row in flight) for fp32; for
+    // bf16 they would spill
+    const int nmax = dtype == 1 ? 4 : 8;
     if (C % V != 0) return 0;
     const int nv = C / V;
     for (int nj = 1; nj <= nmax; nj *= 2)

@@ -45,11 +45,12 @@ def check(c, got):
         assert_close(g, r, c.dtype, name)
 
 
-SHAPES = [  # (B, T, C, dtype): row kernel with 1, 2 and 4 vectors per lane, ragged C
+SHAPES = [  # (B, T, C, dtype): row kernel with 1, 2, 4 (and fp32 8) vectors per lane
     (2, 37, 1600, "bf16"), (1, 300, 768, "bf16"), (3, 20, 256, "bf16"), (1, 5, 2048, "bf16"),
     (2, 33, 1000, "bf16"), (2, 50, 768, "f32"), (1, 70, 1024, "f32"), (3, 9, 100, "f32"),
+    (2, 13, 1600, "f32"), (1, 40, 2048, "f32"), (3, 17, 1028, "f32"),
     # generic kernels: C not a multiple of the vector width, or wider than the row kernel
-    (2, 11, 1603, "bf16"), (1, 9, 2056, "bf16"), (2, 13, 1600, "f32"), (1, 4, 7, "f32"),
+    (2, 11, 1603, "bf16"), (1, 9, 2056, "bf16"), (1, 6, 2052, "f32"), (1, 4, 7, "f32"),
     # degenerate: one row (one busy wave), one channel
     (1, 1, 768, "bf16"), (1, 1, 8, "f32"), (3, 1, 1, "f32"), (1, 2, 1, "bf16"),
 ]
@@ -65,8 +66,8 @@ def test_layernorm_small(dev, shape, prefill):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_layernorm_page_shape(dev, dt):
-    """The page's benchmark shape B=8, T=1024, C=1600 (fp32 takes the generic
-    kernels at this C)."""
+    """The page's benchmark shape B=8, T=1024, C=1600 (fp32 takes the row
+    kernel with 8 vectors per lane and one row in flight per wave)."""
     c = wl.layernorm_case(8, 1024, 1600, dt, seed=1)
     print(f"[parity] {c.name}", flush=True)
     check(c, run_ln(c, dev))
