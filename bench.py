@@ -334,32 +334,61 @@ def _counter_mean(run_dir: str, counter: str, kernel: str):
     return float(np.mean(vals)), len(vals)
 
 
-def summarize_counters(cfg: int, dirs, copy_mib: int, op: str = "backward") -> str:
+def summarize_counters(cfg: int, dirs, copy_mib: int, op: str = "backward",
+                       ln_dtype: str = "bf16") -> str:
     """Text summary of two FETCH_SIZE / WRITE_SIZE passes over the workload and
     the same two passes over a plain copy of copy_mib MiB: the copy kernel's
-    readings fix the KiB-per-counter-unit scale of each counter."""
+    readings fix the KiB-per-counter-unit scale of each counter.  The figure
+    is per step: the MLP pair launches its kernel twice, and a LayerNorm call
+    is a row kernel and a reduce kernel."""
     from linear_layer_backward_amd import workloads as wl
     fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs
-    dtype = "bf16" if cfg >= 4 else "f32"
-    kernel = kernel_name(op, dtype)
+    if op == "layernorm":
+        kernels, per_step = ["ln_bwd_rows", "ln_bwd_reduce"], 1
+        digest_kernel = "ln_bwd_rows"
+        name = f"LayerNorm backward {ln_dtype} B=8 T=1024 C=1600"
+    else:
+        kernels = [kernel_name(op, "bf16" if cfg >= 4 else "f32")]
+        digest_kernel = kernels[0]
+        per_step = len(wl.config_cases(cfg)) if cfg == 3 else 1
+        name = wl.CONFIG_NAMES[cfg] + (" (forward product)" if op == "forward" else "")
     copy_kib = copy_mib * 1024.0
     cf, ncf = _counter_mean(cal_fetch_dir, "FETCH_SIZE", "__amd_rocclr_copyBuffer")
     cw, ncw = _counter_mean(cal_write_dir, "WRITE_SIZE", "__amd_rocclr_copyBuffer")
-    kf, nkf = _counter_mean(fetch_dir, "FETCH_SIZE", kernel)
-    kw, nkw = _counter_mean(write_dir, "WRITE_SIZE", kernel)
     sf, sw = copy_kib / cf, copy_kib / cw
-    fetch_b, write_b = kf * sf * 1024, kw * sw * 1024
     lines = [
-        f"kernel: {kernel}",
-        f"workload: {wl.CONFIG_NAMES[cfg]}" + (" (forward product)" if op == "forward" else ""),
-        f"source_digest: {source_digest(kernel)}",
+        f"kernel: {' + '.join(kernels)}",
+        f"workload: {name}",
+        f"source_digest: {source_digest(digest_kernel)}",
         f"copy calibration: {copy_mib} MiB each way; FETCH_SIZE {cf:.1f} ({ncf} dispatches), "
         f"WRITE_SIZE {cw:.1f} ({ncw}); scale fetch {sf:.4f}, write {sw:.4f}",
-        f"kernel FETCH_SIZE mean {kf:.1f} over {nkf} dispatches -> {fetch_b:.4e} bytes",
-        f"kernel WRITE_SIZE mean {kw:.1f} over {nkw} dispatches -> {write_b:.4e} bytes",
-        f"hbm_bytes_per_launch: {fetch_b + write_b:.6e}",
     ]
+    total = 0.0
+    for k in kernels:
+        kf, nkf = _counter_mean(fetch_dir, "FETCH_SIZE", k)
+        kw, nkw = _counter_mean(write_dir, "WRITE_SIZE", k)
+        fetch_b, write_b = kf * sf * 1024 * per_step, kw * sw * 1024 * per_step
+        total += fetch_b + write_b
+        lines += [f"{k} FETCH_SIZE mean {kf:.1f} over {nkf} dispatches, {per_step} per step -> "
+                  f"{fetch_b:.4e} bytes per step",
+                  f"{k} WRITE_SIZE mean {kw:.1f} over {nkw} dispatches, {per_step} per step -> "
+                  f"{write_b:.4e} bytes per step"]
+    lines.append(f"hbm_bytes_per_launch: {total:.6e}")
     return "\n".join(lines) + "\n"
+
+
+def summarize_trace(run_dir: str, log: str, title: str, digest_kernel: str) -> str:
+    """Text summary of one rocprofv3 --kernel-trace --stats run of bench.py:
+    the per-kernel statistics table and the bench line of the same run."""
+    stats = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {run_dir}")
+    line = [ln for ln in open(log).read().splitlines() if ln.startswith("{")][-1]
+    return (f"# {title}: kernel trace\n"
+            f"source_digest: {source_digest(digest_kernel)}\n\n"
+            f"run_kernel_stats.csv:\n{open(stats[0]).read().strip()}\n\n"
+            f"bench.py line of the same run (launch_ms from HIP events on the launch stream):\n"
+            f"{line}\n")
 
 
 def upload(case, dev):
@@ -464,6 +493,9 @@ def main(argv=None):
                          "(cold-cache figure; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "LOG"),
+                    help="print the kernel-trace summary of a rocprofv3 --kernel-trace --stats "
+                         "run (output DIR) of this bench, whose stdout is in LOG")
     ap.add_argument("--summarize-util", metavar="DIR",
                     help="print the utilisation summary (MFMA, LDS, VALU busy) of the dominant "
                          "kernel from a rocprofv3 --pmc run of bench.UTIL_COUNTERS in DIR")
@@ -472,6 +504,18 @@ def main(argv=None):
                          "workload FETCH_SIZE, workload WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
                          "(the copy run made with --copy-calibration MIB)")
     args = ap.parse_args(argv)
+
+    if args.summarize_trace:
+        from linear_layer_backward_amd import workloads as wl
+        if args.op == "layernorm":
+            k = "ln_bwd_rows"
+            title = f"ln_bwd_rows + ln_bwd_reduce, LayerNorm backward {args.ln_dtype} B=8 T=1024 C=1600"
+        else:
+            k = kernel_name(args.op, "bf16" if args.config >= 4 else "f32")
+            title = f"{k}, workload {wl.CONFIG_NAMES[args.config]}" + (
+                " (forward product)" if args.op == "forward" else "")
+        print(summarize_trace(args.summarize_trace[0], args.summarize_trace[1], title, k), end="")
+        return 0
 
     if args.summarize_util:
         from linear_layer_backward_amd import workloads as wl
@@ -486,7 +530,7 @@ def main(argv=None):
 
     if args.summarize_counters:
         print(summarize_counters(args.config, args.summarize_counters,
-                                 args.copy_calibration or 256, args.op), end="")
+                                 args.copy_calibration or 256, args.op, args.ln_dtype), end="")
         return 0
 
     if args.gpus != 1:
