@@ -301,6 +301,48 @@ def test_side_stream(dev):
     check_full(case, run(case, dev, stream=s))
 
 
+def test_two_streams_interleaved(dev, tune):
+    """Calls on two streams, enqueued alternately with no synchronisation in
+    between: each stream has its own workspace and its own copy of each
+    plan's work list, uploaded in its own order; a plan first made on one
+    stream is then used on the other.  Split counts force partial tiles, so
+    the workspaces are in use; every result is exact."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    tune.set("MMB_SPLITS_DWEIGHT", "3")
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    shapes = [(2, 150, 264, 400, "bf16"), (3, 100, 200, 328, "f32"), (1, 300, 130, 261, "bf16")]
+    jobs = []
+    for n in range(6):
+        B, T, C, OC, dt = shapes[n % 3]
+        case = wl.integer_case(B, T, C, OC, dt, seed=60 + n)
+        bufs = [to_dev(a, dt, dev)[1] for a in (case.dinp0, case.dweight0, case.dout, case.inp,
+                                                 case.weight)]
+        gb = to_dev(np.zeros(OC, np.float32), dt, dev)[1]
+        jobs.append((case, bufs, gb, streams[n % 2]))
+    torch.cuda.synchronize(dev)
+    for case, (gi, gw, dout, inp, w), gb, st in jobs:
+        mmb.mmb_backward_stream(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC,
+                                mmb.MMB_BF16 if case.dtype == "bf16" else mmb.MMB_FP32, st)
+    torch.cuda.synchronize(dev)
+    for case, (gi, gw, _, _, _), gb, _ in jobs:
+        dt = case.dtype
+        check_exact(case, (from_dev(gi, dt).reshape(case.BT, case.C),
+                           from_dev(gw, dt).reshape(case.OC, case.C), from_dev(gb, dt)))
+
+
+def test_release_then_reuse(dev):
+    """mmb_release synchronises and frees every workspace, plan and work list;
+    the next call allocates again and is exact."""
+    from linear_layer_backward_amd import mmb
+    case = wl.integer_case(2, 150, 264, 400, "bf16", seed=70)
+    check_exact(case, run(case, dev))
+    assert mmb._lib.mmb_release() == 0
+    check_exact(case, run(case, dev))
+    case = wl.integer_case(1, 300, 130, 261, "bf16", seed=71)
+    check_exact(case, run(case, dev))
+
+
 def test_tensor_binding(dev):
     """mmb.backward infers shapes and dtype from torch tensors."""
     import torch
