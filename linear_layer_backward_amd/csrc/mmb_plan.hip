@@ -66,10 +66,12 @@ struct Layout {
 };
 
 // Launch order.  Inside one GEMM, tiles with fewer splits (longer units)
-// come first; among equal ones, dweight units are ordered (split, tile_m,
-// tile_n) so that units running together share the inp rows of one K range
-// and the dout columns of one tile_m, and dinp units (tile_m, split, tile_n)
-// so that they share dout rows.  Every run of equal split counts, of the GEMM
+// come first; among equal ones, units are ordered (split, tile_m, tile_n), so
+// that the units an XCD runs together share one K range: the tile_n units of
+// a tile_m share its A rows (dout) and the tile_m units share the B slab of
+// each tile_n (inp for dweight, weight for dinp).  Ordered (tile_m, split,
+// tile_n) instead, every XCD ran every K range of the LM head's dinp and
+// fetched the whole 77 MB weight.  Every run of equal split counts, of the GEMM
 // with the longer units first, is dealt out evenly in contiguous pieces, one
 // per XCD (the remainders rotate over the XCDs), and the XCD sequences are
 // interleaved so that workgroup i lands on XCD i % xcds.
@@ -97,15 +99,9 @@ std::vector<Unit> make_units(const GemmPlan g[2], const Layout& L, const DeviceI
                 const int kt1 = (int)((long long)(s + 1) * G.kiters / S);
                 per[k].push_back(Unit{make_int4(k, m, n, s), make_int4(kt0, kt1, S, slot_of[k][t])});
             };
-            if (k == UNIT_DINP) {
+            for (int s = 0; s < S; ++s)
                 for (int m = 0; m < G.tiles_m; ++m)
-                    for (int s = 0; s < S; ++s)
-                        for (int n = 0; n < G.tiles_n; ++n) emit(m, n, s);
-            } else {
-                for (int s = 0; s < S; ++s)
-                    for (int m = 0; m < G.tiles_m; ++m)
-                        for (int n = 0; n < G.tiles_n; ++n) emit(m, n, s);
-            }
+                    for (int n = 0; n < G.tiles_n; ++n) emit(m, n, s);
         }
     }
     auto longest = [&](int k) {

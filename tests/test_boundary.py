@@ -262,9 +262,9 @@ GPT2_PLANS = {
     ("350M", 256): {"qkv": (2, 1), "attn_proj": (7, 1), "fc": (2, 1), "fc_proj": (2, 1)},
     ("350M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (1, 1), "fc_proj": (1, 1)},
     ("774M", 256): {"qkv": (1, 1), "attn_proj": (6, 1), "fc": (1, 3), "fc_proj": (1, 1)},
-    ("774M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (1, 2), "fc_proj": (1, 1)},
+    ("774M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (1, 1), "fc_proj": (1, 1)},
     ("1558M", 256): {"qkv": (2, 1), "attn_proj": (3, 1), "fc": (1, 2), "fc_proj": (1, 1)},
-    ("1558M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (3, 2), "fc_proj": (1, 1)},
+    ("1558M", 32): {"qkv": (1, 1), "attn_proj": (1, 1), "fc": (1, 1), "fc_proj": (1, 1)},
 }
 
 

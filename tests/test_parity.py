@@ -452,6 +452,23 @@ def test_full_shape_integer_exact(dev, shape):
     check_sampled(case, run(case, dev), seed=5, exact=True)
 
 
+@pytest.mark.parametrize("shape", [(2, 1024, 768, 3072, "bf16"), (1, 1024, 768, 2304, "f32"),
+                                   (1, 1024, 3072, 768, "bf16")],
+                         ids=["fc_bf16_bt2048", "qkv_f32_bt1024", "fc_proj_bf16_bt1024"])
+def test_gpt2_layer_dims_every_element(dev, shape):
+    """GPT-2 124M layer dimensions (C, OC) at B*T = 2048 / 1024 rows: every
+    element of dinp, dweight and dbias, exact with integer inputs and within
+    tolerance with random ones (the full-size workloads are checked on
+    sampled rows above; the oracle's full fp64 pass there takes about a
+    minute)."""
+    B, T, C, OC, dt = shape
+    case = wl.integer_case(B, T, C, OC, dt, seed=C + OC, prefill=True)
+    print(f"[parity] {case.name}", flush=True)
+    check_exact(case, run(case, dev))
+    case = wl.random_case(B, T, C, OC, dt, seed=C + OC + 1)
+    check_full(case, run(case, dev))
+
+
 def test_plan_changes_between_calls(dev, tune):
     """Shapes and split plans alternate on one stream; the workspace is
     reused and regrown, and every result stays exact."""
