@@ -247,6 +247,14 @@ def random_case(B, T, C, OC, dtype="f32", seed=0, with_bias=True, prefill=True,
                  with_bias, seed_add=s)
 
 
+def small_integers(seed: int, shape, lo: int = -2, hi: int = 2) -> np.ndarray:
+    """Integers drawn uniformly from [lo, hi] as int8: one byte per element,
+    for tensors of billions of elements (the values are exact in fp32 and
+    bf16, like integer_case's)."""
+    assert -128 <= lo <= hi <= 127
+    return _rng(30_000_000 + seed).integers(lo, hi + 1, size=shape, dtype=np.int8)
+
+
 def integer_case(B, T, C, OC, dtype="f32", seed=0, with_bias=True, prefill=True,
                  lo=-2, hi=2) -> Case:
     """Every input and prefill drawn uniformly from the integers [lo, hi].
