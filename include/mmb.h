@@ -31,13 +31,15 @@
  * caller.  dout, inp, weight are read only; dinp and dweight are read and
  * written; dbias is written only.  Output buffers may not overlap each other
  * or any input (MMB_ERR_ALIAS).  Any alignment and any dims >= 1 are
- * accepted.  16-byte aligned pointers take the MFMA path: directly when C and
- * OC are multiples of 8 (bf16) or 4 (fp32); otherwise the tensors whose rows
- * are not whole 16-byte vectors (dout when OC is ragged; inp, weight, dinp
- * and dweight when C is) are copied into zero-padded row pitches in the
- * workspace first, and dinp and dweight copied back after (an extra pass over
- * those tensors).  Pointers off the 16-byte alignment take a slower generic
- * path.
+ * accepted.  Calls take the MFMA path: directly when every streamed tensor is
+ * 16-byte aligned and C and OC are multiples of 8 (bf16) or 4 (fp32);
+ * otherwise each tensor whose rows are not whole 16-byte vectors (dout when
+ * OC is ragged; inp, weight, dinp and dweight when C is) or whose address is
+ * not 16-byte aligned is copied into an aligned, zero-padded row pitch in the
+ * workspace first, and the outputs among them (dinp, dweight) are copied back
+ * after (an extra pass over those tensors).  dbias needs no alignment.  Only
+ * C or OC above 2^22, or a pointer not aligned to its element size, take the
+ * much slower generic path (one thread per output element).
  *
  * The library owns only a per-(device, stream) workspace (split-K partial
  * sums, tile counters and work lists), allocated on first use, grown on
@@ -144,8 +146,8 @@ int mmb_backward_sr(void* dinp, void* dweight, void* dbias,
  * bf16).  Every call on a device shares that device's
  * scratch, which keeps the last call's contents: calls that overlap on one
  * device (several streams, or host threads) race and give wrong results;
- * order them on one stream.  Ragged rows (see the file comment) keep their
- * packed copies in the scratch too. */
+ * order them on one stream.  Ragged or unaligned tensors (see the file
+ * comment) keep their packed copies in the scratch too. */
 int mmb_backward_noalloc(void* dinp, void* dweight, void* dbias,
                          const void* dout, const void* inp, const void* weight,
                          int B, int T, int C, int OC, int dtype, void* stream);
@@ -160,8 +162,8 @@ int mmb_check_args(const void* dinp, const void* dweight, const void* dbias,
 const char* mmb_strerror(int status);
 
 /* Which kernel path a call with these arguments takes: 1 = MFMA tiles
- * (directly or on packed copies of ragged rows), 0 = generic path, or a
- * negative mmb_status.  Host only, no HIP call. */
+ * (directly or on packed copies of ragged or unaligned tensors), 0 = generic
+ * path, or a negative mmb_status.  Host only, no HIP call. */
 int mmb_path(const void* dinp, const void* dweight, const void* dbias,
              const void* dout, const void* inp, const void* weight,
              int B, int T, int C, int OC, int dtype);
@@ -198,9 +200,12 @@ int mmb_tile_shape(int dtype, int* shape);
  * read only; one dtype for all four tensors, with the same arithmetic: fp32
  * throughout, or bf16 storage with fp32 accumulation and one round to
  * nearest-even of  fp32 sum + bias.  out may not overlap inp, weight or bias
- * (MMB_ERR_ALIAS).  16-byte aligned out, inp, weight and bias with C and OC
- * multiples of 8 (bf16) or 4 (fp32) take the MFMA tiles, anything else the
- * generic path.  Workspace, errors, determinism and streams as for
+ * (MMB_ERR_ALIAS).  Paths as for mmb_backward: 16-byte aligned out, inp,
+ * weight and bias with C and OC multiples of 8 (bf16) or 4 (fp32) take the
+ * MFMA tiles directly; ragged or unaligned tensors go through packed copies
+ * (inp and weight for ragged C; out and bias for ragged OC; out is copied
+ * back); C or OC above 2^22, or a pointer not aligned to its element size,
+ * the generic path.  Workspace, errors, determinism and streams as for
  * mmb_backward (the two share the per-(device, stream) workspace). */
 int mmb_forward(void* out, const void* inp, const void* weight, const void* bias,
                 int B, int T, int C, int OC, int dtype);
@@ -213,8 +218,8 @@ int mmb_forward_stream(void* out, const void* inp, const void* weight, const voi
 int mmb_forward_check_args(const void* out, const void* inp, const void* weight,
                            const void* bias, int B, int T, int C, int OC, int dtype);
 
-/* Which kernel path a forward call takes: 1 = MFMA tiles, 0 = generic,
- * or a negative mmb_status.  Host only. */
+/* Which kernel path a forward call takes: 1 = MFMA tiles (directly or on
+ * packed copies), 0 = generic, or a negative mmb_status.  Host only. */
 int mmb_forward_path(const void* out, const void* inp, const void* weight,
                      const void* bias, int B, int T, int C, int OC, int dtype);
 

@@ -89,108 +89,133 @@ int check_fwd(const void* out, const void* inp, const void* weight, const void* 
     return MMB_OK;
 }
 
-// 1 when the MFMA tiles can take a forward call: as for the backward pass,
-// and the bias (read as 16-byte groups in the epilogue) is aligned too.
-int choose_path_fwd(const void* out, const void* inp, const void* weight, const void* bias, int C,
-                    int OC, int dtype) {
-    const int vec = dtype == MMB_BF16 ? 8 : 4;
-    if (C % vec != 0 || OC % vec != 0) return 0;
-    if (C > (1 << 22) || OC > (1 << 22)) return 0;
-    const void* ptrs[4] = {out, inp, weight, bias};
-    for (const void* p : ptrs)
-        if ((uintptr_t)p % 16 != 0) return 0;   // NULL bias passes
-    return 1;
-}
+// A tensor the tiles can read or write in place: 16-byte aligned (the tiles
+// move 16-byte vectors).  One aligned to its element size but not to 16
+// bytes goes through a packed copy; one not even aligned to its element size
+// sends the call to the generic path.
+bool aligned16(const void* p) { return (uintptr_t)p % 16 == 0; }
+bool elem_aligned(const void* p, int dtype) { return (uintptr_t)p % elem_size(dtype) == 0; }
 
-// Path of a backward call: 0 the generic kernels (a streamed buffer not
-// 16-byte aligned, or a dimension too large for the tiles' 32-bit offsets),
-// 1 the MFMA tiles on the caller's buffers, 2 the MFMA tiles on packed
-// copies (C or OC not a multiple of the 16-byte vector, so vectors would
-// straddle row ends; see Packing).  dbias is written one element at a time.
-int choose_path(const void* dinp, const void* dweight, const void* dout, const void* inp,
-                const void* weight, int C, int OC, int dtype) {
-    const int vec = dtype == MMB_BF16 ? 8 : 4;
+// Path of a call: 0 the generic kernels (C or OC too large for the tiles'
+// 32-bit offsets, or a streamed buffer not aligned to its element size), 1
+// the MFMA tiles on the caller's buffers, 2 the MFMA tiles with some tensors
+// through packed copies (rows that are not whole 16-byte vectors, or a
+// buffer off the 16-byte alignment; see Packing).  NULL entries (no bias)
+// are skipped; dbias is written one element at a time and never matters.
+int choose_path_of(const void* const* ptrs, int n, int C, int OC, int dtype) {
     // the tiles address one 64-row K slab of an operand with 32-bit offsets
     if (C > (1 << 22) || OC > (1 << 22)) return 0;
-    const void* ptrs[5] = {dinp, dweight, dout, inp, weight};
-    for (const void* p : ptrs)
-        if ((uintptr_t)p % 16 != 0) return 0;
-    return (C % vec != 0 || OC % vec != 0) ? 2 : 1;
+    const int vec = dtype == MMB_BF16 ? 8 : 4;
+    bool direct = C % vec == 0 && OC % vec == 0;
+    for (int i = 0; i < n; ++i) {
+        if (!ptrs[i]) continue;
+        if (!elem_aligned(ptrs[i], dtype)) return 0;
+        direct = direct && aligned16(ptrs[i]);
+    }
+    return direct ? 1 : 2;
 }
 
-// Ragged shapes on the MFMA tiles: the tensors whose rows are not whole
-// 16-byte vectors are copied into zero-padded row pitches (dout when OC is
-// ragged; inp, weight, dinp and dweight when C is), the tiles run on the
-// copies with those pitches (the zero pads add nothing to any sum, and the
-// epilogue writes only the logical columns), and dinp and dweight are copied
-// back.  Offsets into one buffer, each part 256-byte aligned.
+int choose_path(const void* dinp, const void* dweight, const void* dout, const void* inp,
+                const void* weight, int C, int OC, int dtype) {
+    const void* ptrs[5] = {dinp, dweight, dout, inp, weight};
+    return choose_path_of(ptrs, 5, C, OC, dtype);
+}
+
+int choose_path_fwd(const void* out, const void* inp, const void* weight, const void* bias, int C,
+                    int OC, int dtype) {
+    const void* ptrs[4] = {out, inp, weight, bias};
+    return choose_path_of(ptrs, 4, C, OC, dtype);
+}
+
+// Packed copies: a tensor whose rows are not whole 16-byte vectors (the
+// OC-wide dout, out and bias when OC is ragged; the C-wide inp, weight, dinp
+// and dweight when C is) or whose address is not 16-byte aligned is copied
+// into a 16-byte aligned, zero-padded row pitch in the workspace (the pads add
+// nothing to any sum, and the epilogues write only the logical columns); the
+// tiles run on the copies with those pitches, and the outputs among them
+// (dinp, dweight, out) are copied back.  out is assigned by the forward, so
+// its copy starts with no contents.  Offsets into one buffer, each part
+// 256-byte aligned.
+enum PackedTensor { P_DOUT, P_INP, P_WEIGHT, P_DINP, P_DWEIGHT, P_OUT, P_BIAS, P_COUNT };
 struct Packing {
-    bool oc = false, c = false;   // dout / the C-wide tensors packed
-    long long ldo = 0, ldc = 0;   // row pitches the tiles use
-    size_t dout = 0, inp = 0, weight = 0, dinp = 0, dweight = 0, bytes = 0;
+    bool on[P_COUNT] = {};
+    size_t off[P_COUNT] = {};
+    long long ldo = 0, ldc = 0;   // row pitches the tiles use (OC-wide, C-wide tensors)
+    size_t bytes = 0;
 };
 
-Packing plan_packing(int dtype, long long BT, int C, int OC) {
+// ptrs[t]: the caller's tensor t, or NULL where the call has none (the
+// backward has no out or bias to pack, the forward no dout, dinp, dweight).
+Packing plan_packing(int dtype, long long BT, int C, int OC, const void* const ptrs[P_COUNT]) {
     const int vec = dtype == MMB_BF16 ? 8 : 4;
     const size_t es = elem_size(dtype);
     Packing k;
-    k.oc = OC % vec != 0;
-    k.c = C % vec != 0;
-    k.ldo = (OC + vec - 1) / vec * vec;
-    k.ldc = (C + vec - 1) / vec * vec;
-    if (!k.oc) k.ldo = OC;
-    if (!k.c) k.ldc = C;
-    auto part = [&](size_t* off, long long rows, long long pitch) {
-        *off = k.bytes;
-        k.bytes += (size_t)rows * (size_t)pitch * es;
+    k.ldo = ((long long)OC + vec - 1) / vec * vec;
+    k.ldc = ((long long)C + vec - 1) / vec * vec;
+    const bool oc_wide[P_COUNT] = {true, false, false, false, false, true, true};
+    const long long rows[P_COUNT] = {BT, BT, OC, BT, OC, BT, 1};
+    for (int t = 0; t < P_COUNT; ++t) {
+        if (!ptrs[t]) continue;
+        const bool ragged = oc_wide[t] ? OC % vec != 0 : C % vec != 0;
+        if (!ragged && aligned16(ptrs[t])) continue;
+        k.on[t] = true;
+        k.off[t] = k.bytes;
+        k.bytes += (size_t)rows[t] * (size_t)(oc_wide[t] ? k.ldo : k.ldc) * es;
         k.bytes = (k.bytes + 255) / 256 * 256;
-    };
-    if (k.oc) part(&k.dout, BT, k.ldo);
-    if (k.c) {
-        part(&k.inp, BT, k.ldc);
-        part(&k.dinp, BT, k.ldc);
-        part(&k.weight, OC, k.ldc);
-        part(&k.dweight, OC, k.ldc);
     }
     return k;
 }
 
-// Enqueue the packing copies on `s` and point the tile parameters at them.
+Packing plan_packing_bwd(int dtype, long long BT, int C, int OC, const void* dinp,
+                         const void* dweight, const void* dout, const void* inp,
+                         const void* weight) {
+    const void* ptrs[P_COUNT] = {dout, inp, weight, dinp, dweight, nullptr, nullptr};
+    return plan_packing(dtype, BT, C, OC, ptrs);
+}
+
+Packing plan_packing_fwd(int dtype, long long BT, int C, int OC, const void* out, const void* inp,
+                         const void* weight, const void* bias) {
+    const void* ptrs[P_COUNT] = {nullptr, inp, weight, nullptr, nullptr, out, bias};
+    return plan_packing(dtype, BT, C, OC, ptrs);
+}
+
+// Enqueue the packing copies on `s` and point the tile parameters at them
+// (tp holds the caller's pointers on entry).
 hipError_t pack_operands(const Packing& k, char* base, TilesParams* tp, int dtype, hipStream_t s) {
     const int es = (int)elem_size(dtype);
     const long long BT = tp->BT;
-    hipError_t e = hipSuccess;
-    if (k.oc) {
-        e = launch_pack(base + k.dout, k.ldo, tp->dout, tp->OC, BT, tp->OC, es, s);
-        if (e != hipSuccess) return e;
-        tp->dout = base + k.dout;
-    }
-    if (k.c) {
-        const void* src[4] = {tp->inp, tp->dinp, tp->weight, tp->dweight};
-        const size_t off[4] = {k.inp, k.dinp, k.weight, k.dweight};
-        const long long rows[4] = {BT, BT, tp->OC, tp->OC};
-        for (int i = 0; i < 4; ++i) {
-            e = launch_pack(base + off[i], k.ldc, src[i], tp->C, rows[i], tp->C, es, s);
+    const void** fields[P_COUNT] = {&tp->dout, &tp->inp, &tp->weight, (const void**)&tp->dinp,
+                                    (const void**)&tp->dweight, (const void**)&tp->out,
+                                    &tp->bias};
+    const long long rows[P_COUNT] = {BT, BT, tp->OC, BT, tp->OC, BT, 1};
+    const bool oc_wide[P_COUNT] = {true, false, false, false, false, true, true};
+    for (int t = 0; t < P_COUNT; ++t) {
+        if (!k.on[t]) continue;
+        const long long pitch = oc_wide[t] ? k.ldo : k.ldc;
+        const int width = oc_wide[t] ? tp->OC : tp->C;
+        if (t != P_OUT) {   // out is assigned: nothing to copy in
+            const hipError_t e = launch_pack(base + k.off[t], pitch, *fields[t], width, rows[t],
+                                             width, es, s);
             if (e != hipSuccess) return e;
         }
-        tp->inp = base + k.inp;
-        tp->dinp = base + k.dinp;
-        tp->weight = base + k.weight;
-        tp->dweight = base + k.dweight;
+        *fields[t] = base + k.off[t];
     }
     tp->ldo = (int)k.ldo;
     tp->ldc = (int)k.ldc;
     return hipSuccess;
 }
 
-// Copy the packed dinp and dweight back to the caller's buffers.
-hipError_t unpack_outputs(const Packing& k, const char* base, void* dinp, void* dweight, long long BT,
-                          int C, int OC, int dtype, hipStream_t s) {
-    if (!k.c) return hipSuccess;
+// Copy the packed outputs (dinp, dweight; out) back to the caller's buffers.
+hipError_t unpack_outputs(const Packing& k, const char* base, void* dinp, void* dweight, void* out,
+                          long long BT, int C, int OC, int dtype, hipStream_t s) {
     const int es = (int)elem_size(dtype);
-    hipError_t e = launch_unpack(dinp, C, base + k.dinp, k.ldc, BT, C, es, s);
-    if (e != hipSuccess) return e;
-    return launch_unpack(dweight, C, base + k.dweight, k.ldc, OC, C, es, s);
+    hipError_t e = hipSuccess;
+    if (k.on[P_DINP]) e = launch_unpack(dinp, C, base + k.off[P_DINP], k.ldc, BT, C, es, s);
+    if (e == hipSuccess && k.on[P_DWEIGHT])
+        e = launch_unpack(dweight, C, base + k.off[P_DWEIGHT], k.ldc, OC, C, es, s);
+    if (e == hipSuccess && k.on[P_OUT])
+        e = launch_unpack(out, OC, base + k.off[P_OUT], k.ldo, BT, OC, es, s);
+    return e;
 }
 
 // ---------------------------------------------------------------------------
@@ -470,7 +495,7 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     Packing pk;
     char* pbase = nullptr;
     if (path == 2) {
-        pk = plan_packing(dtype, BT, C, OC);
+        pk = plan_packing_bwd(dtype, BT, C, OC, dinp, dweight, dout, inp, weight);
         Workspace& w = g_ws[{dev, s}];
         st = grow(dev, &w.packed, &w.packed_bytes, pk.bytes, false, s);
         if (st != MMB_OK) return st;
@@ -479,7 +504,8 @@ int backward_impl(void* dinp, void* dweight, void* dbias, const void* dout, cons
     }
     const hipError_t e = sr ? launch_tiles_bf16_sr(tp, s) : launch_tiles(dtype, tp, s);
     if (e != hipSuccess) return MMB_ERR_HIP;
-    if (path == 2 && unpack_outputs(pk, pbase, dinp, dweight, BT, C, OC, dtype, s) != hipSuccess)
+    if (path == 2 &&
+        unpack_outputs(pk, pbase, dinp, dweight, nullptr, BT, C, OC, dtype, s) != hipSuccess)
         return MMB_ERR_HIP;
     return MMB_OK;
 }
@@ -556,7 +582,7 @@ int backward_noalloc_impl(void* dinp, void* dweight, void* dbias, const void* do
     const size_t bb = align_up((size_t)plan.ws_bias_floats * 4, 256);
     const size_t wb = align_up((size_t)plan.ws_floats * 4, 256);
     Packing pk;
-    if (path == 2) pk = plan_packing(dtype, BT, C, OC);
+    if (path == 2) pk = plan_packing_bwd(dtype, BT, C, OC, dinp, dweight, dout, inp, weight);
     if (cb + ub + bb + wb + pk.bytes > (size_t)MMB_NOALLOC_SCRATCH_BYTES) return MMB_ERR_SCRATCH;
     char* base = nullptr;
     st = noalloc_scratch(dev, &base);
@@ -593,7 +619,8 @@ int backward_noalloc_impl(void* dinp, void* dweight, void* dbias, const void* do
     char* pbase = base + cb + ub + bb + wb;
     if (path == 2 && pack_operands(pk, pbase, &tp, dtype, s) != hipSuccess) return MMB_ERR_HIP;
     if (launch_tiles(dtype, tp, s) != hipSuccess) return MMB_ERR_HIP;
-    if (path == 2 && unpack_outputs(pk, pbase, dinp, dweight, BT, C, OC, dtype, s) != hipSuccess)
+    if (path == 2 &&
+        unpack_outputs(pk, pbase, dinp, dweight, nullptr, BT, C, OC, dtype, s) != hipSuccess)
         return MMB_ERR_HIP;
     return MMB_OK;
 }
@@ -684,7 +711,8 @@ int forward_impl(void* out, const void* inp, const void* weight, const void* bia
     int st = check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
     const int BT = B * T;
-    if (!choose_path_fwd(out, inp, weight, bias, C, OC, dtype)) {
+    const int path = choose_path_fwd(out, inp, weight, bias, C, OC, dtype);
+    if (path == 0) {
         TraceRange range("mmb forward launch (generic)");
         return launch_fwd_generic(dtype, out, inp, weight, bias, BT, C, OC, s) == hipSuccess
                    ? MMB_OK
@@ -696,7 +724,7 @@ int forward_impl(void* out, const void* inp, const void* weight, const void* bia
     PlanEntry* plan = nullptr;
     st = find_plan(dev, dtype, BT, C, OC, bias != nullptr, true, &plan);
     if (st != MMB_OK) return st;
-    TraceRange range("mmb forward launch");
+    TraceRange range(path == 2 ? "mmb forward launch (packed)" : "mmb forward launch");
     TilesParams tp = plan->plan.proto;
     st = get_workspace(dev, s, *plan, &tp);
     if (st != MMB_OK) return st;
@@ -704,7 +732,21 @@ int forward_impl(void* out, const void* inp, const void* weight, const void* bia
     tp.bias = bias;
     tp.inp = inp;
     tp.weight = weight;
-    return launch_fwd_tiles(dtype, tp, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+    Packing pk;
+    char* pbase = nullptr;
+    if (path == 2) {
+        pk = plan_packing_fwd(dtype, BT, C, OC, out, inp, weight, bias);
+        Workspace& w = g_ws[{dev, s}];
+        st = grow(dev, &w.packed, &w.packed_bytes, pk.bytes, false, s);
+        if (st != MMB_OK) return st;
+        pbase = (char*)w.packed.ptr;
+        if (pack_operands(pk, pbase, &tp, dtype, s) != hipSuccess) return MMB_ERR_HIP;
+    }
+    if (launch_fwd_tiles(dtype, tp, s) != hipSuccess) return MMB_ERR_HIP;
+    if (path == 2 &&
+        unpack_outputs(pk, pbase, nullptr, nullptr, out, BT, C, OC, dtype, s) != hipSuccess)
+        return MMB_ERR_HIP;
+    return MMB_OK;
 }
 
 }  // namespace
@@ -743,7 +785,7 @@ int mmb_forward_path(const void* out, const void* inp, const void* weight, const
                      int T, int C, int OC, int dtype) {
     const int st = mmb::check_fwd(out, inp, weight, bias, B, T, C, OC, dtype);
     if (st != MMB_OK) return st;
-    return mmb::choose_path_fwd(out, inp, weight, bias, C, OC, dtype);
+    return mmb::choose_path_fwd(out, inp, weight, bias, C, OC, dtype) > 0 ? 1 : 0;
 }
 
 int mmb_forward_stream(void* out, const void* inp, const void* weight, const void* bias, int B,

@@ -37,7 +37,8 @@ struct TilesParams {
     const void* weight;
     int BT, C, OC;
     // row pitches in elements: ldo of dout (backward) or out (forward), ldc of
-    // inp, weight, dinp and dweight; OC and C, or larger for packed copies
+    // inp, weight, dinp and dweight; OC and C, or larger for packed copies.
+    // The forward's bias holds ldo elements (zero past OC).
     int ldo, ldc;
     GemmPlan g[2];        // [UNIT_DWEIGHT], [UNIT_DINP]
     const int4* units;    // two int4 per unit (see above), in launch order

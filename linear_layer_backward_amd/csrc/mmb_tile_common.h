@@ -214,17 +214,20 @@ __device__ __forceinline__ void write_tile_lds(T* D, long long ldd, int M, int N
 // beta = 0 with a bias row (the forward product): D[m, n] = acc + bias[n],
 // rounded once; bias == nullptr adds nothing.  Every LDS row of the tile
 // starts as the bias slice [n0, n0 + BN), so the add/round pass is the one of
-// the beta = 1 epilogue.  bias is 16-byte aligned and N a multiple of the
-// 16-byte group, as on the rest of this path.
+// the beta = 1 epilogue.  bias is 16-byte aligned and holds bias_len >= N
+// elements, zero past N and whole 16-byte groups (a packed copy when N is
+// not a multiple of the group): the buffer range checks whole dwords, so a
+// range ending inside the last group would read its last bf16 pair as zero.
 template <typename T, int MB, int NB, int NT, int BM, int BN>
 __device__ __forceinline__ void write_tile_bias(T* D, long long ldd, int M, int N, int m0, int n0,
                                                 const f32x16 (&acc)[MB][NB], char* smem, int tid,
-                                                int lane, int wm0, int wn0, const T* bias) {
+                                                int lane, int wm0, int wn0, const T* bias,
+                                                long long bias_len) {
     typedef OutMap<T, NT, BM, BN> OM;
     constexpr int PITCH = out_pitch<T, BM, BN>();
     const int ch = tid % OM::CHUNKS, row0 = tid / OM::CHUNKS;
     const auto rb = make_rsrc(bias + (bias ? n0 : 0),
-                              bias ? (long long)(N - n0) * (long long)sizeof(T) : 0);
+                              bias ? (bias_len - n0) * (long long)sizeof(T) : 0);
     const u32x4 b = buffer_load16(rb, (uint32_t)(16 * ch) | oob_if_ge(n0 + OM::VEC * ch, N), 0);
     __syncthreads();
 #pragma unroll
@@ -237,14 +240,15 @@ __device__ __forceinline__ void write_tile_bias(T* D, long long ldd, int M, int 
 // beta = 0 with the bias added in registers (the bf16 forward): D = acc +
 // bias[n], rounded once, with no bias rows in LDS.  bv[nb][q] holds the 4
 // bias values (bf16) of the lane's columns n0 + wn0 + nb*32 + 8q + 4*(lane/32)
-// .. +3, loaded by load_bias_frags (zeros past N or without a bias); the
+// .. +3, loaded by load_bias_frags from a bias of bias_len elements as for
+// write_tile_bias (zeros past N or without a bias); the
 // tile then leaves LDS row-contiguously as in add_round_write, with
 // non-temporal stores (measured 2-3 % faster on the forward; no change on
 // the backward's epilogues, which keep the default policy).
 template <int NB>
-__device__ __forceinline__ void load_bias_frags(const bf16_t* bias, int N, int n0, int wn0, int lane,
-                                                u32x2 (&bv)[NB][4]) {
-    const auto rb = make_rsrc(bias + (bias ? n0 : 0), bias ? (long long)(N - n0) * 2 : 0);
+__device__ __forceinline__ void load_bias_frags(const bf16_t* bias, int N, long long bias_len, int n0,
+                                                int wn0, int lane, u32x2 (&bv)[NB][4]) {
+    const auto rb = make_rsrc(bias + (bias ? n0 : 0), bias ? (bias_len - n0) * 2 : 0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll

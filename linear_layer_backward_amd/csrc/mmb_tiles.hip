@@ -306,7 +306,7 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
 
     if constexpr (OP == Op::FWD)
         write_tile_bias<T, Kt::MB, Kt::NB, kThreads, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid,
-                                                            lane, wm0, wn0, (const T*)p.bias);
+                                                            lane, wm0, wn0, (const T*)p.bias, p.ldo);
     else
         write_tile_lds<T, Kt::MB, Kt::NB, kThreads, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid,
                                                            lane, wm0, wn0);

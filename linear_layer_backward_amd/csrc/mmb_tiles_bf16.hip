@@ -315,7 +315,7 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             if (do_bias) bias_add(cur);
             // the forward's bias, fetched while the last stage computes
             if constexpr (LAST && OP == Op::FWD)
-                load_bias_frags<NB>((const bf16_t*)p.bias, N, n0, wn0, lane, bv);
+                load_bias_frags<NB>((const bf16_t*)p.bias, N, p.ldo, n0, wn0, lane, bv);
             // substeps 0..2: pair j of stage it+1 to LDS, pair j of stage it+2
             // into the registers, fragments of substep j+1, MFMAs of substep j
 #pragma unroll
@@ -384,9 +384,9 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
                                                               lane, wm0, wn0, nullptr, p.seed, 1);
         else
             write_tile_bias<bf16_t, MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane,
-                                                        wm0, wn0, (const bf16_t*)p.bias);
+                                                        wm0, wn0, (const bf16_t*)p.bias, p.ldo);
     } else if (!BETA1) {
-        if (nk == 0) load_bias_frags<NB>((const bf16_t*)p.bias, N, n0, wn0, lane, bv);
+        if (nk == 0) load_bias_frags<NB>((const bf16_t*)p.bias, N, p.ldo, n0, wn0, lane, bv);
         bias_round_write<MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0,
                                              bv);
     } else if (nk > 0) {

@@ -121,11 +121,17 @@ def test_path_choice(mmb):
     assert mmb.mmb_path(*args(dtype=0, OC=3070)) == 1
     assert mmb.mmb_path(*args(dtype=1, B=8, C=768, OC=50257, bias=False)) == 1
     assert mmb.mmb_path(*args(dtype=1, C=1 << 23)) == 0      # beyond the tiles' offsets
-    a = args(dtype=1)
-    a[4] += 8                                                  # inp only 8-byte aligned
-    assert mmb.mmb_path(*a) == 0
+    assert mmb.mmb_path(*args(dtype=1, OC=(1 << 22) + 8)) == 0
+    # buffers off the 16-byte alignment go through packed copies; a buffer
+    # not aligned to its element size takes the generic path
+    for i, dt, off, want in [(4, 1, 8, 1), (4, 1, 2, 1), (3, 1, 14, 1), (0, 1, 2, 1),
+                             (1, 0, 4, 1), (5, 0, 12, 1), (4, 1, 1, 0), (0, 0, 2, 0),
+                             (5, 0, 6, 0)]:
+        a = args(dtype=dt)
+        a[i] += off
+        assert mmb.mmb_path(*a) == want, (i, dt, off)
     b = args(dtype=1)
-    b[2] += 2                                                  # dbias alignment is free
+    b[2] += 1                                                  # dbias alignment is free
     assert mmb.mmb_path(*b) == 1
     assert mmb.mmb_path(*args(dtype=5)) == -3
 
@@ -393,15 +399,18 @@ def test_forward_alias(mmb):
 def test_forward_path_choice(mmb):
     assert mmb.mmb_forward_path(*fargs(dtype=1)) == 1
     assert mmb.mmb_forward_path(*fargs(dtype=1, bias=False)) == 1
-    assert mmb.mmb_forward_path(*fargs(dtype=1, C=764)) == 0
+    # ragged rows and buffers off the 16-byte alignment: MFMA tiles on packed
+    # copies; a buffer not aligned to its element size: the generic path
+    assert mmb.mmb_forward_path(*fargs(dtype=1, C=764)) == 1
     assert mmb.mmb_forward_path(*fargs(dtype=0, C=764)) == 1
-    assert mmb.mmb_forward_path(*fargs(dtype=0, OC=3070)) == 0
-    a = fargs(dtype=1)
-    a[3] += 2                                  # the bias is read as 16-byte groups
-    assert mmb.mmb_forward_path(*a) == 0
-    b = fargs(dtype=1)
-    b[0] += 8
-    assert mmb.mmb_forward_path(*b) == 0
+    assert mmb.mmb_forward_path(*fargs(dtype=0, OC=3070)) == 1
+    assert mmb.mmb_forward_path(*fargs(dtype=1, B=8, C=768, OC=50257)) == 1
+    assert mmb.mmb_forward_path(*fargs(dtype=1, OC=1 << 23)) == 0
+    for i, dt, off, want in [(3, 1, 2, 1), (0, 1, 8, 1), (1, 0, 4, 1), (2, 1, 6, 1),
+                             (3, 1, 1, 0), (0, 0, 2, 0), (1, 1, 3, 0)]:
+        a = fargs(dtype=dt)
+        a[i] += off
+        assert mmb.mmb_forward_path(*a) == want, (i, dt, off)
     assert mmb.mmb_forward_path(*fargs(dtype=4)) == -3
 
 

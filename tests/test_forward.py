@@ -70,8 +70,9 @@ SMALL = [
     (2, 16, 64, 192, "f32"), (3, 100, 200, 328, "f32"), (1, 300, 132, 260, "f32"),
     (2, 150, 264, 400, "bf16"), (1, 513, 200, 136, "bf16"), (1, 1, 8, 8, "bf16"),
     (1, 1, 4, 4, "f32"),
-    # generic path: C or OC not a multiple of the vector width
+    # C or OC not a multiple of the vector width: MFMA tiles on packed copies
     (2, 7, 65, 129, "f32"), (3, 5, 33, 17, "bf16"), (1, 3, 12, 10, "bf16"),
+    (2, 40, 130, 258, "bf16"), (1, 70, 68, 300, "f32"),
 ]
 
 
@@ -119,6 +120,19 @@ def test_forward_guard_bands(dev, shape):
     check(case, None, got)
     host = from_dev(full, dt)
     assert np.all(host[:g] == 12288.0) and np.all(host[-g:] == 12288.0)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_forward_ragged_split_k_with_bias(dev, tune, dt):
+    """Ragged C and OC with split K: the last arriver adds the packed bias
+    (its final group straddles OC) to the summed partials."""
+    tune.set("MMB_SPLITS_FWD", "3")
+    case = wl.integer_case(2, 150, 263, 397, dt, seed=5)
+    b = make_bias(397, 6, integer=True)
+    check(case, b, run_fwd(case, b, dev), exact=True)
+    case = wl.random_case(1, 300, 130, 258, dt, seed=7)
+    b = wl.from_storage(wl.storage(make_bias(258, 8), dt), dt)
+    check(case, b, run_fwd(case, b, dev))
 
 
 def test_forward_deterministic(dev, tune):
@@ -226,9 +240,9 @@ def test_forward_and_backward_share_the_workspace(dev, tune):
     assert TOL["f32"] == 1e-4
 
 
-def test_forward_unaligned_pointers_take_generic_path(dev):
-    """Shapes the tiles accept, but out and inp start 2 bytes into their
-    buffers: the call takes the generic kernel and still matches."""
+def test_forward_unaligned_pointers_take_packed_tiles(dev):
+    """Shapes the tiles accept, but out, inp and the bias start some elements
+    past a 16-byte boundary: packed copies on the MFMA tiles, out copied back."""
     import torch
     from linear_layer_backward_amd import mmb
     B, T, C, OC = 2, 40, 64, 96
@@ -236,11 +250,38 @@ def test_forward_unaligned_pointers_take_generic_path(dev):
     bias = wl.normal(32, (OC,), 0.02, "bf16")
     _, xs = to_dev(np.concatenate([[0.0], case.inp.ravel()]), "bf16", dev)
     _, w = to_dev(case.weight, "bf16", dev)
-    _, b = to_dev(bias, "bf16", dev)
+    _, bs = to_dev(np.concatenate([[0.0] * 3, bias]), "bf16", dev)
     _, outs = to_dev(np.full(B * T * OC + 1, np.nan, np.float32), "bf16", dev)
-    x, out = xs[1:], outs[1:]
-    assert mmb.mmb_forward_path(out, x, w, b, B, T, C, OC, mmb.MMB_BF16) == 0
+    x, out, b = xs[1:], outs[1:], bs[3:]
+    assert mmb.mmb_forward_path(out, x, w, b, B, T, C, OC, mmb.MMB_BF16) == 1
     mmb.mmb_forward_stream(out, x, w, b, B, T, C, OC, mmb.MMB_BF16, torch.cuda.current_stream(dev))
     torch.cuda.synchronize(dev)
     got = from_dev(out, "bf16").reshape(B * T, OC)
     check(case, bias, got)
+    assert np.isnan(from_dev(outs[:1], "bf16")).all()   # nothing written before out
+
+
+def test_forward_generic_path_beyond_tile_offsets(dev):
+    """OC above 2^22: the generic forward kernel (B*T = 2, C = 8)."""
+    from linear_layer_backward_amd import mmb
+    for dt in ("bf16", "f32"):
+        case = wl.random_case(1, 2, 8, (1 << 22) + 40, dt, seed=33)
+        bias = wl.from_storage(wl.storage(make_bias(case.OC, 34), dt), dt)
+        _, x = to_dev(case.inp, dt, dev)
+        _, w = to_dev(case.weight, dt, dev)
+        _, b = to_dev(bias, dt, dev)
+        _, out = to_dev(np.full(case.BT * case.OC, np.nan, np.float32), dt, dev)
+        code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+        assert mmb.mmb_forward_path(out, x, w, b, case.B, case.T, case.C, case.OC, code) == 0
+        check(case, bias, run_fwd(case, bias, dev))
+
+
+def test_forward_unpadded_vocabulary(dev):
+    """The GPT-2 LM-head forward at the real vocabulary (OC = 50257): out and
+    the bias on packed copies; sampled rows exact with integer inputs."""
+    case = wl.integer_case(8, 1024, 768, 50257, "bf16", seed=35, with_bias=False, prefill=False)
+    bias = make_bias(case.OC, 36, integer=True)
+    print(f"[forward] {case.name}", flush=True)
+    got = run_fwd(case, bias, dev)
+    rows = sample(case.BT, tile_edges(case.BT, 256), 16, 37)
+    check(case, bias, got, rows=rows, exact=True)

@@ -228,7 +228,7 @@ def test_dbias_is_assigned(dev, dt):
 
 
 @pytest.mark.parametrize("shape", [(2, 150, 264, 400, "bf16"), (3, 100, 200, 328, "f32"),
-                                   (2, 7, 65, 129, "f32")], ids=["bf16", "f32", "generic"])
+                                   (2, 7, 65, 129, "f32")], ids=["bf16", "f32", "ragged_packed"])
 def test_guard_bands(dev, shape):
     """Nothing outside the output tensors is written."""
     B, T, C, OC, dt = shape
@@ -252,24 +252,66 @@ def test_deterministic(dev, tune, split):
         assert x.tobytes() == y.tobytes()
 
 
-def test_unaligned_pointers_take_generic_path(dev):
-    """A buffer that starts one element past an allocation is not 16-byte
-    aligned: the call must still be right (generic path)."""
+def shifted(x, dtype, dev, k):
+    """x uploaded k elements past the start of a fresh buffer (so its address
+    is k * element size bytes past a 256-byte boundary)."""
+    _, t = to_dev(np.concatenate([np.zeros(k, np.float32), np.asarray(x, np.float32).ravel()]),
+                  dtype, dev)
+    return t[k:]
+
+
+@pytest.mark.parametrize("dt,shift", [("f32", {"dout": 1}),
+                                      ("bf16", {"dout": 3, "dinp": 1, "weight": 5}),
+                                      ("bf16", {"inp": 4, "dweight": 2}),
+                                      ("f32", {"inp": 2, "weight": 1, "dinp": 3, "dweight": 1})],
+                         ids=["f32_dout", "bf16_dout_dinp_weight", "bf16_inp_dweight", "f32_all_c"])
+def test_unaligned_pointers_take_packed_tiles(dev, dt, shift):
+    """Buffers that start some elements past a 16-byte boundary go through
+    16-byte aligned packed copies to the MFMA tiles (outputs copied back):
+    random inputs within tolerance, integer inputs exact."""
     import torch
     from linear_layer_backward_amd import mmb
-    case = wl.random_case(2, 20, 64, 96, "f32", seed=14)
-    _, dout = to_dev(np.concatenate([[0.0], case.dout.ravel()]), "f32", dev)
-    dout = dout[1:]
-    _, inp = to_dev(case.inp, "f32", dev)
-    _, w = to_dev(case.weight, "f32", dev)
-    _, gi = to_dev(case.dinp0, "f32", dev)
-    _, gw = to_dev(case.dweight0, "f32", dev)
-    _, gb = to_dev(np.zeros(case.OC, np.float32), "f32", dev)
-    assert mmb.mmb_path(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, 0) == 0
-    mmb.mmb_backward(gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, 0)
-    torch.cuda.synchronize()
-    check_full(case, (from_dev(gi, "f32").reshape(case.BT, case.C),
-                      from_dev(gw, "f32").reshape(case.OC, case.C), from_dev(gb, "f32")))
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+    for case in (wl.random_case(2, 150, 264, 400, dt, seed=14),
+                 wl.integer_case(1, 300, 136, 264, dt, seed=14)):
+        t = {n: shifted(getattr(case, a), dt, dev, shift.get(n, 0))
+             for n, a in (("dout", "dout"), ("inp", "inp"), ("weight", "weight"),
+                          ("dinp", "dinp0"), ("dweight", "dweight0"))}
+        _, gb = to_dev(np.full(case.OC, np.nan, np.float32), dt, dev)
+        args = (t["dinp"], t["dweight"], gb, t["dout"], t["inp"], t["weight"], case.B, case.T,
+                case.C, case.OC, code)
+        assert mmb.mmb_path(*args) == 1
+        mmb.mmb_backward(*args)
+        torch.cuda.synchronize()
+        got = (from_dev(t["dinp"], dt).reshape(case.BT, case.C),
+               from_dev(t["dweight"], dt).reshape(case.OC, case.C), from_dev(gb, dt))
+        if case.meta.get("integer"):
+            check_exact(case, got)
+        else:
+            check_full(case, got)
+
+
+def test_generic_path_beyond_tile_offsets(dev):
+    """C above 2^22 is beyond the tiles' 32-bit slab offsets: the generic
+    kernels take the call (B*T = 1, OC = 8)."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    for dt in ("bf16", "f32"):
+        case = wl.random_case(1, 1, (1 << 22) + 24, 8, dt, seed=17)
+        _, dout = to_dev(case.dout, dt, dev)
+        _, inp = to_dev(case.inp, dt, dev)
+        _, w = to_dev(case.weight, dt, dev)
+        _, gi = to_dev(case.dinp0, dt, dev)
+        _, gw = to_dev(case.dweight0, dt, dev)
+        _, gb = to_dev(np.full(case.OC, np.nan, np.float32), dt, dev)
+        code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+        args = (gi, gw, gb, dout, inp, w, case.B, case.T, case.C, case.OC, code)
+        assert mmb.mmb_path(*args) == 0
+        print(f"[parity] generic {dt} C={case.C}", flush=True)
+        mmb.mmb_backward(*args)
+        torch.cuda.synchronize()
+        check_full(case, (from_dev(gi, dt).reshape(case.BT, case.C),
+                          from_dev(gw, dt).reshape(case.OC, case.C), from_dev(gb, dt)))
 
 
 def test_accumulates_across_calls(dev):

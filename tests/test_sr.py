@@ -63,7 +63,7 @@ def bits_to_f64(b):
 
 
 SHAPES = [(2, 150, 264, 400), (1, 513, 200, 136), (1, 1, 8, 8), (4, 300, 64, 96),
-          (3, 5, 33, 17), (1, 3, 12, 10)]   # the last two take the generic path
+          (3, 5, 33, 17), (1, 3, 12, 10)]   # the last two through packed copies
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
