@@ -1,7 +1,8 @@
 // mmb_generic.hip -- the generic path: one thread per output element, fp32
-// accumulation, any shape and any alignment.  It serves calls the MFMA tiles
-// cannot take (C or OC not a multiple of the 16-byte vector, unaligned
-// pointers).
+// accumulation, any shape and any alignment.  It serves the calls the MFMA
+// tiles cannot take even through packed copies: C or OC above 2^22 (beyond
+// the tiles' 32-bit slab offsets), or a buffer not aligned to its element
+// size.
 //
 // Operation: llm.c page "dev/cuda/matmul_backward.cu" -- the dinp and
 // dweight GEMMs of matmul_backward1 (beta = 1) and the one-thread-per-channel
