@@ -147,6 +147,53 @@ def test_noalloc_generic_path(dev):
     check(wl.random_case(1, 1, (1 << 22) + 16, 8, "bf16", seed=50), dev, with_oracle=False)
 
 
+@pytest.mark.parametrize("shape", [(2, 300, 520, 600, "bf16"), (1, 200, 130, 261, "bf16"),
+                                   (2, 100, 200, 328, "f32")],
+                         ids=["split_partials", "ragged_packed", "f32"])
+def test_noalloc_graph_replays(dev, tune, shape):
+    """A HIP graph captured around one mmb_backward_noalloc call (the call
+    makes no allocation and no host-to-device copy, so it can be captured):
+    every replay, with eager work and synchronisations between replays and
+    the outputs reset to the prefill, gives the eager call's bits."""
+    import torch
+    from linear_layer_backward_amd import mmb
+    if shape[0] == 2 and shape[4] == "bf16":
+        tune.set("MMB_SPLITS_DWEIGHT", "3")
+        tune.set("MMB_SPLITS_DINP", "2")
+    B, T, C, OC, dt = shape
+    case = wl.random_case(B, T, C, OC, dt, seed=51)
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+    dout, inp, w = (up(a, dt, dev) for a in (case.dout, case.inp, case.weight))
+    gi0, gw0 = up(case.dinp0, dt, dev), up(case.dweight0, dt, dev)
+    gi, gw = gi0.clone(), gw0.clone()
+    gb = up(np.zeros(case.OC, np.float32), dt, dev)
+    args = (gi, gw, gb, dout, inp, w, B, T, C, OC, code)
+    # eager reference (also plans the shape and looks up the scratch address)
+    mmb.mmb_backward_noalloc(*args, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize(dev)
+    ref = [down(t, dt) for t in (gi, gw, gb)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mmb.mmb_backward_noalloc(*args, s)
+    torch.cuda.synchronize(dev)
+    for rep in range(3):
+        gi.copy_(gi0)
+        gw.copy_(gw0)
+        gb.fill_(float("nan"))
+        x = dout.float().sum()   # eager work between replays
+        torch.cuda.synchronize(dev)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        assert torch.isfinite(x)
+        for name, a, b in zip(("dinp", "dweight", "dbias"), ref, (gi, gw, gb)):
+            np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          down(b, dt).view(np.uint32) if a.dtype == np.float32
+                                          else down(b, dt), err_msg=f"replay {rep}: {name}")
+
+
 def test_noalloc_rejects_plans_larger_than_the_scratch(dev, tune):
     """16 dweight splits of the GPT-2 fc shape need 144 MiB of partials: the
     call returns MMB_ERR_SCRATCH and enqueues nothing (the outputs keep their
