@@ -653,12 +653,12 @@ int check_ln(const void* dinp, const void* dweight, const void* dbias, const voi
 
 // Vectors per lane of the LayerNorm row kernel, or 0 for the generic kernels
 // (also when a row-streamed buffer is not 16-byte aligned).
-int ln_path(const void* dinp, const void* dout, const void* inp, const void* weight, int C,
-            int dtype) {
+LNLayout ln_path(const void* dinp, const void* dout, const void* inp, const void* weight, int C,
+                 int dtype) {
     const void* ptrs[4] = {dinp, dout, inp, weight};
     for (const void* p : ptrs)
-        if ((uintptr_t)p % 16 != 0) return 0;
-    return ln_vectors_per_lane(dtype, C);
+        if ((uintptr_t)p % 16 != 0) return LNLayout{0, 1};
+    return ln_layout(dtype, C);
 }
 
 int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, const void* inp,
@@ -678,11 +678,11 @@ int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, con
     p.BT = (long long)B * T;
     p.C = C;
     p.partial = nullptr;
-    const int nj = ln_path(dinp, dout, inp, weight, C, dtype);
+    const LNLayout lay = ln_path(dinp, dout, inp, weight, C, dtype);
     int G = 0;
     // held through the launch: another call may not regrow the partials first
     std::unique_lock<std::mutex> lock(g_mu, std::defer_lock);
-    if (nj > 0) {
+    if (lay.nj > 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
         lock.lock();
@@ -696,14 +696,15 @@ int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, con
             const long v = std::strtol(e, nullptr, 10);
             if (v > 0) want = std::min(v, 1L << 16);
         }
-        G = (int)std::max(1LL, std::min<long long>(want, (p.BT + 7) / 8));
+        const long long rows_per_step = 8 / lay.wpr;
+        G = (int)std::max(1LL, std::min<long long>(want, (p.BT + rows_per_step - 1) / rows_per_step));
         Workspace& w = g_ws[{dev, s}];
         st = grow(dev, &w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
         if (st != MMB_OK) return st;
         p.partial = (float*)w.partials.ptr;
     }
     TraceRange range("mmb layernorm launch");
-    return launch_layernorm_backward(dtype, p, G, nj, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
+    return launch_layernorm_backward(dtype, p, G, lay, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }
 
 int forward_impl(void* out, const void* inp, const void* weight, const void* bias, int B, int T,
@@ -773,7 +774,7 @@ int mmb_layernorm_path(const void* dinp, const void* dweight, const void* dbias,
     const int st = mmb::check_ln(dinp, dweight, dbias, dout, inp, weight, mean, rstd, B, T, C,
                                  dtype);
     if (st != MMB_OK) return st;
-    return mmb::ln_path(dinp, dout, inp, weight, C, dtype) > 0 ? 1 : 0;
+    return mmb::ln_path(dinp, dout, inp, weight, C, dtype).nj > 0 ? 1 : 0;
 }
 
 int mmb_forward_check_args(const void* out, const void* inp, const void* weight, const void* bias,

@@ -87,12 +87,18 @@ struct LNParams {
     int C;
     float* partial;        // [G, 2C] fp32 column sums per workgroup
 };
-// 16-byte vectors per lane of the row kernel for C (1, 2 or 4), or 0 for
-// the generic kernels (C not a multiple of the vector width, or too wide).
-int ln_vectors_per_lane(int dtype, int C);
-// G workgroups for the row kernel (partial holds G * 2C floats); nj from
-// ln_vectors_per_lane.  Two launches on `s` (rows, then the column reduce).
-hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, int nj, hipStream_t s);
+// Row-kernel layout for C: nj 16-byte vectors per lane (1, 2, 4; 8 in fp32)
+// and wpr waves per row (1, 2 or 4), or nj = 0 for the generic kernels (C
+// not a multiple of the vector width, or too wide).
+struct LNLayout {
+    int nj, wpr;
+};
+LNLayout ln_layout(int dtype, int C);
+int ln_vectors_per_lane(int dtype, int C);   // ln_layout(dtype, C).nj
+// G workgroups for the row kernel (partial holds G * 2C floats), each taking
+// 8 / wpr rows at a time.  Two launches on `s` (rows, then the column reduce).
+hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, LNLayout k,
+                                     hipStream_t s);
 
 // Row-pitch copies for shapes whose rows are not whole 16-byte vectors:
 // pack: dst[r, c] = src[r, c] for c < cols, 0 for cols <= c < ld_dst;

@@ -13,9 +13,12 @@
 //    dealt out wave by wave (the row index is wave-uniform, so every buffer
 //    descriptor lives in scalar registers).  Lane l owns the 16-byte column
 //    vectors l, l + 64, ... (NJ <= 4 of them in bf16, C <= 2048; NJ <= 8 in
-//    fp32, C <= 2048; wider rows take the generic kernels below), so each row is read
+//    fp32, C <= 2048), so each row is read
 //    with fully coalesced 16-byte loads; the weight row sits in LDS and the
 //    lane's dweight / dbias sums stay in registers for all its rows.
+//  * Wider rows (bf16 C <= 8192, fp32 C <= 4096) take 2 or 4 waves per row,
+//    whose two row sums meet in LDS (see ln_bwd_rows); wider still, the
+//    generic kernels below.
 //  * With up to 4 vectors per lane each wave keeps two rows in flight: the
 //    loads of its next row (dout, inp, the old dinp, mean, rstd) are issued
 //    before it works on the current one; with 8, one row.
@@ -77,7 +80,16 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-template <typename T, int NJ>
+// WPR waves per row: a row wider than one wave's NJ vectors per lane (bf16
+// C > 2048, fp32 C > 2048) is split into WPR contiguous parts, part h of 64 *
+// NJ vectors taken by wave h of a group of WPR waves (LN_NW / WPR rows per
+// workgroup step).  The two row sums then meet in LDS: each wave writes its
+// part's sums, one workgroup barrier, and every wave adds the WPR parts in
+// part order.  All waves of the workgroup take the same number of steps (a
+// group whose row is past the end works on an empty row), so the barriers
+// match; the sums' slots alternate between two buffers, so a wave writing
+// the next row's sums cannot overwrite values a slower wave still reads.
+template <typename T, int NJ, int WPR>
 __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     constexpr int V = Vec<T>::N;
     // Rows in flight per wave: two up to 4 vectors per lane; with 8 (wide
@@ -86,33 +98,37 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     // flight per CU stay the same).
     constexpr bool PIPE2 = NJ <= 4;
     static_assert(NJ <= 4 || sizeof(T) == 4, "8 bf16 vectors per lane would spill registers");
-    constexpr int COLS = 64 * NJ * V;
+    static_assert(WPR >= 1 && LN_NW % WPR == 0, "whole groups of waves");
+    constexpr int GROUPS = LN_NW / WPR;       // rows per workgroup step
+    constexpr int COLS = 64 * NJ * V;         // one wave's columns
     constexpr int SLOT = 2 * COLS;            // one wave's [dweight | dbias] sums
     __shared__ float red[LN_NW * SLOT];
+    __shared__ float xch[2][WPR > 1 ? LN_NW : 1][2];   // WPR > 1: the parts' row sums
     const int tid = threadIdx.x, lane = tid & 63;
     // uniform per wave: the row index, and so every buffer descriptor built
     // from it, stays in scalar registers (a per-lane value would make the
     // compiler wrap each buffer access in a readfirstlane loop)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave / WPR, part = wave % WPR;
     const int C = p.C;
     const long long rowbytes = (long long)C * (long long)sizeof(T);
-    // lane's vector j covers columns V * (lane + 64 j) .. + V - 1
+    // lane's vector j covers columns V * (64 * (NJ * part + j) + lane) .. + V - 1
     uint32_t off[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int col = V * (lane + 64 * j);
+        const int col = WPR == 1 ? V * (lane + 64 * j) : V * (64 * (NJ * part + j) + lane);
         off[j] = (uint32_t)(col * (int)sizeof(T)) | oob_if_ge(col, C);
     }
     // the weight row, shared by the workgroup's waves: vector v at wl[v]
-    __shared__ u32x4 wl[64 * NJ];
+    __shared__ u32x4 wl[64 * NJ * WPR];
     float aw[NJ][V], ab[NJ][V];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int e = 0; e < V; ++e) aw[j][e] = ab[j][e] = 0.f;
 
-    const long long nwaves = (long long)gridDim.x * LN_NW;
-    long long r = (long long)blockIdx.x * LN_NW + wave;
+    const long long ngroups = (long long)gridDim.x * GROUPS;
+    long long r = (long long)blockIdx.x * GROUPS + group;
     const T* dout = (const T*)p.dout;
     const T* inp = (const T*)p.inp;
     T* dinp = (T*)p.dinp;
@@ -140,11 +156,12 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
         S.s = to_f32(((const T*)p.rstd)[rr]);
     };
     const float invC = 1.0f / (float)C;
+    int step = 0;   // WPR > 1: row steps taken (the same in every wave)
     auto process = [&](RowSet& S, long long row) {
         float sa = 0.f, sb = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const u32x4 wj = wl[lane + 64 * j];
+            const u32x4 wj = WPR == 1 ? wl[lane + 64 * j] : wl[64 * (NJ * part + j) + lane];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 const float dv = elem<T>(S.d[j], e);
@@ -156,15 +173,34 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
                 aw[j][e] += nrm * dv;
             }
         }
-        const float a = wave_sum(sa) * invC, b = wave_sum(sb) * invC;
+        float ta = wave_sum(sa), tb = wave_sum(sb);
+        if constexpr (WPR > 1) {
+            float (*x)[2] = xch[step & 1];
+            if (lane == 0) {
+                x[wave][0] = ta;
+                x[wave][1] = tb;
+            }
+            __syncthreads();
+            ta = x[group * WPR][0];
+            tb = x[group * WPR][1];
+#pragma unroll
+            for (int h = 1; h < WPR; ++h) {
+                ta += x[group * WPR + h][0];
+                tb += x[group * WPR + h][1];
+            }
+            ++step;
+        }
+        const float a = ta * invC, b = tb * invC;
         // widen dout and inp again below instead of keeping 2 * NJ * V floats
         // live across the reductions (empty register barrier, no instruction)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(S.d[j]), "+v"(S.x[j]));
-        const auto rg = make_rsrc(dinp + row * C, rowbytes);
+        // (with WPR > 1 a group may step past the last row: an empty range)
+        const bool live = WPR == 1 || row < p.BT;
+        const auto rg = make_rsrc(dinp + (live ? row : 0) * C, live ? rowbytes : 0);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const u32x4 wj = wl[lane + 64 * j];
+            const u32x4 wj = WPR == 1 ? wl[lane + 64 * j] : wl[64 * (NJ * part + j) + lane];
             float o[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) {
@@ -180,29 +216,54 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     // staged while the first row's loads fly
     {
         const auto rw = make_rsrc(p.weight, rowbytes);
-        for (int v = tid; v < 64 * NJ; v += LN_NT)
+        for (int v = tid; v < 64 * NJ * WPR; v += LN_NT)
             wl[v] = buffer_load16(rw, (uint32_t)(V * v * (int)sizeof(T)) | oob_if_ge(V * v, C), 0);
         __syncthreads();
     }
-    if constexpr (PIPE2) {
+    if constexpr (WPR > 1) {
+        // every wave of the workgroup takes the same steps: the loop runs
+        // while the workgroup's first row of the step is live
+        const long long r0 = (long long)blockIdx.x * GROUPS;
+        long long base = r0;
+        if constexpr (PIPE2) {
+            while (base < p.BT) {
+                load_set(B, r + ngroups);
+                process(A, r);
+                r += ngroups;
+                base += ngroups;
+                if (base >= p.BT) break;
+                load_set(A, r + ngroups);
+                process(B, r);
+                r += ngroups;
+                base += ngroups;
+            }
+        } else {
+            while (base < p.BT) {
+                process(A, r);
+                r += ngroups;
+                base += ngroups;
+                if (base < p.BT) load_set(A, r);
+            }
+        }
+    } else if constexpr (PIPE2) {
         while (r < p.BT) {
-            load_set(B, r + nwaves);
+            load_set(B, r + ngroups);
             process(A, r);
-            r += nwaves;
+            r += ngroups;
             if (r >= p.BT) break;
-            load_set(A, r + nwaves);
+            load_set(A, r + ngroups);
             process(B, r);
-            r += nwaves;
+            r += ngroups;
         }
     } else {
         while (r < p.BT) {
             process(A, r);
-            r += nwaves;
+            r += ngroups;
             if (r < p.BT) load_set(A, r);
         }
     }
     // the 8 waves' column sums [dweight | dbias], each wave in its own slot,
-    // then added in wave order per column
+    // then, per column, the groups' sums of its part added in group order
     float* mine = red + wave * SLOT;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -213,16 +274,18 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
             mine[COLS + i] = ab[j][e];
         }
     __syncthreads();
-    float* part = p.partial + (long long)blockIdx.x * 2 * C;
+    float* part_out = p.partial + (long long)blockIdx.x * 2 * C;
     for (int i = tid; i < C; i += LN_NT) {
-        float sw = red[i], sb = red[COLS + i];
+        // column i sits in part h at index il (one part with one wave per row)
+        const int h = WPR == 1 ? 0 : i / COLS, il = WPR == 1 ? i : i - h * COLS;
+        float sw = red[h * SLOT + il], sb = red[h * SLOT + COLS + il];
 #pragma unroll
-        for (int wv = 1; wv < LN_NW; ++wv) {
-            sw += red[wv * SLOT + i];
-            sb += red[wv * SLOT + COLS + i];
+        for (int g = 1; g < GROUPS; ++g) {
+            sw += red[(g * WPR + h) * SLOT + il];
+            sb += red[(g * WPR + h) * SLOT + COLS + il];
         }
-        part[i] = sw;
-        part[C + i] = sb;
+        part_out[i] = sw;
+        part_out[C + i] = sb;
     }
 }
 
@@ -305,46 +368,61 @@ __global__ __launch_bounds__(256) void ln_generic_dwb(LNParams p) {
     *db = from_f32<T>(to_f32(*db) + sb);
 }
 
-template <typename T, int NJ>
+template <typename T, int NJ, int WPR = 1>
 hipError_t launch_rows(const LNParams& p, int G, hipStream_t s) {
-    hipLaunchKernelGGL((ln_bwd_rows<T, NJ>), dim3(G), dim3(LN_NT), 0, s, p);
+    hipLaunchKernelGGL((ln_bwd_rows<T, NJ, WPR>), dim3(G), dim3(LN_NT), 0, s, p);
     hipLaunchKernelGGL((ln_bwd_reduce<T>), dim3((2 * p.C + RED_COLS - 1) / RED_COLS),
                        dim3(RED_COLS * RED_GROUPS), 0, s, p, G);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_ln(const LNParams& p, int G, int nj, hipStream_t s) {
-    if (nj == 0) {
+hipError_t launch_ln(const LNParams& p, int G, LNLayout k, hipStream_t s) {
+    if (k.nj == 0) {
         hipLaunchKernelGGL(ln_generic_dinp<T>, dim3((unsigned)((p.BT + 3) / 4)), dim3(256), 0, s, p);
         hipLaunchKernelGGL(ln_generic_dwb<T>, dim3((p.C + 255) / 256), dim3(256), 0, s, p);
         return hipGetLastError();
     }
-    if (nj == 1) return launch_rows<T, 1>(p, G, s);
-    if (nj == 2) return launch_rows<T, 2>(p, G, s);
-    if (nj == 4) return launch_rows<T, 4>(p, G, s);
-    if constexpr (sizeof(T) == 4)
-        if (nj == 8) return launch_rows<T, 8>(p, G, s);
+    if (k.wpr == 1) {
+        if (k.nj == 1) return launch_rows<T, 1>(p, G, s);
+        if (k.nj == 2) return launch_rows<T, 2>(p, G, s);
+        if (k.nj == 4) return launch_rows<T, 4>(p, G, s);
+        if constexpr (sizeof(T) == 4)
+            if (k.nj == 8) return launch_rows<T, 8>(p, G, s);
+    }
+    if constexpr (sizeof(T) == 2) {
+        if (k.nj == 4 && k.wpr == 2) return launch_rows<T, 4, 2>(p, G, s);
+        if (k.nj == 4 && k.wpr == 4) return launch_rows<T, 4, 4>(p, G, s);
+    } else {
+        if (k.nj == 8 && k.wpr == 2) return launch_rows<T, 8, 2>(p, G, s);
+    }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int ln_vectors_per_lane(int dtype, int C) {
+LNLayout ln_layout(int dtype, int C) {
     const int V = dtype == 1 ? 8 : 4;
-    // 8 vectors per lane fit the registers (one row in flight) for fp32; for
-    // bf16 they would spill
-    const int nmax = dtype == 1 ? 4 : 8;
-    if (C % V != 0) return 0;
+    // vectors per lane of one wave: 8 fit the registers (one row in flight)
+    // for fp32; for bf16 they would spill, so wider bf16 rows take 2 or 4
+    // waves of 4.  The workgroup's LDS (the waves' column sums plus the
+    // weight row) caps the width: bf16 C <= 8192, fp32 C <= 4096.
+    const int nmax = dtype == 1 ? 4 : 8, wmax = dtype == 1 ? 4 : 2;
+    if (C % V != 0) return LNLayout{0, 1};
     const int nv = C / V;
     for (int nj = 1; nj <= nmax; nj *= 2)
-        if (nv <= 64 * nj) return nj;
-    return 0;
+        if (nv <= 64 * nj) return LNLayout{nj, 1};
+    for (int wpr = 2; wpr <= wmax; wpr *= 2)
+        if (nv <= 64 * nmax * wpr) return LNLayout{nmax, wpr};
+    return LNLayout{0, 1};
 }
 
-hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, int nj, hipStream_t s) {
-    if (dtype == 1) return launch_ln<bf16_t>(p, G, nj, s);
-    return launch_ln<float>(p, G, nj, s);
+int ln_vectors_per_lane(int dtype, int C) { return ln_layout(dtype, C).nj; }
+
+hipError_t launch_layernorm_backward(int dtype, const LNParams& p, int G, LNLayout k,
+                                     hipStream_t s) {
+    if (dtype == 1) return launch_ln<bf16_t>(p, G, k, s);
+    return launch_ln<float>(p, G, k, s);
 }
 
 }  // namespace mmb

@@ -49,8 +49,12 @@ SHAPES = [  # (B, T, C, dtype): row kernel with 1, 2, 4 (and fp32 8) vectors per
     (2, 37, 1600, "bf16"), (1, 300, 768, "bf16"), (3, 20, 256, "bf16"), (1, 5, 2048, "bf16"),
     (2, 33, 1000, "bf16"), (2, 50, 768, "f32"), (1, 70, 1024, "f32"), (3, 9, 100, "f32"),
     (2, 13, 1600, "f32"), (1, 40, 2048, "f32"), (3, 17, 1028, "f32"),
+    # wide rows, 2 or 4 waves per row (row counts not a multiple of the rows
+    # a workgroup takes per step, so the last step has groups past the end)
+    (1, 9, 2056, "bf16"), (2, 21, 3000, "bf16"), (1, 37, 4096, "bf16"), (3, 7, 5000, "bf16"),
+    (1, 13, 8192, "bf16"), (1, 6, 2052, "f32"), (2, 19, 3000, "f32"), (1, 11, 4096, "f32"),
     # generic kernels: C not a multiple of the vector width, or wider than the row kernel
-    (2, 11, 1603, "bf16"), (1, 9, 2056, "bf16"), (1, 6, 2052, "f32"), (1, 4, 7, "f32"),
+    (2, 11, 1603, "bf16"), (1, 5, 8200, "bf16"), (1, 4, 4100, "f32"), (1, 4, 7, "f32"),
     # degenerate: one row (one busy wave), one channel
     (1, 1, 768, "bf16"), (1, 1, 8, "f32"), (3, 1, 1, "f32"), (1, 2, 1, "bf16"),
 ]
@@ -61,6 +65,21 @@ SHAPES = [  # (B, T, C, dtype): row kernel with 1, 2, 4 (and fp32 8) vectors per
 def test_layernorm_small(dev, shape, prefill):
     B, T, C, dt = shape
     c = wl.layernorm_case(B, T, C, dt, seed=C + T, prefill=prefill)
+    check(c, run_ln(c, dev))
+
+
+@pytest.mark.parametrize("shape", [(8, 1024, 4096, "bf16"), (4, 1024, 8192, "bf16"),
+                                   (8, 1024, 4096, "f32")], ids=lambda s: "x".join(map(str, s)))
+def test_layernorm_wide_rows(dev, shape):
+    """Rows of 4096 and 8192 channels (several waves per row) at full row
+    counts, against the oracle."""
+    from linear_layer_backward_amd import mmb
+    B, T, C, dt = shape
+    c = wl.layernorm_case(B, T, C, dt, seed=C, prefill=True)
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+    fake = [256 * (i + 1) << 20 for i in range(8)]
+    assert mmb.mmb_layernorm_path(*fake, B, T, C, code) == 1
+    print(f"[layernorm] wide B={B} T={T} C={C} {dt}", flush=True)
     check(c, run_ln(c, dev))
 
 
