@@ -250,9 +250,9 @@ int mmb_forward_plan_units(int B, int T, int C, int OC, int dtype, int has_bias,
  * and one round to nearest-even per output.  Device pointers owned by the
  * caller, all required; outputs may not overlap each other or an input
  * (MMB_ERR_ALIAS).  16-byte aligned dinp, dout, inp and weight with C a
- * multiple of 8 (bf16) / 4 (fp32) and C <= 8192 (bf16) / 4096 (fp32) take
- * the row kernel (one wave per row up to C = 2048, two or four waves sharing
- * a row above; two launches: rows, then a fixed-order column reduction of the
+ * multiple of 8 (bf16) / 4 (fp32) and C <= 16384 take the row kernel (one
+ * wave per row up to C = 2048, two to eight waves sharing a row above; two
+ * launches: rows, then a fixed-order column reduction of the
  * per-workgroup fp32 partials, which live in the library's per-(device,
  * stream) workspace); anything else takes the generic kernels.  Results are
  * deterministic.  Errors as for mmb_backward. */

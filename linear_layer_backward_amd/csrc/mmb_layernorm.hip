@@ -17,8 +17,9 @@
 //    with fully coalesced 16-byte loads; the weight row sits in LDS and the
 //    lane's dweight / dbias sums stay in registers for all its rows.
 //  * Wider rows (bf16 C <= 8192, fp32 C <= 4096) take 2 or 4 waves per row,
-//    whose two row sums meet in LDS (see ln_bwd_rows); wider still, the
-//    generic kernels below.
+//    and rows up to C = 16384 all 8 waves of the workgroup; the parts' two
+//    row sums meet in LDS (see ln_bwd_rows).  Wider still, the generic
+//    kernels below.
 //  * With up to 4 vectors per lane each wave keeps two rows in flight: the
 //    loads of its next row (dout, inp, the old dinp, mean, rstd) are issued
 //    before it works on the current one; with 8, one row.
@@ -102,7 +103,9 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
     constexpr int GROUPS = LN_NW / WPR;       // rows per workgroup step
     constexpr int COLS = 64 * NJ * V;         // one wave's columns
     constexpr int SLOT = 2 * COLS;            // one wave's [dweight | dbias] sums
-    __shared__ float red[LN_NW * SLOT];
+    // the groups' column sums meet in LDS; with one group (WPR = 8) every
+    // column belongs to one wave, which writes its sums out directly
+    __shared__ float red[GROUPS > 1 ? LN_NW * SLOT : 1];
     __shared__ float xch[2][WPR > 1 ? LN_NW : 1][2];   // WPR > 1: the parts' row sums
     const int tid = threadIdx.x, lane = tid & 63;
     // uniform per wave: the row index, and so every buffer descriptor built
@@ -262,6 +265,25 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
             if (r < p.BT) load_set(A, r);
         }
     }
+    float* part_out = p.partial + (long long)blockIdx.x * 2 * C;
+    if constexpr (GROUPS == 1) {
+        // one row per step: the wave's sums are the workgroup's for its
+        // columns (16-byte aligned: the partial rows are 2C floats, C a
+        // multiple of V >= 4)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = V * (64 * (NJ * part + j) + lane);
+            if (col >= C) continue;
+#pragma unroll
+            for (int e = 0; e < V; e += 4) {
+                *(float4*)(part_out + col + e) =
+                    make_float4(aw[j][e], aw[j][e + 1], aw[j][e + 2], aw[j][e + 3]);
+                *(float4*)(part_out + C + col + e) =
+                    make_float4(ab[j][e], ab[j][e + 1], ab[j][e + 2], ab[j][e + 3]);
+            }
+        }
+        return;
+    }
     // the 8 waves' column sums [dweight | dbias], each wave in its own slot,
     // then, per column, the groups' sums of its part added in group order
     float* mine = red + wave * SLOT;
@@ -274,7 +296,6 @@ __global__ __launch_bounds__(LN_NT, 1) void ln_bwd_rows(LNParams p) {
             mine[COLS + i] = ab[j][e];
         }
     __syncthreads();
-    float* part_out = p.partial + (long long)blockIdx.x * 2 * C;
     for (int i = tid; i < C; i += LN_NT) {
         // column i sits in part h at index il (one part with one wave per row)
         const int h = WPR == 1 ? 0 : i / COLS, il = WPR == 1 ? i : i - h * COLS;
@@ -393,8 +414,11 @@ hipError_t launch_ln(const LNParams& p, int G, LNLayout k, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
         if (k.nj == 4 && k.wpr == 2) return launch_rows<T, 4, 2>(p, G, s);
         if (k.nj == 4 && k.wpr == 4) return launch_rows<T, 4, 4>(p, G, s);
+        if (k.nj == 4 && k.wpr == 8) return launch_rows<T, 4, 8>(p, G, s);
     } else {
         if (k.nj == 8 && k.wpr == 2) return launch_rows<T, 8, 2>(p, G, s);
+        if (k.nj == 4 && k.wpr == 8) return launch_rows<T, 4, 8>(p, G, s);
+        if (k.nj == 8 && k.wpr == 8) return launch_rows<T, 8, 8>(p, G, s);
     }
     return hipErrorInvalidValue;
 }
@@ -405,8 +429,10 @@ LNLayout ln_layout(int dtype, int C) {
     const int V = dtype == 1 ? 8 : 4;
     // vectors per lane of one wave: 8 fit the registers (one row in flight)
     // for fp32; for bf16 they would spill, so wider bf16 rows take 2 or 4
-    // waves of 4.  The workgroup's LDS (the waves' column sums plus the
-    // weight row) caps the width: bf16 C <= 8192, fp32 C <= 4096.
+    // waves of 4.  With several rows per workgroup step the LDS (the waves'
+    // column sums plus the weight row) caps that at bf16 C <= 8192, fp32
+    // C <= 4096; wider rows take all 8 waves of the workgroup (one row per
+    // step, no column sums in LDS) up to C = 16384.
     const int nmax = dtype == 1 ? 4 : 8, wmax = dtype == 1 ? 4 : 2;
     if (C % V != 0) return LNLayout{0, 1};
     const int nv = C / V;
@@ -414,6 +440,8 @@ LNLayout ln_layout(int dtype, int C) {
         if (nv <= 64 * nj) return LNLayout{nj, 1};
     for (int wpr = 2; wpr <= wmax; wpr *= 2)
         if (nv <= 64 * nmax * wpr) return LNLayout{nmax, wpr};
+    for (int nj = 4; nj <= nmax; nj *= 2)
+        if (nv <= 64 * nj * LN_NW) return LNLayout{nj, LN_NW};
     return LNLayout{0, 1};
 }
 

@@ -493,13 +493,17 @@ def test_layernorm_path(mmb):
     assert mmb.mmb_layernorm_path(*largs(dtype=1, C=2048)) == 1
     assert mmb.mmb_layernorm_path(*largs(dtype=1, C=2056)) == 1    # two waves per row
     assert mmb.mmb_layernorm_path(*largs(dtype=1, C=8192)) == 1    # four waves per row
-    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=8200)) == 0    # wider than the row kernel
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=8200)) == 1    # eight waves per row
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=16384)) == 1
+    assert mmb.mmb_layernorm_path(*largs(dtype=1, C=16392)) == 0   # wider than the row kernel
     assert mmb.mmb_layernorm_path(*largs(dtype=0, C=1024)) == 1
     assert mmb.mmb_layernorm_path(*largs(dtype=0, C=1600)) == 1    # the page's shape, fp32
     assert mmb.mmb_layernorm_path(*largs(dtype=0, C=2048)) == 1
     assert mmb.mmb_layernorm_path(*largs(dtype=0, C=2052)) == 1    # two waves per row
     assert mmb.mmb_layernorm_path(*largs(dtype=0, C=4096)) == 1
-    assert mmb.mmb_layernorm_path(*largs(dtype=0, C=4100)) == 0
+    assert mmb.mmb_layernorm_path(*largs(dtype=0, C=4100)) == 1    # eight waves per row
+    assert mmb.mmb_layernorm_path(*largs(dtype=0, C=16384)) == 1
+    assert mmb.mmb_layernorm_path(*largs(dtype=0, C=16388)) == 0
     assert mmb.mmb_layernorm_path(*largs(dtype=1, C=1604)) == 0    # not a multiple of 8
     a = largs(dtype=1, C=768)
     a[3] += 8                                  # dout 8-byte aligned only

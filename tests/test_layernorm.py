@@ -53,8 +53,11 @@ SHAPES = [  # (B, T, C, dtype): row kernel with 1, 2, 4 (and fp32 8) vectors per
     # a workgroup takes per step, so the last step has groups past the end)
     (1, 9, 2056, "bf16"), (2, 21, 3000, "bf16"), (1, 37, 4096, "bf16"), (3, 7, 5000, "bf16"),
     (1, 13, 8192, "bf16"), (1, 6, 2052, "f32"), (2, 19, 3000, "f32"), (1, 11, 4096, "f32"),
+    # eight waves per row, one row per workgroup step (parts past C idle)
+    (1, 5, 8200, "bf16"), (2, 3, 12288, "bf16"), (1, 4, 16384, "bf16"), (1, 4, 4100, "f32"),
+    (3, 3, 8192, "f32"), (1, 5, 12300, "f32"), (1, 3, 16384, "f32"),
     # generic kernels: C not a multiple of the vector width, or wider than the row kernel
-    (2, 11, 1603, "bf16"), (1, 5, 8200, "bf16"), (1, 4, 4100, "f32"), (1, 4, 7, "f32"),
+    (2, 11, 1603, "bf16"), (1, 3, 16392, "bf16"), (1, 2, 16388, "f32"), (1, 4, 7, "f32"),
     # degenerate: one row (one busy wave), one channel
     (1, 1, 768, "bf16"), (1, 1, 8, "f32"), (3, 1, 1, "f32"), (1, 2, 1, "bf16"),
 ]
@@ -69,9 +72,10 @@ def test_layernorm_small(dev, shape, prefill):
 
 
 @pytest.mark.parametrize("shape", [(8, 1024, 4096, "bf16"), (4, 1024, 8192, "bf16"),
-                                   (8, 1024, 4096, "f32")], ids=lambda s: "x".join(map(str, s)))
+                                   (8, 1024, 4096, "f32"), (2, 1024, 12288, "bf16"),
+                                   (2, 1024, 8192, "f32")], ids=lambda s: "x".join(map(str, s)))
 def test_layernorm_wide_rows(dev, shape):
-    """Rows of 4096 and 8192 channels (several waves per row) at full row
+    """Rows of 4096 to 12288 channels (several waves per row) at full row
     counts, against the oracle."""
     from linear_layer_backward_amd import mmb
     B, T, C, dt = shape
