@@ -254,8 +254,9 @@ int mmb_forward_plan_units(int B, int T, int C, int OC, int dtype, int has_bias,
  * wave per row up to C = 2048, two to eight waves sharing a row above; two
  * launches: rows, then a fixed-order column reduction of the
  * per-workgroup fp32 partials, which live in the library's per-(device,
- * stream) workspace); anything else takes the generic kernels.  Results are
- * deterministic.  Errors as for mmb_backward. */
+ * stream) workspace); anything else takes the generic kernels (dinp one
+ * wave per row; dweight and dbias as partial sums over bands of rows, reduced
+ * the same way).  Results are deterministic.  Errors as for mmb_backward. */
 int mmb_layernorm_backward(void* dinp, void* dweight, void* dbias,
                            const void* dout, const void* inp, const void* weight,
                            const void* mean, const void* rstd,

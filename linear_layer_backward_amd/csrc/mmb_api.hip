@@ -679,30 +679,31 @@ int layernorm_impl(void* dinp, void* dweight, void* dbias, const void* dout, con
     p.C = C;
     p.partial = nullptr;
     const LNLayout lay = ln_path(dinp, dout, inp, weight, C, dtype);
-    int G = 0;
     // held through the launch: another call may not regrow the partials first
-    std::unique_lock<std::mutex> lock(g_mu, std::defer_lock);
-    if (lay.nj > 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
-        lock.lock();
-        DeviceInfo di;
-        st = device_info(dev, &di);
-        if (st != MMB_OK) return st;
-        // one workgroup of 8 row-waves per CU (fewer for few rows);
-        // MMB_LN_WORKGROUPS overrides the count (tuning aid)
-        long long want = di.cus;
-        if (const char* e = g_tune.get(T_LN_WORKGROUPS)) {
-            const long v = std::strtol(e, nullptr, 10);
-            if (v > 0) want = std::min(v, 1L << 16);
-        }
-        const long long rows_per_step = 8 / lay.wpr;
-        G = (int)std::max(1LL, std::min<long long>(want, (p.BT + rows_per_step - 1) / rows_per_step));
-        Workspace& w = g_ws[{dev, s}];
-        st = grow(dev, &w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
-        if (st != MMB_OK) return st;
-        p.partial = (float*)w.partials.ptr;
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MMB_ERR_HIP;
+    DeviceInfo di;
+    st = device_info(dev, &di);
+    if (st != MMB_OK) return st;
+    // G partial rows of [dweight | dbias]: the row kernel runs one workgroup
+    // of 8 row-waves per CU (fewer for few rows), the generic kernels one
+    // band of rows per CU; MMB_LN_WORKGROUPS overrides the count (tuning aid)
+    long long want = di.cus;
+    if (const char* e = g_tune.get(T_LN_WORKGROUPS)) {
+        const long v = std::strtol(e, nullptr, 10);
+        if (v > 0) want = std::min(v, 1L << 16);
     }
+    // rows per workgroup step (row kernel) or per band (generic); the
+    // generic kernels' bands are a grid dimension, at most 65535
+    const long long rows_per_step = lay.nj > 0 ? 8 / lay.wpr : 1;
+    if (lay.nj == 0) want = std::min(want, 65535LL);
+    const int G =
+        (int)std::max(1LL, std::min<long long>(want, (p.BT + rows_per_step - 1) / rows_per_step));
+    Workspace& w = g_ws[{dev, s}];
+    st = grow(dev, &w.partials, &w.partial_bytes, (size_t)G * 2 * C * sizeof(float), false, s);
+    if (st != MMB_OK) return st;
+    p.partial = (float*)w.partials.ptr;
     TraceRange range("mmb layernorm launch");
     return launch_layernorm_backward(dtype, p, G, lay, s) == hipSuccess ? MMB_OK : MMB_ERR_HIP;
 }

@@ -370,23 +370,27 @@ __global__ __launch_bounds__(256) void ln_generic_dinp(LNParams p) {
     }
 }
 
-// dweight / dbias: one thread per column, rows in order.
+// dweight / dbias partials: one thread per column over a band of `band`
+// consecutive rows (in order), band y writing partial row y [dweight |
+// dbias]; ln_bwd_reduce then adds the bands in its fixed order, adds the old
+// values and rounds once, as after the row kernel.
 template <typename T>
-__global__ __launch_bounds__(256) void ln_generic_dwb(LNParams p) {
+__global__ __launch_bounds__(256) void ln_generic_dwb(LNParams p, long long band) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= p.C) return;
+    const long long r0 = (long long)blockIdx.y * band;
+    const long long r1 = r0 + band < p.BT ? r0 + band : p.BT;
     float sw = 0.f, sb = 0.f;
-    for (long long r = 0; r < p.BT; ++r) {
+    for (long long r = r0; r < r1; ++r) {
         const float dv = to_f32(((const T*)p.dout)[r * p.C + i]);
         const float nrm = (to_f32(((const T*)p.inp)[r * p.C + i]) - to_f32(((const T*)p.mean)[r])) *
                           to_f32(((const T*)p.rstd)[r]);
         sb += dv;
         sw += nrm * dv;
     }
-    T* dw = (T*)p.dweight + i;
-    T* db = (T*)p.dbias + i;
-    *dw = from_f32<T>(to_f32(*dw) + sw);
-    *db = from_f32<T>(to_f32(*db) + sb);
+    float* out = p.partial + (long long)blockIdx.y * 2 * p.C;
+    out[i] = sw;
+    out[p.C + i] = sb;
 }
 
 template <typename T, int NJ, int WPR = 1>
@@ -400,8 +404,14 @@ hipError_t launch_rows(const LNParams& p, int G, hipStream_t s) {
 template <typename T>
 hipError_t launch_ln(const LNParams& p, int G, LNLayout k, hipStream_t s) {
     if (k.nj == 0) {
+        // G bands of whole rows (the last one shorter), one partial row each
+        const long long band = (p.BT + G - 1) / G;
+        const int bands = (int)((p.BT + band - 1) / band);
         hipLaunchKernelGGL(ln_generic_dinp<T>, dim3((unsigned)((p.BT + 3) / 4)), dim3(256), 0, s, p);
-        hipLaunchKernelGGL(ln_generic_dwb<T>, dim3((p.C + 255) / 256), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(ln_generic_dwb<T>, dim3((p.C + 255) / 256, bands), dim3(256), 0, s, p,
+                           band);
+        hipLaunchKernelGGL((ln_bwd_reduce<T>), dim3((2 * p.C + RED_COLS - 1) / RED_COLS),
+                           dim3(RED_COLS * RED_GROUPS), 0, s, p, bands);
         return hipGetLastError();
     }
     if (k.wpr == 1) {
