@@ -87,6 +87,25 @@ def test_layernorm_wide_rows(dev, shape):
     check(c, run_ln(c, dev))
 
 
+@pytest.mark.parametrize("shape", [(4, 777, 1603, "bf16"), (2, 1000, 770, "f32"),
+                                   (1, 600, 16392, "bf16")], ids=lambda s: "x".join(map(str, s)))
+def test_layernorm_generic_bands(dev, shape):
+    """The generic kernels with many rows: dweight/dbias summed over bands of
+    rows (several rows per band, the last band shorter), then reduced."""
+    from linear_layer_backward_amd import mmb
+    B, T, C, dt = shape
+    c = wl.layernorm_case(B, T, C, dt, seed=C + 1, prefill=True)
+    code = mmb.MMB_BF16 if dt == "bf16" else mmb.MMB_FP32
+    fake = [256 * (i + 1) << 20 for i in range(8)]
+    assert mmb.mmb_layernorm_path(*fake, B, T, C, code) == 0
+    print(f"[layernorm] generic B={B} T={T} C={C} {dt}", flush=True)
+    a = run_ln(c, dev)
+    check(c, a)
+    b = run_ln(c, dev)
+    for x, y in zip(a, b):
+        assert x.tobytes() == y.tobytes()
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_layernorm_page_shape(dev, dt):
     """The page's benchmark shape B=8, T=1024, C=1600 (fp32 takes the row
