@@ -373,6 +373,54 @@ def test_two_streams_interleaved(dev, tune):
                            from_dev(gw, dt).reshape(case.OC, case.C), from_dev(gb, dt)))
 
 
+def test_host_threads(dev):
+    """Four host threads, each with its own stream, enqueue backward calls
+    of shapes no other test uses (so plans, work lists and workspaces are
+    created while the other threads call into the library), three calls
+    each on separate buffers; every result is exact."""
+    import threading
+    import torch
+    from linear_layer_backward_amd import mmb
+    shapes = [(1, 77, 136, 344, "bf16"), (2, 45, 264, 200, "f32"), (1, 130, 400, 72, "bf16"),
+              (3, 33, 96, 520, "f32")]
+    jobs = []
+    for t, (B, T, C, OC, dt) in enumerate(shapes):
+        mine = []
+        for n in range(3):
+            case = wl.integer_case(B, T, C, OC, dt, seed=300 + 10 * t + n)
+            bufs = [to_dev(a, dt, dev)[1] for a in (case.dinp0, case.dweight0, case.dout,
+                                                     case.inp, case.weight)]
+            mine.append((case, bufs, to_dev(np.zeros(OC, np.float32), dt, dev)[1]))
+        jobs.append((torch.cuda.Stream(dev), mine))
+    torch.cuda.synchronize(dev)
+    status = [[] for _ in jobs]
+
+    def work(t):
+        st, mine = jobs[t]
+        for case, (gi, gw, dout, inp, w), gb in mine:
+            try:
+                mmb.mmb_backward_stream(gi, gw, gb, dout, inp, w, case.B, case.T, case.C,
+                                        case.OC,
+                                        mmb.MMB_BF16 if case.dtype == "bf16" else mmb.MMB_FP32,
+                                        st)
+                status[t].append(0)
+            except mmb.MmbError as e:
+                status[t].append(str(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(len(jobs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize(dev)
+    assert status == [[0, 0, 0]] * len(jobs)
+    for _, mine in jobs:
+        for case, (gi, gw, _, _, _), gb in mine:
+            dt = case.dtype
+            check_exact(case, (from_dev(gi, dt).reshape(case.BT, case.C),
+                               from_dev(gw, dt).reshape(case.OC, case.C), from_dev(gb, dt)))
+
+
 def test_release_then_reuse(dev):
     """mmb_release synchronises and frees every workspace, plan and work list;
     the next call allocates again and is exact."""
