@@ -213,16 +213,24 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         const uint32_t kmask_b = BKC ? oob_if_ge(k0 + b_kc[j], Kd) : 0u;
         stg_b[j] = buffer_load16(rb, b_off[j] | kmask_b, 0);
     };
-    // Old output tile, passes 2j and 2j+1 of the epilogue, into the staging
-    // registers of pair j (an empty range for units that publish a partial;
-    // the forward has no old tile).
+    // Old output tile, passes p0 + 2j and p0 + 2j + 1 of the epilogue, into
+    // the staging registers of pair j (an empty range for units that publish
+    // a partial; the forward has no old tile).
     const bool own_write = BETA1 && splits <= 1;
     const long long out_base = (long long)m0 * ldd + n0;
     const auto ro = make_rsrc(D + out_base, own_write ? ((long long)M * ldd - out_base) * 2 : 0);
-    auto load_out_pair = [&](int j) {
-        stg_a[j] = buffer_load16(ro, out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, 2 * j), 0);
-        stg_b[j] = buffer_load16(ro, out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, 2 * j + 1), 0);
+    auto load_out_pair = [&](int j, int p0) {
+        stg_a[j] = buffer_load16(ro, out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, p0 + 2 * j), 0);
+        stg_b[j] = buffer_load16(ro, out_off<bf16_t, NT, BM, BN>(ldd, M, N, m0, n0, tid, p0 + 2 * j + 1), 0);
     };
+    // With two or more K iterations, a unit that writes its own tile fetches
+    // the whole old tile inside the loop: the next-to-last iteration's load
+    // slots (which would fetch a stage past the end) take passes 0..7, the
+    // last iteration stores them to the free LDS buffer like a stage and
+    // takes passes 8..15, so no load is left for the epilogue to wait on.
+    // (not in units that also sum dbias: that reduction takes the LDS
+    // before the epilogue)
+    const bool early = own_write && nk >= 2 && !do_bias;
     // Registers -> LDS buffer `stage`: load j of wave w fills 1 KB block
     // LOADS * w + j of each operand region, lane p at byte 16p.
     auto store_pair = [&](int stage, int j) {
@@ -306,11 +314,15 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         __syncthreads();
         Frag f0, f1;
         read_sub(0, 0, f0);
-        // One iteration; in the last one there is no next stage to store,
-        // and its load slots fetch the first half of the old output tile for
-        // the epilogue instead (units that write their tile themselves).
-        auto iteration = [&](int it, auto last) {
-            constexpr bool LAST = decltype(last)::value;
+        // One iteration.  In the last one there is no next stage to store:
+        // its load slots fetch passes 0..7 of the old tile for the epilogue,
+        // or, with `early`, the next-to-last iteration fetches passes 0..7
+        // instead of the stage past the end and the last one stores them to
+        // the free buffer like a stage and fetches passes 8..15.
+        auto iteration = [&](int it, auto mode) {
+            // 0: steady state, 1: next to last with `early`, 2: last
+            constexpr int MODE = decltype(mode)::value;
+            constexpr bool LAST = MODE == 2;
             const int cur = it & 1;
             if (do_bias) bias_add(cur);
             // the forward's bias, fetched while the last stage computes
@@ -322,10 +334,16 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             for (int j = 0; j < 3; ++j) {
                 wait_loads<2 * (LOADS - 1)>();
                 if constexpr (LAST) {
-                    if constexpr (BETA1) load_out_pair(j);
+                    if constexpr (BETA1) {
+                        if (early) store_pair(cur ^ 1, j);
+                        load_out_pair(j, early ? 2 * LOADS : 0);
+                    }
                 } else {
                     store_pair(cur ^ 1, j);
-                    load_pair(kt0 + it + 2, j);
+                    if constexpr (MODE == 1)
+                        load_out_pair(j, 0);
+                    else
+                        load_pair(kt0 + it + 2, j);
                 }
                 read_sub(cur, j + 1, (j & 1) ? f0 : f1);
                 mma_sub((j & 1) ? f1 : f0);
@@ -334,18 +352,27 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
             }
             wait_loads<2 * (LOADS - 1)>();
             if constexpr (LAST) {
-                if constexpr (BETA1) load_out_pair(3);
+                if constexpr (BETA1) {
+                    if (early) store_pair(cur ^ 1, 3);
+                    load_out_pair(3, early ? 2 * LOADS : 0);
+                }
             } else {
                 store_pair(cur ^ 1, 3);
-                load_pair(kt0 + it + 2, 3);
+                if constexpr (MODE == 1)
+                    load_out_pair(3, 0);
+                else
+                    load_pair(kt0 + it + 2, 3);
             }
             __syncthreads();
             if constexpr (!LAST) read_sub(cur ^ 1, 0, f0);
             mma_sub(f1);
             __builtin_amdgcn_sched_barrier(0);
         };
-        for (int it = 0; it + 1 < nk; ++it) iteration(it, std::false_type());
-        iteration(nk - 1, std::true_type());
+        const int steady = early ? nk - 2 : nk - 1;
+        for (int it = 0; it < steady; ++it) iteration(it, std::integral_constant<int, 0>());
+        if constexpr (BETA1)
+            if (early) iteration(nk - 2, std::integral_constant<int, 1>());
+        iteration(nk - 1, std::integral_constant<int, 2>());
     }
     wait_loads<0>();
 
@@ -389,6 +416,22 @@ __device__ __forceinline__ void run_unit(const TilesParams& p, const GemmPlan& g
         if (nk == 0) load_bias_frags<NB>((const bf16_t*)p.bias, N, p.ldo, n0, wn0, lane, bv);
         bias_round_write<MB, NB, NT, BM, BN>(D, ldd, M, N, m0, n0, acc, smem, tid, lane, wm0, wn0,
                                              bv);
+    } else if (early) {
+        // the whole old tile: passes 0..7 from the free LDS buffer (each
+        // thread reads back the vectors it stored there itself), 8..15 staged
+        static_assert(LOADS == 4, "the old tile's 16 passes: 8 read back, 8 in the staging pairs");
+        const char* e = smem + (((nk - 1) & 1) ^ 1) * STAGE + LOADS * wave * 1024 + 16 * lane;
+        u32x4 ev[2 * LOADS];
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            ev[2 * j] = *(const u32x4*)(e + j * 1024);
+            ev[2 * j + 1] = *(const u32x4*)(e + j * 1024 + REGION);
+        }
+        const u32x4 pre[4 * LOADS] = {ev[0],    ev[1],    ev[2],    ev[3],    ev[4],    ev[5],
+                                      ev[6],    ev[7],    stg_a[0], stg_b[0], stg_a[1], stg_b[1],
+                                      stg_a[2], stg_b[2], stg_a[3], stg_b[3]};
+        write_tile_lds<bf16_t, MB, NB, NT, BM, BN, 4 * LOADS, SR>(D, ldd, M, N, m0, n0, acc, smem,
+                                                                   tid, lane, wm0, wn0, pre, p.seed, 1);
     } else if (nk > 0) {
         // the last K iteration loaded passes 0..7 of the old tile
         static_assert(LOADS == 4, "the old tile's first 8 passes sit in the 4 staging pairs");
