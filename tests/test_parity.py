@@ -314,6 +314,36 @@ def test_generic_path_beyond_tile_offsets(dev):
                           from_dev(gw, dt).reshape(case.OC, case.C), from_dev(gb, dt)))
 
 
+@pytest.mark.parametrize("dt,splits", [("bf16", None), ("f32", None), ("bf16", "3"),
+                                       ("f32", "2")])
+def test_nonfinite_inputs_propagate(dev, tune, dt, splits):
+    """IEEE propagation, as the definitions give it: +inf in dout[r0, o0]
+    makes dinp row r0 and dweight row o0 +-inf (nan where the other factor
+    is 0) and dbias[o0] +inf; nan in inp[r1, c1] makes dweight column c1
+    nan.  Such a pattern does not depend on summation order, so the
+    positions of nan and inf and the signs of inf must equal the oracle's,
+    and the finite outputs must agree within the usual tolerance; also with
+    split partial tiles and their fix-up."""
+    if splits:
+        tune.set("MMB_SPLITS_DWEIGHT", splits)
+    case = wl.random_case(2, 37, 264, 200, dt, seed=41)
+    r0, o0, r1, c1 = 5, 17, 40, 100
+    case.dout[r0, o0] = np.inf
+    case.inp[r1, c1] = np.nan
+    case.weight[o0, 3] = 0.0          # inf * 0 = nan in dinp[r0, 3]
+    got = run(case, dev)
+    ref = oracle.case_backward(case)
+    for name, g, r in zip(("dinp", "dweight", "dbias"), got, ref):
+        np.testing.assert_array_equal(np.isnan(g), np.isnan(r), err_msg=name)
+        np.testing.assert_array_equal(np.isinf(g), np.isinf(r), err_msg=name)
+        inf = np.isinf(r)
+        np.testing.assert_array_equal(np.sign(g[inf]), np.sign(r[inf]), err_msg=name)
+        fin = np.isfinite(r)
+        assert_close(g[fin], r[fin], dt, name)
+    assert np.isnan(got[0][r0, 3]) and np.isinf(got[2][o0])
+    assert np.isnan(got[1][:, c1]).all()
+
+
 def test_accumulates_across_calls(dev):
     """Two calls add the gradient twice (beta = 1), exactly with integers."""
     import torch
