@@ -314,19 +314,21 @@ def test_generic_path_beyond_tile_offsets(dev):
                           from_dev(gw, dt).reshape(case.OC, case.C), from_dev(gb, dt)))
 
 
-@pytest.mark.parametrize("dt,splits", [("bf16", None), ("f32", None), ("bf16", "3"),
-                                       ("f32", "2")])
-def test_nonfinite_inputs_propagate(dev, tune, dt, splits):
+@pytest.mark.parametrize("dt,splits,C,OC", [("bf16", None, 264, 200), ("f32", None, 264, 200),
+                                             ("bf16", "3", 264, 200), ("f32", "2", 264, 200),
+                                             ("bf16", None, 263, 201), ("f32", "2", 261, 203)])
+def test_nonfinite_inputs_propagate(dev, tune, dt, splits, C, OC):
     """IEEE propagation, as the definitions give it: +inf in dout[r0, o0]
     makes dinp row r0 and dweight row o0 +-inf (nan where the other factor
     is 0) and dbias[o0] +inf; nan in inp[r1, c1] makes dweight column c1
     nan.  Such a pattern does not depend on summation order, so the
     positions of nan and inf and the signs of inf must equal the oracle's,
     and the finite outputs must agree within the usual tolerance; also with
-    split partial tiles and their fix-up."""
+    split partial tiles and their fix-up, and on the zero-padded copies of
+    ragged shapes."""
     if splits:
         tune.set("MMB_SPLITS_DWEIGHT", splits)
-    case = wl.random_case(2, 37, 264, 200, dt, seed=41)
+    case = wl.random_case(2, 37, C, OC, dt, seed=41)
     r0, o0, r1, c1 = 5, 17, 40, 100
     case.dout[r0, o0] = np.inf
     case.inp[r1, c1] = np.nan
