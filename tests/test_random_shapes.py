@@ -7,6 +7,8 @@ Integer inputs in [-2, 2], so every sum is exact in any order: fp32 results
 must equal the oracle bit for bit, bf16 results its exact value rounded once
 to nearest-even.  Each call's outputs sit between canaries that must survive.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -16,7 +18,8 @@ from test_parity import from_dev, round_bf16
 
 pytestmark = pytest.mark.gpu
 
-CASES = 120
+# more calls for a longer sweep: MMB_RANDOM_CALLS=1000 python -m pytest ...
+CASES = int(os.environ.get("MMB_RANDOM_CALLS", "120"))
 CANARY = 12288.0
 
 
