@@ -106,6 +106,30 @@ def test_layernorm_generic_bands(dev, shape):
         assert x.tobytes() == y.tobytes()
 
 
+LN_RANDOM = 60
+
+
+@pytest.mark.parametrize("i", range(LN_RANDOM))
+def test_layernorm_random_call(dev, i):
+    """Seeded random calls: row counts, widths from a few channels to past
+    the row kernel's limit (every layout: one to eight waves per row, ragged
+    and generic), both dtypes, prefilled or zero outputs."""
+    g = np.random.default_rng(7000 + i)
+    dt = ["bf16", "f32"][i % 2]
+    vec = 8 if dt == "bf16" else 4
+    kind = i % 3
+    if kind == 0:
+        C = int(g.integers(1, 2200))                       # often ragged
+    elif kind == 1:
+        C = vec * int(g.integers(1, 2100))                 # row kernel, up to 16800
+    else:
+        C = vec * int(g.integers(256, 2100)) + int(g.integers(0, 2))
+    B, T = int(g.integers(1, 4)), int(g.integers(1, 120))
+    c = wl.layernorm_case(B, T, C, dt, seed=i, prefill=bool(i % 4 < 2))
+    print(f"[layernorm] random {i}: B={B} T={T} C={C} {dt}", flush=True)
+    check(c, run_ln(c, dev))
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_layernorm_page_shape(dev, dt):
     """The page's benchmark shape B=8, T=1024, C=1600 (fp32 takes the row
