@@ -66,6 +66,35 @@ def check(case, bias, got, exact=False, rows=None):
         assert_close(g, ref, case.dtype, "out")
 
 
+
+def assert_same_nonfinite(g, r, dt, what):
+    """nan and inf at the same positions, infs of the same sign, finite
+    values within tolerance."""
+    np.testing.assert_array_equal(np.isnan(g), np.isnan(r), err_msg=what)
+    np.testing.assert_array_equal(np.isinf(g), np.isinf(r), err_msg=what)
+    inf = np.isinf(r)
+    np.testing.assert_array_equal(np.sign(g[inf]), np.sign(r[inf]), err_msg=what)
+    fin = np.isfinite(r)
+    assert_close(g[fin], r[fin], dt, what)
+
+
+@pytest.mark.parametrize("dt,C,OC", [("bf16", 264, 400), ("f32", 132, 260), ("bf16", 130, 258)])
+def test_forward_nonfinite_inputs_propagate(dev, dt, C, OC):
+    """nan in inp[r1, c1] makes out row r1 nan; +inf in weight[o0, c0] makes
+    out column o0 +-inf (nan where inp is 0); +inf in the bias makes its
+    column +inf: positions and signs as the oracle gives them."""
+    case = wl.random_case(2, 40, C, OC, dt, seed=43)
+    bias = make_bias(OC, 44)
+    r1, c1, o0, c0, ob = 7, 11, 9, 5, 20
+    case.inp[r1, c1] = np.nan
+    case.weight[o0, c0] = np.inf
+    case.inp[3, c0] = 0.0
+    bias[ob] = np.inf
+    got = run_fwd(case, bias, dev)
+    ref = oracle_fwd(case, bias)
+    assert_same_nonfinite(got, ref, dt, "out")
+    assert np.isnan(got[r1]).all() and np.isnan(got[3, o0])
+
 SMALL = [
     (2, 16, 64, 192, "f32"), (3, 100, 200, 328, "f32"), (1, 300, 132, 260, "f32"),
     (2, 150, 264, 400, "bf16"), (1, 513, 200, 136, "bf16"), (1, 1, 8, 8, "bf16"),

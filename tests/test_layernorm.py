@@ -106,6 +106,29 @@ def test_layernorm_generic_bands(dev, shape):
         assert x.tobytes() == y.tobytes()
 
 
+@pytest.mark.parametrize("dt,C", [("bf16", 1600), ("f32", 1600), ("bf16", 4096), ("bf16", 1603)])
+def test_layernorm_nonfinite_inputs_propagate(dev, dt, C):
+    """nan in inp[r, i] makes dinp row r nan (both row means see it) and
+    dweight[i] nan; +inf in dout[r2, j] makes dinp row r2 nan or inf,
+    dweight[j] and dbias[j] inf: positions and signs as the oracle gives
+    them (row kernel, several waves per row, generic kernels)."""
+    c = wl.layernorm_case(2, 37, C, dt, seed=C + 5, prefill=True)
+    r, i, r2, j = 4, 10, 20, 33
+    c.inp[r, i] = np.nan
+    c.dout[r2, j] = np.inf
+    got = run_ln(c, dev)
+    ref = oracle.layernorm_backward(c.dout, c.inp, c.weight, c.mean, c.rstd, c.dinp0, c.dweight0,
+                                    c.dbias0, B=c.B, T=c.T, C=c.C)
+    for name, g, rr in zip(("dinp", "dweight", "dbias"), got, ref):
+        np.testing.assert_array_equal(np.isnan(g), np.isnan(rr), err_msg=name)
+        np.testing.assert_array_equal(np.isinf(g), np.isinf(rr), err_msg=name)
+        inf = np.isinf(rr)
+        np.testing.assert_array_equal(np.sign(g[inf]), np.sign(rr[inf]), err_msg=name)
+        fin = np.isfinite(rr)
+        assert_close(g[fin], rr[fin], dt, name)
+    assert np.isnan(got[0][r]).all() and np.isnan(got[1][i])
+
+
 LN_RANDOM = 60
 
 
