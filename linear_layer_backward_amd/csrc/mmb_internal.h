@@ -88,7 +88,7 @@ struct LNParams {
     float* partial;        // [G, 2C] fp32 column sums per workgroup
 };
 // Row-kernel layout for C: nj 16-byte vectors per lane (1, 2, 4; 8 in fp32)
-// and wpr waves per row (1, 2 or 4), or nj = 0 for the generic kernels (C
+// and wpr waves per row (1, 2, 4 or 8), or nj = 0 for the generic kernels (C
 // not a multiple of the vector width, or too wide).
 struct LNLayout {
     int nj, wpr;

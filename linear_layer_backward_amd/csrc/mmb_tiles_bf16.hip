@@ -46,6 +46,9 @@
 //  * Split K (dweight's K = B*T): fp32 partial tiles in the workspace, the
 //    last arriver adds them in split order, adds the old output and rounds
 //    once to bf16.
+//  * A unit that writes its own tile fetches the old tile inside the K
+//    loop, in load slots that would otherwise fetch past the last stage, so
+//    that the beta = 1 epilogue waits on no load.
 #include <type_traits>
 
 #include "mmb_tile_common.h"
